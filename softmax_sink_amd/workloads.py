@@ -1,0 +1,197 @@
+"""Seeded synthetic inputs for sink attention (shared by tests and bench).
+
+This module only draws numbers and lays them out; it holds none of the
+attention arithmetic. Both the HIP path and the CPU oracle consume what it
+produces, so it imports neither of them.
+
+Recipe (one numpy ``default_rng(seed)`` stream per problem; draw order:
+sequence lengths, q, k, v, dO, sinks):
+
+* values are drawn as fp32 N(0, 1); for bf16 problems they are rounded to
+  bf16 with round-to-nearest-even and kept as raw bf16 bit patterns
+  (``uint16``); ``as_f32`` widens them exactly;
+* the softmax scale is the fp32 value of 1/sqrt(head_dim) unless given;
+* sink logits are fp32: drawn N(0, 1) per q-head ("learnable offset"), or a
+  constant ln n for softmax_n problems.
+
+The named configurations follow the five workloads of the benchmark spec:
+``softmax1_fp32`` (1 x 128 x 128, 1 head, D 64, n = 1, non-causal),
+``prefill_varlen`` (16 sequences, lengths uniform in [64, 2048], 32/32
+heads, D 128, causal), ``train_varlen`` (8 sequences summing to 32768
+tokens, lengths uniform in [1024, 8192], 32/32 heads, D 128, causal,
+forward + backward), ``gqa_window`` (4 x 8192, 64/8 heads, D 128, causal
+with window (1024, 0), forward + backward) and ``decode_softmax_n`` (64
+sequences, q length uniform in [1, 16], kv length uniform in [512, 32768],
+32/8 heads, D 128, bottom-right causal, n = 0.5).
+"""
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+_CHUNK = 1 << 24
+
+
+def round_to_bf16_bits(x):
+    """fp32 array -> uint16 bf16 bit patterns, round to nearest even.
+    Inputs are finite normal draws (no NaN handling needed)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits):
+    """Exact widening of bf16 bit patterns to fp32."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _normal(rng, n, bf16):
+    """n draws of N(0,1) in fp32, drawn chunk by chunk (same stream as one
+    call), optionally rounded to bf16 bits."""
+    out = np.empty(n, dtype=np.uint16 if bf16 else np.float32)
+    for a in range(0, n, _CHUNK):
+        b = min(n, a + _CHUNK)
+        x = rng.standard_normal(b - a, dtype=np.float32)
+        out[a:b] = round_to_bf16_bits(x) if bf16 else x
+    return out
+
+
+@dataclass
+class Problem:
+    name: str
+    dtype: str                     # "bf16" or "fp32"
+    cu_q: np.ndarray               # int32 [B+1]
+    cu_k: np.ndarray               # int32 [B+1]
+    num_heads_q: int
+    num_heads_k: int
+    head_dim: int
+    causal: bool
+    win_left: int
+    win_right: int
+    scale: np.float32
+    sinks: np.ndarray              # fp32 [Hq]; -inf allowed (no sink)
+    q: np.ndarray                  # uint16 bf16 bits or fp32, [Tq,Hq,D]
+    k: np.ndarray                  # [Tk,Hk,D]
+    v: np.ndarray                  # [Tk,Hk,D]
+    dout: np.ndarray               # [Tq,Hq,D]
+    seed: int = 0
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def batch(self):
+        return len(self.cu_q) - 1
+
+    @property
+    def total_q(self):
+        return int(self.cu_q[-1])
+
+    @property
+    def total_k(self):
+        return int(self.cu_k[-1])
+
+    @property
+    def max_seqlen_q(self):
+        return int(np.diff(self.cu_q).max()) if self.batch else 0
+
+    @property
+    def max_seqlen_k(self):
+        return int(np.diff(self.cu_k).max()) if self.batch else 0
+
+    def as_f32(self, name):
+        """Exact fp32 view of one of q, k, v, dout."""
+        x = getattr(self, name)
+        return bf16_bits_to_f32(x) if self.dtype == "bf16" else x
+
+    def sub_batch(self, seqs):
+        """A new Problem holding only the listed sequences (same heads,
+        sinks, scale and mask) -- used to check samples of a large batch."""
+        qs, ks, cq, ck = [], [], [0], [0]
+        for b in seqs:
+            qs.append(slice(int(self.cu_q[b]), int(self.cu_q[b + 1])))
+            ks.append(slice(int(self.cu_k[b]), int(self.cu_k[b + 1])))
+            cq.append(cq[-1] + qs[-1].stop - qs[-1].start)
+            ck.append(ck[-1] + ks[-1].stop - ks[-1].start)
+        cat = lambda x, sl: np.concatenate([x[s] for s in sl], axis=0)
+        return Problem(self.name + "[sub]", self.dtype,
+                       np.array(cq, np.int32), np.array(ck, np.int32),
+                       self.num_heads_q, self.num_heads_k, self.head_dim,
+                       self.causal, self.win_left, self.win_right, self.scale,
+                       self.sinks, cat(self.q, qs), cat(self.k, ks),
+                       cat(self.v, ks), cat(self.dout, qs), self.seed,
+                       dict(self.meta, parent_seqs=list(seqs)))
+
+
+def make_problem(seed, lens_q, lens_k, num_heads_q, num_heads_k, head_dim,
+                 dtype="bf16", causal=True, win_left=-1, win_right=-1,
+                 sinks="normal", scale=None, name="custom", rng=None):
+    """Draw q, k, v, dO (and sinks) for given sequence lengths.
+
+    sinks: "normal" (N(0,1) fp32 per q-head), a float (same logit for every
+    head; -inf = no sink), or an explicit array of Hq fp32 values."""
+    rng = np.random.default_rng(seed) if rng is None else rng
+    lens_q = np.asarray(lens_q, dtype=np.int64)
+    lens_k = np.asarray(lens_k, dtype=np.int64)
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    Tq, Tk = int(cu_q[-1]), int(cu_k[-1])
+    bf16 = dtype == "bf16"
+    q = _normal(rng, Tq * num_heads_q * head_dim, bf16).reshape(Tq, num_heads_q, head_dim)
+    k = _normal(rng, Tk * num_heads_k * head_dim, bf16).reshape(Tk, num_heads_k, head_dim)
+    v = _normal(rng, Tk * num_heads_k * head_dim, bf16).reshape(Tk, num_heads_k, head_dim)
+    dout = _normal(rng, Tq * num_heads_q * head_dim, bf16).reshape(Tq, num_heads_q, head_dim)
+    if isinstance(sinks, str) and sinks == "normal":
+        s = rng.standard_normal(num_heads_q, dtype=np.float32)
+    elif np.isscalar(sinks):
+        s = np.full(num_heads_q, sinks, dtype=np.float32)
+    else:
+        s = np.asarray(sinks, dtype=np.float32)
+    if scale is None:
+        scale = np.float32(1.0 / math.sqrt(head_dim))
+    return Problem(name, dtype, cu_q, cu_k, num_heads_q, num_heads_k, head_dim,
+                   bool(causal), int(win_left), int(win_right),
+                   np.float32(scale), s, q, k, v, dout, seed)
+
+
+def _train_lengths(rng, n=8, total=32768, lo=1024, hi=8192):
+    """n lengths uniform in [lo, hi] summing to total: draw n-1, set the last
+    to the remainder, redraw all until the last is in range."""
+    while True:
+        head = rng.integers(lo, hi + 1, n - 1)
+        last = total - int(head.sum())
+        if lo <= last <= hi:
+            return np.concatenate([head, [last]])
+
+
+CONFIG_NAMES = ("softmax1_fp32", "prefill_varlen", "train_varlen",
+                "gqa_window", "decode_softmax_n")
+
+
+def config(name):
+    """The named workload with its fixed seed."""
+    if name == "softmax1_fp32":
+        return make_problem(1, [128], [128], 1, 1, 64, dtype="fp32",
+                            causal=False, sinks=0.0,
+                            scale=np.float32(0.125), name=name)
+    if name == "prefill_varlen":
+        rng = np.random.default_rng(2)
+        lens = rng.integers(64, 2049, 16)
+        return make_problem(2, lens, lens, 32, 32, 128, causal=True,
+                            name=name, rng=rng)
+    if name == "train_varlen":
+        rng = np.random.default_rng(3)
+        lens = _train_lengths(rng)
+        return make_problem(3, lens, lens, 32, 32, 128, causal=True,
+                            name=name, rng=rng)
+    if name == "gqa_window":
+        lens = np.full(4, 8192)
+        return make_problem(4, lens, lens, 64, 8, 128, causal=True,
+                            win_left=1024, win_right=0, name=name)
+    if name == "decode_softmax_n":
+        rng = np.random.default_rng(5)
+        lq = rng.integers(1, 17, 64)
+        lk = rng.integers(512, 32769, 64)
+        return make_problem(5, lq, lk, 32, 8, 128, causal=True,
+                            sinks=np.float32(math.log(0.5)), name=name,
+                            rng=rng)
+    raise KeyError(name)

@@ -1,0 +1,60 @@
+"""Seeded input generators: rounding, reproducibility and the workload
+recipes (lengths, ranges, shapes)."""
+import math
+
+import numpy as np
+import torch
+
+from softmax_sink_amd import workloads as W
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32),
+                        np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8,
+                                  3.0e-39, 65504.0], np.float32)])
+    ours = W.round_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+    back = W.bf16_bits_to_f32(ours)
+    np.testing.assert_array_equal(back, torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+def test_chunked_draws_equal_single_draw(monkeypatch):
+    a = W._normal(np.random.default_rng(7), 1000, False)
+    monkeypatch.setattr(W, "_CHUNK", 64)
+    b = W._normal(np.random.default_rng(7), 1000, False)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_make_problem_is_reproducible():
+    p1 = W.make_problem(9, [3, 5], [4, 6], 4, 2, 64)
+    p2 = W.make_problem(9, [3, 5], [4, 6], 4, 2, 64)
+    for n in ("q", "k", "v", "dout", "sinks"):
+        np.testing.assert_array_equal(getattr(p1, n), getattr(p2, n))
+    assert p1.q.shape == (8, 4, 64) and p1.k.shape == (10, 2, 64)
+    assert p1.scale == np.float32(1 / math.sqrt(64))
+    sub = p1.sub_batch([1])
+    np.testing.assert_array_equal(sub.q, p1.q[3:])
+    np.testing.assert_array_equal(sub.cu_k, [0, 6])
+
+
+def test_named_configs_small():
+    c1 = W.config("softmax1_fp32")
+    assert c1.dtype == "fp32" and c1.q.shape == (128, 1, 64)
+    assert c1.sinks.tolist() == [0.0] and c1.scale == np.float32(0.125)
+    assert not c1.causal
+
+
+def test_length_recipes():
+    # lengths only: reproduce the draws without materialising the tensors
+    rng = np.random.default_rng(2)
+    lens = rng.integers(64, 2049, 16)
+    assert lens.min() >= 64 and lens.max() <= 2048
+    rng = np.random.default_rng(3)
+    tl = W._train_lengths(rng)
+    assert tl.sum() == 32768 and tl.min() >= 1024 and tl.max() <= 8192 and len(tl) == 8
+    rng = np.random.default_rng(5)
+    lq, lk = rng.integers(1, 17, 64), rng.integers(512, 32769, 64)
+    assert lq.min() >= 1 and lq.max() <= 16 and lk.min() >= 512 and lk.max() <= 32768
+    assert (lq <= lk).all()
