@@ -1,0 +1,178 @@
+/*
+ * sink_attn.h -- C ABI of libsinkattn.so: attention whose softmax
+ * denominator carries one extra "sink" logit per query head, forward and
+ * backward, over packed variable-length (THD) sequences, for AMD MI355X
+ * (gfx950).
+ *
+ * What is computed. For each sequence b, q-head h (kv-head hk = h / (Hq/Hk))
+ * and query row i, with S_ij = scale * q_i . k_j over the kept keys j:
+ *
+ *   out_i = sum_j e^{S_ij} v_j / (e^{s_h} + sum_j e^{S_ij})
+ *   lse_i = ln(e^{s_h} + sum_j e^{S_ij})              (sink INCLUSIVE)
+ *
+ * i.e. softmax over the scores with the sink s_h appended as one more
+ * column, that column dropped afterwards ("slime: learnable_softmax_
+ * attention.py", module docstring), evaluated in the max-stabilised form
+ * m = max(s_h, max_j S_ij) of the "CANN ops-transformer: flash_attn" page
+ * (Formula section). softmax_n ("Flash-Attention-Softmax-N" README,
+ * introduction) is the special case s_h = ln n; s_h = -inf (or a NULL sink
+ * pointer) is plain softmax attention. The sink is not multiplied by scale.
+ *
+ * Masks ("pytorch/pytorch issue #108108", Proposal section): row i stands
+ * at key position p_i = i + (Lk_b - Lq_b) (bottom-right alignment).
+ * causal keeps j <= p_i; win_right >= 0 keeps j <= p_i + win_right;
+ * win_left >= 0 keeps j >= p_i - win_left (inclusive; -1 = unbounded, as in
+ * the "slime" wrapper's window_size and the CANN page's win_left/win_right).
+ * causal requires win_right in {-1, 0}. A row that keeps no key gets
+ * out = 0 and lse = s_h (-inf without a sink; its gradients are then 0).
+ *
+ * Backward ("slime", _LearnableSoftmaxFlashAttnVarlen.backward, and the
+ * chain rule through the extended softmax): with P_ij = e^{S_ij - lse_i},
+ * D_i = dO_i . out_i and dS_ij = P_ij (dO_i . v_j - D_i):
+ *   dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i,
+ *   dv_j = sum_i P_ij dO_i  (dk, dv summed over the q-heads of a group),
+ *   dsink_h = -sum_i e^{s_h - lse_i} D_i.
+ *
+ * Layouts (all contiguous, row-major, base pointers 16-byte aligned):
+ *   q, out, dout, dq : [total_q, num_heads_q, head_dim]  (dtype)
+ *   k, v, dk, dv     : [total_k, num_heads_k, head_dim]  (dtype)
+ *   lse              : [num_heads_q, total_q] fp32
+ *   sink_logits, dsink: [num_heads_q] fp32
+ *   cu_seqlens_q/k   : [batch + 1] int32, first 0, non-decreasing,
+ *                      last = total ("slime" wrapper docstring; CANN page,
+ *                      SeqLengths parameter group)
+ *
+ * Ownership and threading. The library allocates nothing and keeps no state
+ * between calls (except the one-shot timing events of sink_attn_arm_timing,
+ * which are per host thread). Every device buffer and the stream belong to
+ * the caller; fwd/bwd only enqueue work on `stream` and return, so device
+ * buffers, meta_dev and workspace must stay alive until that work is done.
+ * Outputs must not alias inputs. Calls are reentrant.
+ *
+ * Errors. Every argument the host can see is checked and reported through
+ * the returned status; nothing is thrown across the ABI and nothing is
+ * launched when a check fails. Values that live only in device memory
+ * (device cu_seqlens equal to the host copy used for the metadata, NaN
+ * inputs) are not checked: passing inconsistent ones is undefined, as on
+ * the CANN page (Constraints, "Declaration").
+ */
+#ifndef SINK_ATTN_H
+#define SINK_ATTN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SINK_ATTN_ABI_VERSION 1
+
+typedef enum {
+  SINK_ATTN_OK = 0,
+  SINK_ATTN_E_INVALID = 1,          /* bad argument value or pointer        */
+  SINK_ATTN_E_UNSUPPORTED = 2,      /* head_dim or dtype not built          */
+  SINK_ATTN_E_META_MISMATCH = 3,    /* metadata header differs from call    */
+  SINK_ATTN_E_BUFFER_TOO_SMALL = 4, /* meta capacity or workspace too small */
+  SINK_ATTN_E_HIP = 5               /* a HIP launch failed                  */
+} sink_attn_status;
+
+typedef enum { SINK_ATTN_FP32 = 0, SINK_ATTN_BF16 = 1 } sink_attn_dtype;
+
+/* The problem, passed by pointer and not retained. Checks: 0 < batch <
+ * 65536; total_q, total_k, num_heads_q, num_heads_k > 0; num_heads_q %
+ * num_heads_k == 0 (CANN page, axis validation); head_dim in {64, 128};
+ * max_seqlen_q/k equal to the true maxima of the host cu_seqlens (the CANN
+ * page leaves a mismatch undefined; here it is E_INVALID); causal in {0,1};
+ * win_left, win_right >= -1; dtype a sink_attn_dtype. */
+typedef struct {
+  int32_t batch, num_heads_q, num_heads_k, head_dim;
+  int32_t total_q, total_k, max_seqlen_q, max_seqlen_k;
+  int32_t causal, win_left, win_right;
+  int32_t dtype;
+} sink_attn_problem;
+
+/* Tile schedule ("CANN ops-transformer: flash_attn", Function section: a
+ * separate metadata call records the task split that the main call then
+ * uses). Host only, synchronous, touches no GPU.
+ *
+ * Reads the HOST copies of cu_seqlens_q/k ([batch+1] int32 each). Writes an
+ * int32 table into meta_host (capacity meta_capacity_words) and reports
+ * *meta_words (table size), *fwd_workspace_bytes and *bwd_workspace_bytes
+ * (device scratch the later calls need). Two-call protocol: with
+ * meta_host == NULL only the three sizes are written. The table holds a
+ * header that repeats every problem field, the tile sizes, and the work
+ * items: per (sequence, query tile) the range of key tiles with at least one
+ * kept element and, inside it, the range whose every element is kept; the
+ * same per (sequence, key tile) for the backward; and split-KV items for
+ * short query groups. Masked-out tiles are never visited. Copy the table
+ * unchanged to device memory (meta_dev) for fwd/bwd.
+ * Errors: E_INVALID (problem or cu_seqlens checks above, NULL pointers),
+ * E_UNSUPPORTED, E_BUFFER_TOO_SMALL (meta_capacity_words < *meta_words; the
+ * sizes are still written). */
+sink_attn_status sink_attn_metadata(const sink_attn_problem* p,
+                                    const int32_t* cu_seqlens_q_host,
+                                    const int32_t* cu_seqlens_k_host,
+                                    int32_t* meta_host,
+                                    int64_t meta_capacity_words,
+                                    int64_t* meta_words,
+                                    int64_t* fwd_workspace_bytes,
+                                    int64_t* bwd_workspace_bytes);
+
+/* Forward. Enqueues on `stream` and returns. meta_host is the table from
+ * sink_attn_metadata for this same problem (its header is compared with *p:
+ * E_META_MISMATCH), meta_dev its device copy. q, k, v, cu_seqlens_q/k,
+ * sink_logits (may be NULL = no sink), out, lse and workspace are device
+ * pointers; workspace must hold fwd_workspace_bytes (may be NULL when that
+ * is 0). scale must be finite and > 0 (the Python layer defaults it to
+ * 1/sqrt(head_dim), as the "slime" wrapper does). Writes out and lse.
+ * Errors: E_INVALID, E_UNSUPPORTED, E_META_MISMATCH, E_BUFFER_TOO_SMALL,
+ * E_HIP. */
+sink_attn_status sink_attn_fwd(const sink_attn_problem* p,
+                               const int32_t* meta_host,
+                               const int32_t* meta_dev,
+                               const void* q, const void* k, const void* v,
+                               const int32_t* cu_seqlens_q,
+                               const int32_t* cu_seqlens_k,
+                               const float* sink_logits, float scale,
+                               void* out, float* lse,
+                               void* workspace, int64_t workspace_bytes,
+                               hipStream_t stream);
+
+/* Backward. Same conventions as sink_attn_fwd. out and lse are what
+ * sink_attn_fwd wrote for the same inputs; dout has the layout of out.
+ * Writes dq, dk, dv (dtype) and dsink ([num_heads_q] fp32). dsink must be
+ * NULL exactly when sink_logits is NULL. workspace must hold
+ * bwd_workspace_bytes. dq accumulates through fp32 atomics, so its last bits
+ * may differ from run to run; dk, dv and dsink are deterministic.
+ * Errors: as sink_attn_fwd. */
+sink_attn_status sink_attn_bwd(const sink_attn_problem* p,
+                               const int32_t* meta_host,
+                               const int32_t* meta_dev,
+                               const void* dout, const void* q, const void* k,
+                               const void* v, const void* out, const float* lse,
+                               const int32_t* cu_seqlens_q,
+                               const int32_t* cu_seqlens_k,
+                               const float* sink_logits, float scale,
+                               void* dq, void* dk, void* dv, float* dsink,
+                               void* workspace, int64_t workspace_bytes,
+                               hipStream_t stream);
+
+/* Measurement aid: the next sink_attn_fwd or sink_attn_bwd made on this host
+ * thread records `start` just before and `stop` just after its main kernel
+ * (forward: the attention tile loop, or the split-KV kernel for short query
+ * groups; backward: the dQ/dK/dV tile loop), on its stream, and then
+ * disarms. Pass NULL, NULL to disarm. The events belong to the caller. */
+sink_attn_status sink_attn_arm_timing(hipEvent_t start, hipEvent_t stop);
+
+/* Static text for a status code. */
+const char* sink_attn_status_string(sink_attn_status s);
+
+/* SINK_ATTN_ABI_VERSION of the built library. */
+int32_t sink_attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SINK_ATTN_H */

@@ -1,0 +1,296 @@
+"""ctypes binding of libsinkattn.so (include/sink_attn.h).
+
+Argument marshalling only: every step of the computation runs in the
+library's HIP kernels; torch provides device memory and the stream. The
+functions ``sink_attn_metadata``, ``sink_attn_fwd``, ``sink_attn_bwd`` and
+``sink_attn_arm_timing`` mirror the C entry points one to one. ``Plan``,
+``forward``, ``backward``, ``SinkAttnFunction`` and
+``learnable_sink_attn_varlen`` are conveniences that allocate outputs and
+workspace with torch and call them.
+
+If the library has not been built the first call raises: there is no other
+path.
+"""
+import ctypes
+import math
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsinkattn.so")
+
+OK, E_INVALID, E_UNSUPPORTED, E_META_MISMATCH, E_BUFFER_TOO_SMALL, E_HIP = range(6)
+FP32, BF16 = 0, 1
+
+
+class SinkAttnError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "num_heads_q", "num_heads_k", "head_dim",
+        "total_q", "total_k", "max_seqlen_q", "max_seqlen_k",
+        "causal", "win_left", "win_right", "dtype")]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises when it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m softmax_sink_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        vp = ctypes.c_void_p
+        L.sink_attn_metadata.argtypes = [ctypes.POINTER(Problem), i32p, i32p, i32p,
+                                         ctypes.c_int64, i64p, i64p, i64p]
+        L.sink_attn_metadata.restype = ctypes.c_int
+        L.sink_attn_fwd.argtypes = [ctypes.POINTER(Problem), i32p, vp, vp, vp, vp, vp, vp,
+                                    vp, ctypes.c_float, vp, vp, vp, ctypes.c_int64, vp]
+        L.sink_attn_fwd.restype = ctypes.c_int
+        L.sink_attn_bwd.argtypes = [ctypes.POINTER(Problem), i32p, vp, vp, vp, vp, vp, vp,
+                                    vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp,
+                                    ctypes.c_int64, vp]
+        L.sink_attn_bwd.restype = ctypes.c_int
+        L.sink_attn_arm_timing.argtypes = [vp, vp]
+        L.sink_attn_arm_timing.restype = ctypes.c_int
+        L.sink_attn_status_string.argtypes = [ctypes.c_int]
+        L.sink_attn_status_string.restype = ctypes.c_char_p
+        L.sink_attn_abi_version.argtypes = []
+        L.sink_attn_abi_version.restype = ctypes.c_int32
+        _lib = L
+    return _lib
+
+
+def status_string(s):
+    return lib().sink_attn_status_string(int(s)).decode()
+
+
+def abi_version():
+    return lib().sink_attn_abi_version()
+
+
+def _i32p(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if a is not None else None
+
+
+def _ptr(t):
+    """Device pointer of a tensor (or an int address), None -> NULL."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def make_problem(cu_q, cu_k, num_heads_q, num_heads_k, head_dim, causal,
+                 win_left=-1, win_right=-1, dtype=BF16):
+    """Problem struct from host cu_seqlens (numpy int32)."""
+    cu_q = np.asarray(cu_q, dtype=np.int32)
+    cu_k = np.asarray(cu_k, dtype=np.int32)
+    lq, lk = np.diff(cu_q), np.diff(cu_k)
+    return Problem(len(cu_q) - 1, num_heads_q, num_heads_k, head_dim,
+                   int(cu_q[-1]), int(cu_k[-1]),
+                   int(lq.max()) if len(lq) else 0, int(lk.max()) if len(lk) else 0,
+                   int(bool(causal)), int(win_left), int(win_right), int(dtype))
+
+
+def sink_attn_metadata(problem, cu_seqlens_q_host, cu_seqlens_k_host):
+    """-> (meta int32 array, fwd_workspace_bytes, bwd_workspace_bytes)."""
+    L = lib()
+    cq = np.ascontiguousarray(cu_seqlens_q_host, dtype=np.int32)
+    ck = np.ascontiguousarray(cu_seqlens_k_host, dtype=np.int32)
+    words, fws, bws = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    st = L.sink_attn_metadata(ctypes.byref(problem), _i32p(cq), _i32p(ck), None, 0,
+                              ctypes.byref(words), ctypes.byref(fws), ctypes.byref(bws))
+    if st != OK:
+        raise SinkAttnError(st, "sink_attn_metadata")
+    meta = np.zeros(words.value, dtype=np.int32)
+    st = L.sink_attn_metadata(ctypes.byref(problem), _i32p(cq), _i32p(ck), _i32p(meta),
+                              words.value, ctypes.byref(words), ctypes.byref(fws),
+                              ctypes.byref(bws))
+    if st != OK:
+        raise SinkAttnError(st, "sink_attn_metadata")
+    return meta, fws.value, bws.value
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def sink_attn_fwd(problem, meta_host, meta_dev, q, k, v, cu_q, cu_k, sinks, scale,
+                  out, lse, workspace=None, workspace_bytes=0, stream=None,
+                  check=True):
+    st = lib().sink_attn_fwd(ctypes.byref(problem), _i32p(meta_host), _ptr(meta_dev),
+                             _ptr(q), _ptr(k), _ptr(v), _ptr(cu_q), _ptr(cu_k),
+                             _ptr(sinks), float(scale), _ptr(out), _ptr(lse),
+                             _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if check and st != OK:
+        raise SinkAttnError(st, "sink_attn_fwd")
+    return st
+
+
+def sink_attn_bwd(problem, meta_host, meta_dev, dout, q, k, v, out, lse, cu_q, cu_k,
+                  sinks, scale, dq, dk, dv, dsink, workspace=None, workspace_bytes=0,
+                  stream=None, check=True):
+    st = lib().sink_attn_bwd(ctypes.byref(problem), _i32p(meta_host), _ptr(meta_dev),
+                             _ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                             _ptr(cu_q), _ptr(cu_k), _ptr(sinks), float(scale),
+                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsink), _ptr(workspace),
+                             int(workspace_bytes), _stream(stream))
+    if check and st != OK:
+        raise SinkAttnError(st, "sink_attn_bwd")
+    return st
+
+
+def sink_attn_arm_timing(start, stop):
+    """start/stop: torch.cuda.Event (recorded by the next fwd/bwd call
+    around its main kernel) or None to disarm."""
+    def h(e):
+        if e is None:
+            return None
+        e.query()        # make sure torch has created the underlying event
+        return e.cuda_event
+    st = lib().sink_attn_arm_timing(h(start), h(stop))
+    if st != OK:
+        raise SinkAttnError(st, "sink_attn_arm_timing")
+
+
+# ---------------------------------------------------------------------------
+# Conveniences over the C entry points (allocation with torch only).
+# ---------------------------------------------------------------------------
+class Plan:
+    """Metadata for one packed batch: build once, use for fwd and bwd."""
+
+    def __init__(self, cu_seqlens_q, cu_seqlens_k, num_heads_q, num_heads_k,
+                 head_dim, causal, window=(-1, -1), dtype="bf16", device="cuda"):
+        import torch
+        self.cu_q_host = np.asarray(cu_seqlens_q, dtype=np.int32)
+        self.cu_k_host = np.asarray(cu_seqlens_k, dtype=np.int32)
+        self.dtype_code = BF16 if dtype in ("bf16", torch.bfloat16) else FP32
+        self.problem = make_problem(self.cu_q_host, self.cu_k_host, num_heads_q,
+                                    num_heads_k, head_dim, causal, window[0],
+                                    window[1], self.dtype_code)
+        self.meta, self.fwd_ws_bytes, self.bwd_ws_bytes = sink_attn_metadata(
+            self.problem, self.cu_q_host, self.cu_k_host)
+        self.device = device
+        self.meta_dev = torch.from_numpy(self.meta).to(device)
+        self.cu_q = torch.from_numpy(self.cu_q_host).to(device)
+        self.cu_k = torch.from_numpy(self.cu_k_host).to(device)
+
+    @property
+    def mode(self):
+        return int(self.meta[14])
+
+
+def _workspace(nbytes, device):
+    import torch
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def forward(plan, q, k, v, sinks, scale):
+    """-> out (q's dtype, THD), lse [Hq, Tq] fp32."""
+    import torch
+    out = torch.empty_like(q)
+    lse = torch.empty(plan.problem.num_heads_q, plan.problem.total_q,
+                      dtype=torch.float32, device=q.device)
+    ws = _workspace(plan.fwd_ws_bytes, q.device)
+    sink_attn_fwd(plan.problem, plan.meta, plan.meta_dev, q, k, v, plan.cu_q, plan.cu_k,
+                  sinks, scale, out, lse, ws, plan.fwd_ws_bytes)
+    return out, lse
+
+
+def backward(plan, dout, q, k, v, out, lse, sinks, scale):
+    """-> dq, dk, dv, dsink (dsink None without sinks)."""
+    import torch
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dsink = (torch.empty(plan.problem.num_heads_q, dtype=torch.float32, device=q.device)
+             if sinks is not None else None)
+    ws = _workspace(plan.bwd_ws_bytes, q.device)
+    sink_attn_bwd(plan.problem, plan.meta, plan.meta_dev, dout, q, k, v, out, lse,
+                  plan.cu_q, plan.cu_k, sinks, scale, dq, dk, dv, dsink, ws,
+                  plan.bwd_ws_bytes)
+    return dq, dk, dv, dsink
+
+
+def _autograd_function():
+    import torch
+
+    class SinkAttnFunction(torch.autograd.Function):
+        """Autograd wrapper with the argument order of the "slime" wrapper
+        (q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+        softmax_offset, softmax_scale, causal, window_size)."""
+
+        @staticmethod
+        def forward(ctx, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                    max_seqlen_k, softmax_offset, softmax_scale, causal, window_size):
+            plan = Plan(cu_seqlens_q.cpu().numpy(), cu_seqlens_k.cpu().numpy(),
+                        q.shape[1], k.shape[1], q.shape[2], causal, window_size,
+                        q.dtype, q.device)
+            if plan.problem.max_seqlen_q != max_seqlen_q or plan.problem.max_seqlen_k != max_seqlen_k:
+                raise SinkAttnError(E_INVALID, "max_seqlen does not match cu_seqlens")
+            q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+            sinks = softmax_offset.float().contiguous() if softmax_offset is not None else None
+            out, lse = forward(plan, q, k, v, sinks, softmax_scale)
+            ctx.save_for_backward(q, k, v, out, lse, sinks)
+            ctx.plan, ctx.scale = plan, softmax_scale
+            ctx.has_sink = softmax_offset is not None
+            ctx.offset_dtype = softmax_offset.dtype if softmax_offset is not None else None
+            return out
+
+        @staticmethod
+        def backward(ctx, dout):
+            q, k, v, out, lse, sinks = ctx.saved_tensors
+            dq, dk, dv, dsink = backward(ctx.plan, dout.contiguous(), q, k, v, out, lse,
+                                         sinks if ctx.has_sink else None, ctx.scale)
+            if dsink is not None:
+                dsink = dsink.to(ctx.offset_dtype)
+            return dq, dk, dv, None, None, None, None, dsink, None, None, None
+
+    return SinkAttnFunction
+
+
+_SAF = None
+
+
+def learnable_sink_attn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                               max_seqlen_k, softmax_offset, softmax_scale=None,
+                               causal=False, window_size=(-1, -1)):
+    """Packed (THD) attention with a learnable per-head sink logit; default
+    scale 1/sqrt(head_dim) as in the "slime" wrapper."""
+    global _SAF
+    if _SAF is None:
+        _SAF = _autograd_function()
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(q.shape[-1])
+    return _SAF.apply(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                      softmax_offset, softmax_scale, causal, tuple(window_size))
+
+
+def softmax_n_attn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                          max_seqlen_k, n, softmax_scale=None, causal=False,
+                          window_size=(-1, -1)):
+    """softmax_n attention ("Flash-Attention-Softmax-N" README): the sink logit
+    is ln n for every head (n = 0: no sink)."""
+    import torch
+    if n < 0:
+        raise ValueError("softmax_n needs n >= 0")
+    sinks = None if n == 0 else torch.full((q.shape[1],), math.log(n),
+                                          dtype=torch.float32, device=q.device)
+    return learnable_sink_attn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                                      max_seqlen_k, sinks, softmax_scale, causal,
+                                      window_size)

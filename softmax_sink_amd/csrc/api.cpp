@@ -1,0 +1,190 @@
+// C ABI of libsinkattn.so: argument checks, workspace carving and kernel
+// dispatch. Declarations and the contract are in include/sink_attn.h.
+#include <cmath>
+#include <cstdint>
+
+#include "sink_attn_internal.h"
+
+using namespace sinkattn;
+
+namespace {
+
+thread_local TimingHook g_timing;
+
+TimingHook take_timing() {
+  TimingHook t = g_timing;
+  g_timing = TimingHook{};
+  return t;
+}
+
+bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+int64_t header_i64(const int32_t* h, int lo, int hi) {
+  return static_cast<int64_t>(static_cast<uint32_t>(h[lo])) |
+         (static_cast<int64_t>(h[hi]) << 32);
+}
+
+sink_attn_status common_checks(const sink_attn_problem* p,
+                               const int32_t* meta_host,
+                               const int32_t* meta_dev, float scale) {
+  sink_attn_status st = validate_problem(p);
+  if (st != SINK_ATTN_OK) return st;
+  if (!meta_host || !meta_dev) return SINK_ATTN_E_INVALID;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return SINK_ATTN_E_INVALID;
+  return check_header(*p, meta_host);
+}
+
+}  // namespace
+
+extern "C" {
+
+sink_attn_status sink_attn_metadata(const sink_attn_problem* p,
+                                    const int32_t* cu_seqlens_q_host,
+                                    const int32_t* cu_seqlens_k_host,
+                                    int32_t* meta_host,
+                                    int64_t meta_capacity_words,
+                                    int64_t* meta_words,
+                                    int64_t* fwd_workspace_bytes,
+                                    int64_t* bwd_workspace_bytes) {
+  sink_attn_status st = validate_problem(p);
+  if (st != SINK_ATTN_OK) return st;
+  if (!meta_words || !fwd_workspace_bytes || !bwd_workspace_bytes)
+    return SINK_ATTN_E_INVALID;
+  st = validate_cu_seqlens(*p, cu_seqlens_q_host, cu_seqlens_k_host);
+  if (st != SINK_ATTN_OK) return st;
+  if (meta_host && meta_capacity_words < 0) return SINK_ATTN_E_INVALID;
+  return build_metadata(*p, cu_seqlens_q_host, cu_seqlens_k_host, meta_host,
+                        meta_capacity_words, meta_words, fwd_workspace_bytes,
+                        bwd_workspace_bytes);
+}
+
+sink_attn_status sink_attn_fwd(const sink_attn_problem* p,
+                               const int32_t* meta_host,
+                               const int32_t* meta_dev, const void* q,
+                               const void* k, const void* v,
+                               const int32_t* cu_seqlens_q,
+                               const int32_t* cu_seqlens_k,
+                               const float* sink_logits, float scale,
+                               void* out, float* lse, void* workspace,
+                               int64_t workspace_bytes, hipStream_t stream) {
+  sink_attn_status st = common_checks(p, meta_host, meta_dev, scale);
+  if (st != SINK_ATTN_OK) return st;
+  if (!q || !k || !v || !out || !lse || !cu_seqlens_q || !cu_seqlens_k)
+    return SINK_ATTN_E_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      !aligned16(lse))
+    return SINK_ATTN_E_INVALID;
+  const int64_t need = header_i64(meta_host, kFwdWsLo, kFwdWsHi);
+  if (workspace_bytes < need) return SINK_ATTN_E_BUFFER_TOO_SMALL;
+  if (need > 0 && (!workspace || !aligned16(workspace))) return SINK_ATTN_E_INVALID;
+
+  const int mode = meta_host[kMode];
+  FwdArgs a{};
+  a.q = q; a.k = k; a.v = v;
+  a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
+  a.sinks = sink_logits;
+  a.out = out; a.lse = lse;
+  a.batch = p->batch; a.hq = p->num_heads_q; a.hk = p->num_heads_k;
+  a.group = p->num_heads_q / p->num_heads_k;
+  a.causal = p->causal; a.win_left = p->win_left; a.win_right = p->win_right;
+  a.total_q = p->total_q; a.total_k = p->total_k;
+  a.scale = scale;
+  const TimingHook t = take_timing();
+  hipError_t e;
+  if (p->dtype == SINK_ATTN_FP32) {
+    e = launch_fwd_f32(a, p->head_dim, stream, t);
+  } else if (mode == kModeDecode) {
+    const FwdWorkspace w = fwd_workspace_layout(meta_host[kDecRows], p->head_dim,
+                                                p->dtype, mode);
+    char* base = static_cast<char*>(workspace);
+    a.items = meta_dev + meta_host[kDecOff];
+    a.n_items = meta_host[kNDec];
+    a.dec_seq = meta_dev + meta_host[kDecSeqOff];
+    a.ws_o = reinterpret_cast<float*>(base + w.o_off);
+    a.ws_m = reinterpret_cast<float*>(base + w.m_off);
+    a.ws_l = reinterpret_cast<float*>(base + w.l_off);
+    e = launch_fwd_bf16(a, p->head_dim, mode, stream, t);
+  } else {
+    a.items = meta_dev + meta_host[kFwdOff];
+    a.n_items = meta_host[kNFwd];
+    e = launch_fwd_bf16(a, p->head_dim, mode, stream, t);
+  }
+  return e == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_E_HIP;
+}
+
+sink_attn_status sink_attn_bwd(const sink_attn_problem* p,
+                               const int32_t* meta_host,
+                               const int32_t* meta_dev, const void* dout,
+                               const void* q, const void* k, const void* v,
+                               const void* out, const float* lse,
+                               const int32_t* cu_seqlens_q,
+                               const int32_t* cu_seqlens_k,
+                               const float* sink_logits, float scale, void* dq,
+                               void* dk, void* dv, float* dsink,
+                               void* workspace, int64_t workspace_bytes,
+                               hipStream_t stream) {
+  sink_attn_status st = common_checks(p, meta_host, meta_dev, scale);
+  if (st != SINK_ATTN_OK) return st;
+  if (!dout || !q || !k || !v || !out || !lse || !cu_seqlens_q ||
+      !cu_seqlens_k || !dq || !dk || !dv)
+    return SINK_ATTN_E_INVALID;
+  if ((sink_logits == nullptr) != (dsink == nullptr)) return SINK_ATTN_E_INVALID;
+  if (!aligned16(dout) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
+      !aligned16(out) || !aligned16(lse) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv))
+    return SINK_ATTN_E_INVALID;
+  const int64_t need = header_i64(meta_host, kBwdWsLo, kBwdWsHi);
+  if (workspace_bytes < need) return SINK_ATTN_E_BUFFER_TOO_SMALL;
+  if (need > 0 && (!workspace || !aligned16(workspace))) return SINK_ATTN_E_INVALID;
+
+  const int64_t pre_blocks = meta_host[kBwdPreBlocks];
+  const BwdWorkspace w = bwd_workspace_layout(p->total_q, p->num_heads_q,
+                                              p->head_dim, p->dtype, pre_blocks);
+  char* base = static_cast<char*>(workspace);
+  BwdArgs a{};
+  a.dout = dout; a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
+  a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k; a.sinks = sink_logits;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dsink = dsink;
+  a.items = meta_dev + meta_host[kBwdOff];
+  a.n_items = meta_host[kNBwd];
+  a.pre_blocks = static_cast<int>(pre_blocks);
+  a.dval = reinterpret_cast<float*>(base + w.dval_off);
+  a.part = reinterpret_cast<float*>(base + w.part_off);
+  a.dq_acc = p->dtype == SINK_ATTN_BF16
+                 ? reinterpret_cast<float*>(base + w.dqacc_off) : nullptr;
+  a.batch = p->batch; a.hq = p->num_heads_q; a.hk = p->num_heads_k;
+  a.group = p->num_heads_q / p->num_heads_k;
+  a.causal = p->causal; a.win_left = p->win_left; a.win_right = p->win_right;
+  a.total_q = p->total_q; a.total_k = p->total_k;
+  a.scale = scale;
+  const TimingHook t = take_timing();
+  hipError_t e = p->dtype == SINK_ATTN_FP32
+                     ? launch_bwd_f32(a, p->head_dim, stream, t)
+                     : launch_bwd_bf16(a, p->head_dim, stream, t);
+  return e == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_E_HIP;
+}
+
+sink_attn_status sink_attn_arm_timing(hipEvent_t start, hipEvent_t stop) {
+  if ((start == nullptr) != (stop == nullptr)) return SINK_ATTN_E_INVALID;
+  g_timing.start = start;
+  g_timing.stop = stop;
+  return SINK_ATTN_OK;
+}
+
+const char* sink_attn_status_string(sink_attn_status s) {
+  switch (s) {
+    case SINK_ATTN_OK: return "ok";
+    case SINK_ATTN_E_INVALID: return "invalid argument";
+    case SINK_ATTN_E_UNSUPPORTED: return "unsupported head_dim or dtype";
+    case SINK_ATTN_E_META_MISMATCH: return "metadata does not match the call";
+    case SINK_ATTN_E_BUFFER_TOO_SMALL: return "buffer too small";
+    case SINK_ATTN_E_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t sink_attn_abi_version(void) { return SINK_ATTN_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,175 @@
+// Device-side building blocks for gfx950 (CDNA4): MFMA fragments, LDS tile
+// swizzle, transposed LDS reads, wave-half exchange, exp2/log2.
+//
+// Lane layouts (checked on the hardware with an in-bounds probe):
+//  * v_mfma_f32_32x32x16_bf16: lane l holds A[m = l%32][k = 8(l/32)+i] and
+//    B[k = 8(l/32)+i][n = l%32], i = 0..7; the 16 results of lane l are
+//    C[8(r/4) + 4(l/32) + r%4][l%32], r = 0..15.
+//  * ds_read_b64_tr_b16: in each group of 16 lanes, lane 4a+c supplies the
+//    address of 4 consecutive 16-bit elements (row a of a 4x16 block,
+//    columns 4c..4c+3); lane n of the group receives column n of the 4 rows.
+//  * v_permlane32_swap: returns (own, partner) for lanes 0..31 and
+//    (partner, own) for lanes 32..63, where partner = lane ^ 32.
+//
+// Because every MFMA sums over its K slots, the order in which keys (or
+// queries) are assigned to K slots is free as long as both operands agree.
+// The kernels use the slot order that the 32x32 result layout produces:
+// K slot i of lane half hl in chunk t is row 16t + 8(i/4) + 4hl + i%4. A
+// probability tile computed as an MFMA result is then directly the B operand
+// of the next MFMA, and the other operand is read with two transposed LDS
+// reads (rows 16t + 4hl + e and 16t + 8 + 4hl + e).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace sinkattn {
+namespace dev {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 2^x with the hardware v_exp_f32 (exact at -inf -> 0); e^x is obtained by
+// the caller as 2^(x log2 e).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+// log2 with the hardware v_log_f32 (x > 0).
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value held by lane ^ 32.
+__device__ __forceinline__ float half_partner(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                            false, false);
+  const int lane = threadIdx.x & 63;
+  return __uint_as_float(lane < 32 ? r[1] : r[0]);
+}
+
+__device__ __forceinline__ float half_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                            false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// ---------------------------------------------------------------------------
+// LDS tiles of bf16 rows (D elements = D/8 16-byte chunks per row), stored
+// without padding; the 16-byte chunk c of row r sits at chunk c ^ f(r).
+// f makes both access patterns conflict-free over the 64 4-byte banks:
+//   (a) 16 lanes reading the same chunk of 16 consecutive rows (ds_read_b128);
+//   (b) a transposed read of 4 consecutive rows x 64 contiguous bytes.
+// D = 128 (256-byte rows): f = 4(r%4) + (r/4)%4, a permutation of 0..15 on
+//   any 16 consecutive rows whose upper two bits differ on 4 consecutive rows.
+// D = 64 (128-byte rows, two rows per bank sweep): f = 4((r/2)%2) + (r/4)%4.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// Byte offset of element (r, col) (col a multiple of 4 elements).
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int col) {
+  const int chunk = col >> 3;
+  return r * (D * 2) + ((chunk ^ swz<D>(r)) << 4) + ((col & 7) << 1);
+}
+
+// 16-byte chunk (8 elements starting at column 8*chunk) of row r.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_row_chunk(const char* tile, int r, int chunk) {
+  return *reinterpret_cast<const bf16x8*>(tile + r * (D * 2) +
+                                          ((chunk ^ swz<D>(r)) << 4));
+}
+
+template <int D>
+__device__ __forceinline__ void lds_store_chunk(char* tile, int r, int chunk, u32x4 v) {
+  *reinterpret_cast<u32x4*>(tile + r * (D * 2) + ((chunk ^ swz<D>(r)) << 4)) = v;
+}
+
+__device__ __forceinline__ s16x4 ds_read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+}
+
+// MFMA operand whose K slots run down the rows of an LDS tile (rows
+// row0 + 8(i/4) + 4hl + i%4, i = 0..7) and whose M/N index is column
+// col0 + lane%32: two transposed reads.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_col_operand(const char* tile, int row0, int col0) {
+  const int lane = threadIdx.x & 63;
+  const int grp = lane >> 4;          // 16-lane group
+  const int hl = grp >> 1;            // lane half
+  const int nu = lane & 15;
+  const int r = row0 + 4 * hl + (nu >> 2);
+  const int col = col0 + 16 * (grp & 1) + 4 * (nu & 3);
+  s16x4 lo = ds_read_tr(tile + tile_off<D>(r, col));
+  s16x4 hi = ds_read_tr(tile + tile_off<D>(r + 8, col));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Eight fp32 values -> bf16x8, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3,
+                                        float a4, float a5, float a6, float a7) {
+  bf16x8 r = {(bf16)a0, (bf16)a1, (bf16)a2, (bf16)a3,
+              (bf16)a4, (bf16)a5, (bf16)a6, (bf16)a7};
+  return r;
+}
+
+// Slots 8h..8h+7 of a 32x32 result fragment as the next MFMA's operand.
+__device__ __forceinline__ bf16x8 frag_half(const f32x16& c, int h) {
+  return pack8(c[8 * h + 0], c[8 * h + 1], c[8 * h + 2], c[8 * h + 3],
+               c[8 * h + 4], c[8 * h + 5], c[8 * h + 6], c[8 * h + 7]);
+}
+
+__device__ __forceinline__ u32x2 pack4_bits(float a, float b, float c, float d) {
+  bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Global 16-byte load / store helpers.
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Kept key interval [jlo, jhi] of query row i (bottom-right aligned, clipped
+// to [0, lk-1]); an empty interval has jhi < jlo.
+__device__ __forceinline__ void row_key_range(int i, int lq, int lk, int causal,
+                                              int wl, int wr, int& jlo, int& jhi) {
+  const int pos = i + lk - lq;
+  jlo = wl >= 0 ? max(0, pos - wl) : 0;
+  int hi = lk - 1;
+  if (causal) hi = min(hi, pos);
+  else if (wr >= 0) hi = min(hi, pos + wr);
+  jhi = hi;
+  if (i >= lq) jhi = -1;
+}
+
+// Query rows [ilo, ihi] that keep key j (inverse of row_key_range).
+__device__ __forceinline__ void key_row_range(int j, int lq, int lk, int causal,
+                                              int wl, int wr, int& ilo, int& ihi) {
+  const int off = lk - lq;
+  int lo = 0, hi = lq - 1;
+  if (causal) lo = max(lo, j - off);
+  else if (wr >= 0) lo = max(lo, j - off - wr);
+  if (wl >= 0) hi = min(hi, j - off + wl);
+  if (j >= lk) hi = -1;
+  ilo = lo;
+  ihi = hi;
+}
+
+}  // namespace dev
+}  // namespace sinkattn

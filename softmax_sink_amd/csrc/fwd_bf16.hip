@@ -1,0 +1,448 @@
+// Forward kernels, bf16 inputs, fp32 softmax state, for gfx950.
+//
+// Method: "slime: learnable_softmax_attention.py" (module docstring) defines
+// the probabilities as softmax over [scores, sink] with the sink column
+// dropped; "CANN ops-transformer: flash_attn" (Formula section) writes the
+// same thing in max-stabilised form m = max(sink, max S). The tile loop
+// keeps that form online: the running max starts at the sink logit and the
+// running denominator at e^(sink - m) = 1, so the sink enters exactly once
+// and the tiles only ever add real keys -- the virtual logit / zero-value
+// sink of "hf-attention-normalizers" (Important Limitations). The returned
+// lse includes the sink; the backward recomputes P = e^(S - lse) from it.
+//
+// Prefill kernel (one work item = 128 query rows of one (sequence, q-head)):
+// 4 waves x 32 rows. Per 64-key tile, K and V are staged HBM -> LDS
+// (double buffered, 16-byte coalesced loads, swizzled rows) and each wave
+// computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so that every lane
+// owns one query row: the row max needs one exchange with lane ^ 32, the
+// rescale factor is a per-lane scalar, and the probabilities are already the
+// B operand of O^T += V^T P^T (V^T read with ds_read_b64_tr_b16). Only tiles
+// that the schedule marks partial evaluate the mask.
+//
+// Split-KV kernel (short query groups): one work item = one (sequence,
+// kv-head, key chunk); all (query row, q-head of the group) pairs, at most
+// 64, share every K/V tile, which is read from HBM exactly once. Each item
+// writes unnormalised partial (O, m, l) without the sink; the combine kernel
+// merges the chunks by their maxima and adds e^(sink) once.
+#include "device_common.h"
+#include "sink_attn_internal.h"
+
+namespace sinkattn {
+namespace {
+
+using namespace dev;
+
+// Stage a [64 x D] bf16 tile of rows [row0, row0 + 64) of a THD tensor
+// (row stride `stride` elements) into registers; rows >= nrows read as 0.
+template <int D>
+struct TileLoader {
+  static constexpr int kChunks = 64 * D / 8;           // 16-byte chunks per tile
+  static constexpr int kPerThread = kChunks / 256;     // 4 (D=128) or 2 (D=64)
+  u32x4 r[kPerThread];
+  __device__ __forceinline__ void load(const bf16* base, int64_t stride, int row0,
+                                       int nrows) {
+#pragma unroll
+    for (int s = 0; s < kPerThread; ++s) {
+      const int u = threadIdx.x + 256 * s;
+      const int row = u / (D / 8), c = u % (D / 8);
+      if (row0 + row < nrows)
+        r[s] = ld16(base + (int64_t)(row0 + row) * stride + c * 8);
+      else
+        r[s] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ __forceinline__ void store(char* tile) const {
+#pragma unroll
+    for (int s = 0; s < kPerThread; ++s) {
+      const int u = threadIdx.x + 256 * s;
+      lds_store_chunk<D>(tile, u / (D / 8), u % (D / 8), r[s]);
+    }
+  }
+};
+
+// Head index for the j-th slot of the head-fastest block numbering. Blocks
+// are spread over the 8 XCDs round robin (block id mod 8); with this map the
+// q-heads of one kv group -- which read the same K/V -- share an XCD and
+// its L2 whenever Hq is a multiple of 8.
+__device__ __forceinline__ int head_of_slot(int j, int hq) {
+  if ((hq & 7) == 0) return (j & 7) * (hq >> 3) + (j >> 3);
+  return j;
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdArgs a) {
+  constexpr int BN = kFwdBN;
+  constexpr int NT = D / 16;            // K chunks of the QK^T product
+  constexpr int NB = D / 32;            // 32-column blocks of O^T
+  constexpr int TILE = BN * D * 2;      // bytes per K or V tile
+  __shared__ __attribute__((aligned(16))) char lds[2][2 * TILE];
+
+  const int item = blockIdx.x / a.hq;
+  const int h = head_of_slot(blockIdx.x % a.hq, a.hq);
+  const int* it = a.items + item * kItemWords;
+  const int b = it[0], qt = it[1], kt_lo = it[2], kt_hi = it[3];
+  const int kf_lo = it[4], kf_hi = it[5];
+  const int q0 = a.cu_q[b], lq = a.cu_q[b + 1] - q0;
+  const int k0 = a.cu_k[b], lk = a.cu_k[b + 1] - k0;
+  const int hk = h / a.group;
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int hl = lane >> 5, c = lane & 31;
+  const int i = qt * kFwdBM + w * 32 + c;     // this lane's query row
+
+  const int64_t qstride = (int64_t)a.hq * D;
+  const int64_t kstride = (int64_t)a.hk * D;
+  const bf16* qp = static_cast<const bf16*>(a.q) + (int64_t)q0 * qstride + h * D;
+  const bf16* kp = static_cast<const bf16*>(a.k) + (int64_t)k0 * kstride + hk * D;
+  const bf16* vp = static_cast<const bf16*>(a.v) + (int64_t)k0 * kstride + hk * D;
+
+  // Q as the B operand of S^T = K Q^T: lane (hl, c) holds Q[i][16t + 8hl .. +7]
+  bf16x8 qf[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (i < lq) qf[t] = __builtin_bit_cast(bf16x8, ld16(qp + (int64_t)i * qstride + 16 * t + 8 * hl));
+    else qf[t] = bf16x8{};
+  }
+
+  const float sink = a.sinks ? a.sinks[h] : kNegInf;
+  const float c2 = a.scale * kLog2e;         // scores -> log2 domain
+  float m = sink * kLog2e;                   // running max (log2 domain)
+  float l = (hl == 0 && sink > kNegInf) ? 1.f : 0.f;   // e^(sink - m), counted once
+  f32x16 o[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) o[n] = f32x16{};
+
+  int jlo, jhi;
+  row_key_range(i, lq, lk, a.causal, a.win_left, a.win_right, jlo, jhi);
+
+  TileLoader<D> kl, vl;
+  if (kt_lo < kt_hi) {
+    kl.load(kp, kstride, kt_lo * BN, lk);
+    vl.load(vp, kstride, kt_lo * BN, lk);
+    kl.store(lds[0]);
+    vl.store(lds[0] + TILE);
+  }
+  __syncthreads();
+
+  for (int kt = kt_lo; kt < kt_hi; ++kt) {
+    const int cur = (kt - kt_lo) & 1;
+    const bool more = kt + 1 < kt_hi;
+    if (more) {
+      kl.load(kp, kstride, (kt + 1) * BN, lk);
+      vl.load(vp, kstride, (kt + 1) * BN, lk);
+    }
+    const char* kt_lds = lds[cur];
+    const char* vt_lds = lds[cur] + TILE;
+
+    // S^T for the two 32-key blocks of the tile
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        bf16x8 kf = lds_row_chunk<D>(kt_lds, kb * 32 + c, 2 * t + hl);
+        s[kb] = mfma32(kf, qf[t], s[kb]);
+      }
+    }
+
+    // mask (partial tiles only): key of slot r is kt*BN + 32kb + 8(r/4) + 4hl + r%4
+    if (kt < kf_lo || kt >= kf_hi) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = kt * BN + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (j < jlo || j > jhi) s[kb][r] = kNegInf;
+        }
+    }
+
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = half_max(mx);
+    const float m_new = fmaxf(m, mx * c2);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = exp2_hw(m - m_use);
+    m = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2_hw(__builtin_fmaf(s[kb][r], c2, -m_use));
+        s[kb][r] = p;
+        psum += p;
+      }
+    l = l * alpha + psum;
+    if (!__all(alpha == 1.f)) {
+#pragma unroll
+      for (int n = 0; n < NB; ++n) o[n] *= alpha;
+    }
+
+    // O^T += V^T P^T over the 4 16-key chunks of the tile
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const bf16x8 pf = frag_half(s[t >> 1], t & 1);
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        const bf16x8 vf = lds_col_operand<D>(vt_lds, 16 * t, 32 * n);
+        o[n] = mfma32(vf, pf, o[n]);
+      }
+    }
+
+    if (more) {
+      kl.store(lds[cur ^ 1]);
+      vl.store(lds[cur ^ 1] + TILE);
+    }
+    __syncthreads();
+  }
+
+  // epilogue: out = O / l, lse = m + log2(l) (natural log), sink included
+  const float lt = l + half_partner(l);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (i < lq) {
+    bf16* op = static_cast<bf16*>(a.out) + (int64_t)(q0 + i) * qstride + h * D;
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * n + 8 * g + 4 * hl;
+        *reinterpret_cast<u32x2*>(op + d) =
+            pack4_bits(o[n][4 * g] * inv, o[n][4 * g + 1] * inv,
+                       o[n][4 * g + 2] * inv, o[n][4 * g + 3] * inv);
+      }
+    if (hl == 0)
+      a.lse[(int64_t)h * a.total_q + q0 + i] = lt > 0.f ? (m + log2_hw(lt)) * kLn2 : kNegInf;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split-KV forward for short query groups.
+// Wave w: query block qb = w & 1 (rows 32qb..32qb+31 of the group), key half
+// kh = w >> 1 (keys 32kh..32kh+31 of each 64-key tile). Group row r = g*Lq+i
+// is query row i of q-head hk*G + g.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256, 2) void fwd_split_kernel(FwdArgs a) {
+  constexpr int BN = kDecBN;
+  constexpr int NT = D / 16;
+  constexpr int NB = D / 32;
+  constexpr int TILE = BN * D * 2;
+  __shared__ __attribute__((aligned(16))) char lds[2][2 * TILE];
+
+  const int item = blockIdx.x / a.hk;
+  const int hk = blockIdx.x % a.hk;
+  const int* it = a.items + item * kItemWords;
+  const int b = it[0], k_lo = it[2], k_hi = it[3], row_base = it[4];
+  const int q0 = a.cu_q[b], lq = a.cu_q[b + 1] - q0;
+  const int k0 = a.cu_k[b], lk = a.cu_k[b + 1] - k0;
+  const int G = a.group;
+  const int rows = lq * G;
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int hl = lane >> 5, c = lane & 31;
+  const int qb = w & 1, kh = w >> 1;
+  const int r = qb * 32 + c;                 // this lane's group row
+  const int g = lq > 0 ? r / lq : 0, i = lq > 0 ? r % lq : 0;
+  const int h = hk * G + g;
+
+  const int64_t qstride = (int64_t)a.hq * D;
+  const int64_t kstride = (int64_t)a.hk * D;
+  const bf16* kp = static_cast<const bf16*>(a.k) + (int64_t)k0 * kstride + hk * D;
+  const bf16* vp = static_cast<const bf16*>(a.v) + (int64_t)k0 * kstride + hk * D;
+
+  bf16x8 qf[NT];
+  const bool live_row = r < rows;
+  const bf16* qrow = static_cast<const bf16*>(a.q) + (int64_t)(q0 + i) * qstride + h * D;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    qf[t] = live_row ? __builtin_bit_cast(bf16x8, ld16(qrow + 16 * t + 8 * hl)) : bf16x8{};
+
+  int jlo, jhi;
+  row_key_range(i, lq, lk, a.causal, a.win_left, a.win_right, jlo, jhi);
+  if (!live_row) jhi = -1;
+
+  const float c2 = a.scale * kLog2e;
+  float m = kNegInf, l = 0.f;
+  f32x16 o[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) o[n] = f32x16{};
+
+  const int nt = (k_hi - k_lo + BN - 1) / BN;
+  TileLoader<D> kl, vl;
+  if (nt > 0) {
+    kl.load(kp, kstride, k_lo, k_hi);
+    vl.load(vp, kstride, k_lo, k_hi);
+    kl.store(lds[0]);
+    vl.store(lds[0] + TILE);
+  }
+  __syncthreads();
+
+  for (int n_t = 0; n_t < nt; ++n_t) {
+    const int cur = n_t & 1;
+    const bool more = n_t + 1 < nt;
+    const int base = k_lo + n_t * BN;
+    if (more) {
+      kl.load(kp, kstride, base + BN, k_hi);
+      vl.load(vp, kstride, base + BN, k_hi);
+    }
+    const char* kt_lds = lds[cur];
+    const char* vt_lds = lds[cur] + TILE;
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      bf16x8 kf = lds_row_chunk<D>(kt_lds, kh * 32 + c, 2 * t + hl);
+      s = mfma32(kf, qf[t], s);
+    }
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int j = base + kh * 32 + 8 * (rr >> 2) + 4 * hl + (rr & 3);
+      if (j < jlo || j > jhi) s[rr] = kNegInf;
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[rr]);
+    mx = half_max(mx);
+    const float m_new = fmaxf(m, mx * c2);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = exp2_hw(m - m_use);
+    m = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const float p = exp2_hw(__builtin_fmaf(s[rr], c2, -m_use));
+      s[rr] = p;
+      psum += p;
+    }
+    l = l * alpha + psum;
+    if (!__all(alpha == 1.f)) {
+#pragma unroll
+      for (int n = 0; n < NB; ++n) o[n] *= alpha;
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const bf16x8 pf = frag_half(s, t);
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        const bf16x8 vf = lds_col_operand<D>(vt_lds, kh * 32 + 16 * t, 32 * n);
+        o[n] = mfma32(vf, pf, o[n]);
+      }
+    }
+    if (more) {
+      kl.store(lds[cur ^ 1]);
+      vl.store(lds[cur ^ 1] + TILE);
+    }
+    __syncthreads();
+  }
+
+  // merge the two key halves: waves 2,3 hand (m, l, O) to waves 0,1
+  l = l + half_partner(l);
+  float* xo = reinterpret_cast<float*>(lds[0]);        // [2 waves][NB*16][64 lanes]
+  float* xm = xo + 2 * NB * 16 * 64;                   // [2 waves][64 lanes]
+  float* xl = xm + 2 * 64;
+  if (kh == 1) {
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) xo[(qb * NB * 16 + n * 16 + rr) * 64 + lane] = o[n][rr];
+    xm[qb * 64 + lane] = m;
+    xl[qb * 64 + lane] = l;
+  }
+  __syncthreads();
+  if (kh == 0 && live_row) {
+    const float m1 = xm[qb * 64 + lane], l1 = xl[qb * 64 + lane];
+    const float mt = fmaxf(m, m1);
+    const float mu = mt == kNegInf ? 0.f : mt;
+    const float f0 = exp2_hw(m - mu), f1 = exp2_hw(m1 - mu);
+    const int prow = row_base + h * lq + i;
+    float* po = a.ws_o + (int64_t)prow * D;
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d = 32 * n + 8 * gq + 4 * hl;
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[e] = o[n][4 * gq + e] * f0 + xo[(qb * NB * 16 + n * 16 + 4 * gq + e) * 64 + lane] * f1;
+        *reinterpret_cast<f32x4*>(po + d) = v;
+      }
+    if (hl == 0) {
+      a.ws_m[prow] = mt;
+      a.ws_l[prow] = l * f0 + l1 * f1;
+    }
+  }
+}
+
+// One wave per (token, q-head) row: merge the chunk partials of its sequence
+// by their maxima, add the sink once, normalise.
+template <int D>
+__global__ __launch_bounds__(256) void fwd_combine_kernel(FwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.total_q * a.hq) return;
+  const int t = row / a.hq, h = row % a.hq;
+  int lo = 0, hi = a.batch;                     // sequence of token t
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.cu_q[mid] <= t) lo = mid; else hi = mid;
+  }
+  const int b = lo;
+  const int q0 = a.cu_q[b], lq = a.cu_q[b + 1] - q0, i = t - q0;
+  const int first = a.dec_seq[2 * b], n = a.dec_seq[2 * b + 1];
+  const float sink = a.sinks ? a.sinks[h] : kNegInf;
+  float mt = sink * kLog2e;
+  for (int s = 0; s < n; ++s) {
+    const int prow = a.items[(first + s) * kItemWords + 4] + h * lq + i;
+    mt = fmaxf(mt, a.ws_m[prow]);
+  }
+  const float mu = mt == kNegInf ? 0.f : mt;
+  float lt = exp2_hw(sink * kLog2e - mu);
+  constexpr int PER = D / 64;
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  for (int s = 0; s < n; ++s) {
+    const int prow = a.items[(first + s) * kItemWords + 4] + h * lq + i;
+    const float f = exp2_hw(a.ws_m[prow] - mu);
+    lt += a.ws_l[prow] * f;
+    const float* po = a.ws_o + (int64_t)prow * D + lane * PER;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] += po[e] * f;
+  }
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  bf16* op = static_cast<bf16*>(a.out) + ((int64_t)t * a.hq + h) * D + lane * PER;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) op[e] = (bf16)(acc[e] * inv);
+  if (lane == 0)
+    a.lse[(int64_t)h * a.total_q + t] = lt > 0.f ? (mt + log2_hw(lt)) * kLn2 : kNegInf;
+}
+
+template <int D>
+hipError_t launch_fwd_d(const FwdArgs& a, int mode, hipStream_t s, const TimingHook& th) {
+  if (mode == kModeDecode) {
+    if (th.start) hipEventRecord(th.start, s);
+    if (a.n_items > 0)
+      hipLaunchKernelGGL(fwd_split_kernel<D>, dim3(a.n_items * a.hk), dim3(256), 0, s, a);
+    if (th.stop) hipEventRecord(th.stop, s);
+    const int rows = a.total_q * a.hq;
+    hipLaunchKernelGGL(fwd_combine_kernel<D>, dim3((rows + 3) / 4), dim3(256), 0, s, a);
+  } else {
+    if (th.start) hipEventRecord(th.start, s);
+    hipLaunchKernelGGL(fwd_prefill_kernel<D>, dim3(a.n_items * a.hq), dim3(256), 0, s, a);
+    if (th.stop) hipEventRecord(th.stop, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mode, hipStream_t s,
+                           const TimingHook& t) {
+  return head_dim == 128 ? launch_fwd_d<128>(a, mode, s, t)
+                         : launch_fwd_d<64>(a, mode, s, t);
+}
+
+}  // namespace sinkattn

@@ -1,0 +1,132 @@
+// Internal declarations shared by the host scheduler, the C ABI layer and
+// the kernel launchers of libsinkattn.so.
+#pragma once
+
+#include <cstdint>
+#include <hip/hip_runtime_api.h>
+
+#include "../../include/sink_attn.h"
+
+namespace sinkattn {
+
+// ---------------------------------------------------------------------------
+// Metadata table: kHeaderWords int32 header words, then the item arrays.
+// ---------------------------------------------------------------------------
+enum MetaWord : int {
+  kMagic = 0, kVersion, kBatch, kHq, kHk, kHeadDim, kTq, kTk, kMaxQ, kMaxK,
+  kCausal, kWinL, kWinR, kDtype, kMode,
+  kWordFwdBM, kWordFwdBN, kWordBwdBM, kWordBwdBN, kWordDecBN, kWordDecChunk,
+  kNFwd, kFwdOff, kNBwd, kBwdOff, kNDec, kDecOff, kDecSeqOff, kDecRows,
+  kFwdWsLo, kFwdWsHi, kBwdWsLo, kBwdWsHi, kCuHash, kMetaWords,
+  kBwdPreBlocks,
+  kHeaderWords = 48
+};
+
+constexpr int32_t kMagicValue = 0x4B4E4953;  // "SINK" little-endian
+constexpr int kItemWords = 8;
+
+// Forward item:  b, qt, kt_lo, kt_hi, kf_lo, kf_hi, 0, 0
+// Backward item: b, kt, qt_lo, qt_hi, qf_lo, qf_hi, 0, 0
+// Decode item:   b, split, k_lo, k_hi, row_base, 0, 0, 0
+// Decode per-sequence table (2 words per sequence): first item, count.
+
+enum Mode : int32_t { kModePrefill = 0, kModeDecode = 1 };
+
+// Tile shapes of the bf16 kernels (recorded in the header; the kernels are
+// compiled for exactly these values and the ABI layer checks them).
+constexpr int kFwdBM = 128;    // query rows per forward work item (4 waves x 32)
+constexpr int kFwdBN = 64;     // keys per forward tile step
+constexpr int kBwdBM = 64;     // query rows per backward tile step
+constexpr int kBwdBN = 128;    // keys per backward work item (4 waves x 32)
+constexpr int kDecBN = 64;     // keys per split-KV tile step
+constexpr int kDecChunk = 2048;// keys per split-KV work item
+constexpr int kDecMaxRows = 64;// (query rows x GQA group) handled per split item
+constexpr int kPreRows = 64;   // tokens per block of the backward preprocess
+
+inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// Workspace layouts (byte offsets), derived from the header only.
+struct FwdWorkspace {
+  int64_t o_off, m_off, l_off, bytes;
+};
+struct BwdWorkspace {
+  int64_t dval_off, part_off, dqacc_off, bytes;
+};
+FwdWorkspace fwd_workspace_layout(int64_t dec_rows, int head_dim, int dtype,
+                                  int mode);
+BwdWorkspace bwd_workspace_layout(int64_t total_q, int hq, int head_dim,
+                                  int dtype, int64_t pre_blocks);
+
+// Host checks and the schedule builder (schedule.cpp).
+sink_attn_status validate_problem(const sink_attn_problem* p);
+sink_attn_status validate_cu_seqlens(const sink_attn_problem& p,
+                                     const int32_t* cu_q, const int32_t* cu_k);
+// Builds the table; writes it when `out` is non-null and capacity allows.
+sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
+                                const int32_t* cu_k, int32_t* out,
+                                int64_t capacity, int64_t* words,
+                                int64_t* fwd_ws, int64_t* bwd_ws);
+sink_attn_status check_header(const sink_attn_problem& p, const int32_t* meta);
+
+// ---------------------------------------------------------------------------
+// Kernel arguments and launchers (kernels_*.hip).
+// ---------------------------------------------------------------------------
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const float* sinks;       // null: no sink
+  void* out;
+  float* lse;
+  const int32_t* items;     // device: forward or decode items
+  const int32_t* dec_seq;   // device: decode per-sequence table
+  float* ws_o;              // decode partials
+  float* ws_m;
+  float* ws_l;
+  int n_items;
+  int batch, hq, hk, group, causal, win_left, win_right;
+  int total_q, total_k;
+  float scale;
+};
+
+struct BwdArgs {
+  const void* dout;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const float* lse;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const float* sinks;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dsink;
+  const int32_t* items;     // device: backward items
+  float* dval;              // [hq, total_q]
+  float* part;              // [hq, pre_blocks]
+  float* dq_acc;            // [total_q, hq, head_dim] (bf16 path)
+  int n_items, pre_blocks;
+  int batch, hq, hk, group, causal, win_left, win_right;
+  int total_q, total_k;
+  float scale;
+};
+
+struct TimingHook {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mode,
+                           hipStream_t s, const TimingHook& t);
+hipError_t launch_bwd_bf16(const BwdArgs& a, int head_dim, hipStream_t s,
+                           const TimingHook& t);
+hipError_t launch_fwd_f32(const FwdArgs& a, int head_dim, hipStream_t s,
+                          const TimingHook& t);
+hipError_t launch_bwd_f32(const BwdArgs& a, int head_dim, hipStream_t s,
+                          const TimingHook& t);
+
+}  // namespace sinkattn

@@ -1,0 +1,74 @@
+"""Helpers for the GPU parity tests: move seeded problems to the device,
+run the HIP path through the C ABI binding, compare with the oracle."""
+import sys
+
+import numpy as np
+import torch
+
+import oracle as O
+from softmax_sink_amd import binding as B
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(p, name):
+    x = getattr(p, name)
+    if p.dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def dev_sinks(p):
+    return torch.from_numpy(np.ascontiguousarray(p.sinks)).cuda()
+
+
+class GpuRun:
+    """Device copies of a workloads.Problem and the HIP results on them."""
+
+    def __init__(self, p, with_sink=True):
+        self.p = p
+        self.plan = B.Plan(p.cu_q, p.cu_k, p.num_heads_q, p.num_heads_k, p.head_dim,
+                           p.causal, (p.win_left, p.win_right), p.dtype)
+        self.q, self.k, self.v = to_dev(p, "q"), to_dev(p, "k"), to_dev(p, "v")
+        self.sinks = dev_sinks(p) if with_sink else None
+        self.scale = float(p.scale)
+
+    def fwd(self):
+        self.out, self.lse = B.forward(self.plan, self.q, self.k, self.v, self.sinks, self.scale)
+        torch.cuda.synchronize()
+        return self.out.float().cpu().numpy().astype(np.float64), self.lse.cpu().numpy().astype(np.float64)
+
+    def bwd(self):
+        self.dout = to_dev(self.p, "dout")
+        dq, dk, dv, ds = B.backward(self.plan, self.dout, self.q, self.k, self.v, self.out,
+                                    self.lse, self.sinks, self.scale)
+        torch.cuda.synchronize()
+        f = lambda t: t.float().cpu().numpy().astype(np.float64)
+        return f(dq), f(dk), f(dv), (ds.cpu().numpy().astype(np.float64) if ds is not None else None)
+
+
+def oracle_inputs(p, with_sink=True):
+    sinks = p.sinks.astype(np.float64) if with_sink else np.full(p.num_heads_q, -np.inf)
+    return (p.as_f32("q"), p.as_f32("k"), p.as_f32("v"), p.cu_q, p.cu_k, sinks,
+            float(p.scale), p.causal, p.win_left, p.win_right)
+
+
+def max_abs(a, b):
+    a, b = np.asarray(a), np.asarray(b)
+    both_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
+    d = np.where(both_inf, 0.0, np.abs(a - b))
+    return float(np.max(d)) if d.size else 0.0
+
+
+def rel_l2(a, b):
+    num = np.linalg.norm((np.asarray(a) - np.asarray(b)).ravel())
+    den = np.linalg.norm(np.asarray(b).ravel())
+    return float(num / den) if den > 0 else float(num)
+
+
+# tolerances stated for the method: fp32 out/lse max abs 1e-5; bf16 out max
+# abs 1e-2, lse max abs 1e-3, gradients relative L2 2e-2
+TOL = {"fp32": dict(out=1e-5, lse=1e-5, grad=1e-5), "bf16": dict(out=1e-2, lse=1e-3, grad=2e-2)}

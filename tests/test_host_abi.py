@@ -1,0 +1,204 @@
+"""The C ABI on the host (no GPU): exported symbols, argument checks and
+error codes, and the tile schedule compared bit for bit with the oracle's
+brute-force bookkeeping."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from softmax_sink_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "sink_attn.h")
+
+# header word indices / tile shapes as laid out by the library
+W_MODE, W_FWDBM, W_FWDBN, W_BWDBM, W_BWDBN, W_DECBN, W_DECCHUNK = 14, 15, 16, 17, 18, 19, 20
+W_NFWD, W_FWDOFF, W_NBWD, W_BWDOFF, W_NDEC, W_DECOFF, W_DECSEQ, W_DECROWS = range(21, 29)
+
+
+@pytest.fixture(scope="module")
+def L():
+    return B.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    text = open(HDR).read()
+    names = set(re.findall(r"\b(sink_attn_[a-z_]+)\s*\(", text))
+    assert {"sink_attn_metadata", "sink_attn_fwd", "sink_attn_bwd",
+            "sink_attn_status_string", "sink_attn_abi_version",
+            "sink_attn_arm_timing"} <= names
+    for n in names:
+        assert hasattr(L, n), n
+    assert B.abi_version() == 1
+    for s in range(6):
+        assert isinstance(B.status_string(s), str)
+
+
+def _meta(cu_q, cu_k, hq=4, hk=2, d=128, causal=True, wl=-1, wr=-1, dtype=B.BF16):
+    p = B.make_problem(cu_q, cu_k, hq, hk, d, causal, wl, wr, dtype)
+    return p, B.sink_attn_metadata(p, cu_q, cu_k)
+
+
+def _items(meta, n_word, off_word, width=6):
+    n, off = meta[n_word], meta[off_word]
+    return [tuple(int(x) for x in meta[off + 8 * i: off + 8 * i + width]) for i in range(n)]
+
+
+def _check_against_oracle(cu_q, cu_k, causal, wl, wr, hq=4, hk=2):
+    cu_q = np.asarray(cu_q, np.int32)
+    cu_k = np.asarray(cu_k, np.int32)
+    p, (meta, fws, bws) = _meta(cu_q, cu_k, hq, hk, 128, causal, wl, wr)
+    fbm, fbn, bbm, bbn = meta[W_FWDBM], meta[W_FWDBN], meta[W_BWDBM], meta[W_BWDBN]
+    assert _items(meta, W_NFWD, W_FWDOFF) == O.forward_items(cu_q, cu_k, fbm, fbn, causal, wl, wr)
+    assert _items(meta, W_NBWD, W_BWDOFF) == O.backward_items(cu_q, cu_k, bbm, bbn, causal, wl, wr)
+    ditems, per_seq = O.decode_items(cu_q, cu_k, meta[W_DECBN], meta[W_DECCHUNK], causal, wl, wr)
+    assert _items(meta, W_NDEC, W_DECOFF, 4) == ditems
+    seq = meta[meta[W_DECSEQ]: meta[W_DECSEQ] + 2 * (len(cu_q) - 1)].reshape(-1, 2)
+    assert [tuple(int(x) for x in r) for r in seq] == per_seq
+    # partial-row bases: running sum of (query rows x q-heads) over the items
+    bases = [int(meta[meta[W_DECOFF] + 8 * i + 4]) for i in range(meta[W_NDEC])]
+    want, acc = [], 0
+    for b, _, _, _ in ditems:
+        want.append(acc)
+        acc += int(cu_q[b + 1] - cu_q[b]) * hq
+    assert bases == want and meta[W_DECROWS] == acc
+    return meta
+
+
+def test_schedule_matches_oracle_random():
+    rng = np.random.default_rng(123)
+    for trial in range(60):
+        Bn = int(rng.integers(1, 6))
+        lq = rng.integers(0, 300, Bn)
+        lk = rng.integers(0, 300, Bn)
+        if trial % 3 == 0:
+            lk = lq.copy()
+        lq[0] = max(1, lq[0]); lk[0] = max(1, lk[0])
+        causal = bool(rng.integers(0, 2))
+        wl = int(rng.choice([-1, 0, 1, 17, 64, 200]))
+        wr = 0 if causal and rng.integers(0, 2) else (-1 if causal else int(rng.choice([-1, 0, 5, 100])))
+        cu_q = np.r_[0, np.cumsum(lq)].astype(np.int32)
+        cu_k = np.r_[0, np.cumsum(lk)].astype(np.int32)
+        _check_against_oracle(cu_q, cu_k, causal, wl, wr)
+
+
+def test_schedule_matches_oracle_on_workload_lengths():
+    rng = np.random.default_rng(2)
+    lens = rng.integers(64, 2049, 16)
+    cu = np.r_[0, np.cumsum(lens)].astype(np.int32)
+    m = _check_against_oracle(cu, cu, True, -1, -1, 32, 32)
+    assert m[W_MODE] == 0
+    cu4 = np.arange(0, 32769, 8192, dtype=np.int32)
+    _check_against_oracle(cu4, cu4, True, 1024, 0, 64, 8)
+    rng = np.random.default_rng(5)
+    lq, lk = rng.integers(1, 17, 64), rng.integers(512, 32769, 64)
+    m = _check_against_oracle(np.r_[0, np.cumsum(lq)].astype(np.int32),
+                              np.r_[0, np.cumsum(lk)].astype(np.int32), True, -1, -1, 32, 8)
+    assert m[W_MODE] == 1          # 16 rows x 4 heads fit one split-KV group
+
+
+def test_metadata_two_call_protocol_and_sizes(L):
+    cu = np.array([0, 100, 300], np.int32)
+    p = B.make_problem(cu, cu, 8, 2, 128, True)
+    words, fws, bws = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    st = L.sink_attn_metadata(ctypes.byref(p), B._i32p(cu), B._i32p(cu), None, 0,
+                              ctypes.byref(words), ctypes.byref(fws), ctypes.byref(bws))
+    assert st == B.OK and words.value > 48
+    small = np.zeros(10, np.int32)
+    st = L.sink_attn_metadata(ctypes.byref(p), B._i32p(cu), B._i32p(cu), B._i32p(small), 10,
+                              ctypes.byref(words), ctypes.byref(fws), ctypes.byref(bws))
+    assert st == B.E_BUFFER_TOO_SMALL
+    meta, f, b = B.sink_attn_metadata(p, cu, cu)
+    assert meta[0] == 0x4B4E4953 and meta[1] == 1 and len(meta) == words.value
+    # bwd workspace: D [Hq,Tq] + partials + fp32 dQ accumulator
+    assert b >= 300 * 8 * 4 + 300 * 8 * 128 * 4
+    assert f == 0       # prefill mode needs no forward scratch
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("batch", 0, B.E_INVALID), ("batch", 70000, B.E_INVALID),
+    ("num_heads_q", 6, B.E_INVALID),           # not a multiple of num_heads_k = 4
+    ("num_heads_k", 0, B.E_INVALID),
+    ("head_dim", 96, B.E_UNSUPPORTED), ("dtype", 7, B.E_UNSUPPORTED),
+    ("win_left", -2, B.E_INVALID), ("win_right", 3, B.E_INVALID),   # causal + right window
+    ("causal", 2, B.E_INVALID), ("max_seqlen_q", 99, B.E_INVALID),
+    ("max_seqlen_k", 201, B.E_INVALID), ("total_q", 299, B.E_INVALID),
+    ("total_k", 0, B.E_INVALID),
+])
+def test_metadata_rejects(field, value, status):
+    cu = np.array([0, 100, 300], np.int32)
+    p = B.make_problem(cu, cu, 8, 4, 128, True)
+    setattr(p, field, value)
+    with pytest.raises(B.SinkAttnError) as e:
+        B.sink_attn_metadata(p, cu, cu)
+    assert e.value.status == status
+
+
+def test_metadata_rejects_bad_cu_seqlens():
+    p = B.make_problem([0, 5, 9], [0, 5, 9], 2, 2, 64, False)
+    for cq in ([1, 5, 9], [0, 6, 5], [0, 5, 8]):
+        with pytest.raises(B.SinkAttnError) as e:
+            B.sink_attn_metadata(p, np.array(cq, np.int32), np.array([0, 5, 9], np.int32))
+        assert e.value.status == B.E_INVALID
+
+
+def test_zero_length_sequences_allowed():
+    cu_q = np.array([0, 0, 7, 7, 12], np.int32)
+    cu_k = np.array([0, 3, 3, 9, 20], np.int32)
+    _check_against_oracle(cu_q, cu_k, True, -1, -1)
+    _check_against_oracle(cu_q, cu_k, False, 2, 1)
+
+
+FAKE = 0x10000  # an aligned, never-dereferenced address: every call below fails its checks first
+
+
+def _fwd(p, meta, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, cu_q=FAKE, cu_k=FAKE, sinks=FAKE, scale=0.1,
+                out=FAKE, lse=FAKE, workspace=None, workspace_bytes=0)
+    args.update(kw)
+    return B.sink_attn_fwd(p, meta, FAKE, args["q"], args["k"], args["v"], args["cu_q"],
+                           args["cu_k"], args["sinks"], args["scale"], args["out"],
+                           args["lse"], args["workspace"], args["workspace_bytes"],
+                           stream=0, check=False)
+
+
+def _bwd(p, meta, **kw):
+    args = dict(dout=FAKE, q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, cu_q=FAKE,
+                cu_k=FAKE, sinks=FAKE, scale=0.1, dq=FAKE, dk=FAKE, dv=FAKE, dsink=FAKE,
+                workspace=FAKE, workspace_bytes=1 << 40)
+    args.update(kw)
+    a = args
+    return B.sink_attn_bwd(p, meta, FAKE, a["dout"], a["q"], a["k"], a["v"], a["out"],
+                           a["lse"], a["cu_q"], a["cu_k"], a["sinks"], a["scale"], a["dq"],
+                           a["dk"], a["dv"], a["dsink"], a["workspace"],
+                           a["workspace_bytes"], stream=0, check=False)
+
+
+def test_fwd_bwd_argument_checks():
+    cu = np.array([0, 40, 100], np.int32)
+    p, (meta, fws, bws) = _meta(cu, cu, 4, 2, 128, True)
+    assert _fwd(p, meta, q=None) == B.E_INVALID
+    assert _fwd(p, meta, lse=FAKE + 4) == B.E_INVALID          # misaligned
+    assert _fwd(p, meta, scale=0.0) == B.E_INVALID
+    assert _fwd(p, meta, scale=float("nan")) == B.E_INVALID
+    assert _fwd(p, None) == B.E_INVALID
+    other = B.make_problem(cu, cu, 4, 2, 128, False)
+    assert _fwd(other, meta) == B.E_META_MISMATCH
+    bad = meta.copy(); bad[0] ^= 1
+    assert _fwd(p, bad) == B.E_META_MISMATCH
+    assert _bwd(p, meta, dsink=None) == B.E_INVALID            # sink given, dsink missing
+    assert _bwd(p, meta, sinks=None) == B.E_INVALID
+    assert _bwd(p, meta, workspace_bytes=bws - 1) == B.E_BUFFER_TOO_SMALL
+    assert _bwd(p, meta, dq=None) == B.E_INVALID
+    assert _bwd(other, meta) == B.E_META_MISMATCH
+    # decode-mode forward needs its split-KV scratch
+    cq = np.array([0, 3, 5], np.int32); ck = np.array([0, 900, 3000], np.int32)
+    p2, (meta2, fws2, _) = _meta(cq, ck, 8, 2, 128, True)
+    assert meta2[W_MODE] == 1 and fws2 > 0
+    assert _fwd(p2, meta2, workspace=FAKE, workspace_bytes=fws2 - 1) == B.E_BUFFER_TOO_SMALL
+    assert _fwd(p2, meta2, workspace=None, workspace_bytes=fws2) == B.E_INVALID
+    assert B.lib().sink_attn_arm_timing(FAKE, None) == B.E_INVALID
+    assert B.lib().sink_attn_arm_timing(None, None) == B.OK
