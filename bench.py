@@ -1,0 +1,230 @@
+"""Throughput of packed (THD) sink attention on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                [--no-cpu-baseline]
+
+One step = the whole hot path over one batch: the host tile schedule
+(sink_attn_metadata) and its copy to the device, the forward
+(sink_attn_fwd) and, for training workloads, the backward (sink_attn_bwd),
+all through the C ABI on torch's current stream. Inputs are resident in HBM
+before timing starts. Prints one JSON line.
+
+FLOPs count only kept (query row, key, q-head) pairs: 4*D per pair forward,
+10*D backward (the backward recomputes S). Bytes (decode) count K and V read
+once plus q, out, lse.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+METRIC = "sink-attention fwd+bwd TFLOP/s and % of bf16 MFMA peak, varlen THD causal"
+TRAIN = {"train_varlen", "gqa_window"}
+
+
+def kept_pairs(cu_q, cu_k, causal, wl, wr):
+    """Kept (row, key) pairs per head, counted row by row from the
+    bottom-right aligned mask bounds."""
+    total = 0
+    for b in range(len(cu_q) - 1):
+        lq, lk = int(cu_q[b + 1] - cu_q[b]), int(cu_k[b + 1] - cu_k[b])
+        if lq == 0 or lk == 0:
+            continue
+        pos = np.arange(lq, dtype=np.int64) + (lk - lq)
+        lo = np.maximum(0, pos - wl) if wl >= 0 else np.zeros(lq, np.int64)
+        if causal:
+            hi = np.minimum(lk - 1, pos)
+        elif wr >= 0:
+            hi = np.minimum(lk - 1, pos + wr)
+        else:
+            hi = np.full(lq, lk - 1, np.int64)
+        total += int(np.maximum(0, hi - lo + 1).sum())
+    return total
+
+
+def to_dev(p, name):
+    import torch
+    x = np.ascontiguousarray(getattr(p, name))
+    if p.dtype == "bf16":
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(x).cuda()
+
+
+def cpu_baseline(p, train, seconds_hint):
+    """The fp64 oracle on the host over a bounded sample of the workload:
+    one (sequence, q-head) slice, forward (+ backward for training)."""
+    import oracle as O
+    from threadpoolctl import threadpool_info
+    lens = np.diff(p.cu_q)
+    b = int(np.argsort(lens)[len(lens) // 2])        # a median-length sequence
+    sub = p.sub_batch([b])
+    h = 0
+    hk = h // (p.num_heads_q // p.num_heads_k)
+    args = (sub.as_f32("q")[:, h:h + 1], sub.as_f32("k")[:, hk:hk + 1],
+            sub.as_f32("v")[:, hk:hk + 1], sub.cu_q, sub.cu_k,
+            sub.sinks[h:h + 1].astype(np.float64), float(p.scale), p.causal,
+            p.win_left, p.win_right)
+    pairs = kept_pairs(sub.cu_q, sub.cu_k, p.causal, p.win_left, p.win_right)
+    t0 = time.perf_counter()
+    if train:
+        O.sink_attention_backward(sub.as_f32("dout")[:, h:h + 1], *args)
+    else:
+        O.sink_attention_forward(*args)
+    dt = time.perf_counter() - t0
+    flops = pairs * p.head_dim * (14 if train else 4)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"sequence {b} (Lq={int(lens[b])}), q-head {h}: "
+                      f"{'forward+backward' if train else 'forward'}, {pairs} kept pairs, "
+                      f"{dt:.1f} s on {os.cpu_count()} host cpus"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="train_varlen")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from softmax_sink_amd import binding as B
+    from softmax_sink_amd import workloads as W
+
+    torch.cuda.set_device(0)
+    p = W.config(args.workload)
+    train = args.workload in TRAIN
+    decode = args.workload == "decode_softmax_n"
+    D, Hq, Hk = p.head_dim, p.num_heads_q, p.num_heads_k
+    q, k, v = to_dev(p, "q"), to_dev(p, "k"), to_dev(p, "v")
+    dout = to_dev(p, "dout") if train else None
+    sinks = torch.from_numpy(p.sinks).cuda()
+    scale = float(p.scale)
+    dtype_code = B.BF16 if p.dtype == "bf16" else B.FP32
+    problem = B.make_problem(p.cu_q, p.cu_k, Hq, Hk, D, p.causal, p.win_left, p.win_right,
+                             dtype_code)
+    cu_q_dev = torch.from_numpy(p.cu_q).cuda()
+    cu_k_dev = torch.from_numpy(p.cu_k).cuda()
+    meta0, fws, bws = B.sink_attn_metadata(problem, p.cu_q, p.cu_k)
+    # two pinned host / device metadata buffers, alternated across steps
+    meta_host = [torch.empty(len(meta0), dtype=torch.int32).pin_memory() for _ in range(2)]
+    meta_dev = [torch.empty(len(meta0), dtype=torch.int32, device="cuda") for _ in range(2)]
+    copied = [None, None]
+    out = torch.empty_like(q)
+    lse = torch.empty(Hq, p.total_q, dtype=torch.float32, device="cuda")
+    fwd_ws = torch.empty(max(fws, 1), dtype=torch.uint8, device="cuda")
+    if train:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dsink = torch.empty(Hq, dtype=torch.float32, device="cuda")
+        bwd_ws = torch.empty(max(bws, 1), dtype=torch.uint8, device="cuda")
+    cq = np.ascontiguousarray(p.cu_q)
+    ck = np.ascontiguousarray(p.cu_k)
+    main_events = []
+
+    def step(n, timed):
+        slot = n & 1
+        if copied[slot] is not None:
+            copied[slot].synchronize()       # the host buffer is free again
+        mh = meta_host[slot].numpy()
+        m, _, _ = B.sink_attn_metadata(problem, cq, ck)
+        mh[:] = m
+        meta_dev[slot].copy_(meta_host[slot], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record()
+        copied[slot] = ev
+        if timed:
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            B.sink_attn_arm_timing(s0, s1)
+        B.sink_attn_fwd(problem, mh, meta_dev[slot], q, k, v, cu_q_dev, cu_k_dev, sinks,
+                        scale, out, lse, fwd_ws, fws)
+        if timed and not train:
+            main_events.append(("fwd", s0, s1))
+        if train:
+            if timed:
+                b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                B.sink_attn_arm_timing(b0, b1)
+                main_events.append(("fwd", s0, s1))
+            B.sink_attn_bwd(problem, mh, meta_dev[slot], dout, q, k, v, out, lse, cu_q_dev,
+                            cu_k_dev, sinks, scale, dq, dk, dv, dsink, bwd_ws, bws)
+            if timed:
+                main_events.append(("bwd", b0, b1))
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(args.steps):
+        step(args.warmup + i, True)
+        print(f"# step {i + 1}/{args.steps} enqueued", file=sys.stderr, flush=True)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+
+    pairs = kept_pairs(p.cu_q, p.cu_k, p.causal, p.win_left, p.win_right) * Hq
+    fwd_flops = 4.0 * D * pairs
+    bwd_flops = 10.0 * D * pairs
+    step_flops = fwd_flops + (bwd_flops if train else 0.0)
+    value = step_flops / (ms * 1e-3) / 1e12
+    kms = {}
+    for name, a, b in main_events:
+        kms.setdefault(name, []).append(a.elapsed_time(b))
+    kavg = {n: float(np.mean(x)) for n, x in kms.items()}
+    esize = 2 if p.dtype == "bf16" else 4
+    if decode:
+        kv_bytes = 2.0 * p.total_k * Hk * D * esize
+        qo_bytes = 2.0 * p.total_q * Hq * D * esize + 4.0 * p.total_q * Hq
+        alg_bytes = kv_bytes + qo_bytes
+        achieved = alg_bytes / (kavg["fwd"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "fwd_split_kernel", "achieved": achieved,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                "traffic": None, "launch_ms": kavg["fwd"]}
+    else:
+        name = "bwd" if train else "fwd"
+        flops = bwd_flops if train else fwd_flops
+        peak = PEAK_BF16_TFLOPS if p.dtype == "bf16" else PEAK_FP32_TFLOPS
+        achieved = flops / (kavg[name] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": "bwd_main_kernel" if train else "fwd_prefill_kernel",
+                "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": None, "launch_ms": kavg[name]}
+    res = {
+        "metric": METRIC if train else f"sink-attention forward {'GB/s' if decode else 'TFLOP/s'}",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": p.dtype, "data": "synthetic",
+        "config": {"workload": args.workload, "batch": p.batch, "total_q": p.total_q,
+                   "total_k": p.total_k, "heads_q": Hq, "heads_kv": Hk, "head_dim": D,
+                   "causal": p.causal, "window": [p.win_left, p.win_right],
+                   "seed": p.seed, "kept_pairs": pairs,
+                   "passes": "metadata+fwd+bwd" if train else "metadata+fwd"},
+        "frac_of_bf16_peak": value / PEAK_BF16_TFLOPS,
+        "main_kernel_ms": kavg,
+        "roofline": roof,
+    }
+    if decode:
+        res["value_gbs"] = alg_bytes / (ms * 1e-3) / 1e9
+    if not args.no_cpu_baseline:
+        print("# timing the oracle on the host", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(p, train, 20)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -245,6 +245,32 @@ def sink_attention_backward(dout, q, k, v, cu_q, cu_k, sinks, scale, causal,
     return dq, dk, dv, dsink
 
 
+def sink_attention_dsink(dout, q, k, v, cu_q, cu_k, sinks, scale, causal,
+                         win_left=-1, win_right=-1, block_rows=512, heads=None):
+    """Only the sink gradient, [Hq] (NaN for heads not computed): the
+    forward per slice, then dsink_h = -sum_i p_sink,i (dO_i . out_i) -- the
+    same sum _slice_backward forms, without the dq/dk/dv products."""
+    cu_q, cu_k, G = _check_problem(q, k, v, cu_q, cu_k, sinks)
+    Hq = q.shape[1]
+    dsink = np.full(Hq, np.nan)
+    heads = range(Hq) if heads is None else heads
+    for h in heads:
+        dsink[h] = 0.0
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        keep = keep_mask(q1 - q0, k1 - k0, causal, win_left, win_right)
+        for h in heads:
+            hk = h // G
+            for r0, r1, j0, j1 in _row_blocks(keep, block_rows):
+                f = _slice_forward(_f64(q[q0 + r0:q0 + r1, h]),
+                                   _f64(k[k0 + j0:k0 + j1, hk]),
+                                   _f64(v[k0 + j0:k0 + j1, hk]),
+                                   float(sinks[h]), scale, keep[r0:r1, j0:j1])
+                D = (_f64(dout[q0 + r0:q0 + r1, h]) * f["out"]).sum(axis=1)
+                dsink[h] += float(-(f["p_sink"] * D).sum())
+    return dsink
+
+
 def sink_attention_rows(q, k, v, cu_q, cu_k, sinks, scale, causal,
                         win_left, win_right, rows, dout=None):
     """Forward (and, with ``dout``, the dq row) for sampled (token, q-head)

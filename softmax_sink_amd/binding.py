@@ -161,8 +161,8 @@ def sink_attn_arm_timing(start, stop):
     def h(e):
         if e is None:
             return None
-        e.query()        # make sure torch has created the underlying event
-        return e.cuda_event
+        e.record()       # torch creates the event on first record; the
+        return e.cuda_event  # library records it again around its kernel
     st = lib().sink_attn_arm_timing(h(start), h(stop))
     if st != OK:
         raise SinkAttnError(st, "sink_attn_arm_timing")

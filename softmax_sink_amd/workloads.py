@@ -36,8 +36,11 @@ _CHUNK = 1 << 24
 def round_to_bf16_bits(x):
     """fp32 array -> uint16 bf16 bit patterns, round to nearest even.
     Inputs are finite normal draws (no NaN handling needed)."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (u >> 16) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u                       # finite inputs: no wrap-around
+    r >>= np.uint32(16)
     return r.astype(np.uint16)
 
 

@@ -429,3 +429,13 @@ def test_items_cover_every_kept_element():
                 for _, _, a, c in mine:
                     got[a:c] = True
                 assert not (colkeep & ~got).any()
+
+
+def test_dsink_only_matches_full_backward():
+    rng = np.random.default_rng(24)
+    cu = [0, 7, 19]
+    q = _rand(rng, 19, 4, 8); k = _rand(rng, 19, 2, 8); v = _rand(rng, 19, 2, 8)
+    dout = _rand(rng, 19, 4, 8); sinks = np.array([0.3, -0.2, -np.inf, 1.0])
+    full = O.sink_attention_backward(dout, q, k, v, cu, cu, sinks, 0.4, True, 3, 0)[3]
+    only = O.sink_attention_dsink(dout, q, k, v, cu, cu, sinks, 0.4, True, 3, 0, block_rows=4)
+    np.testing.assert_allclose(only, full, rtol=1e-12, atol=1e-15)
