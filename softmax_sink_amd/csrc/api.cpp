@@ -149,11 +149,11 @@ sink_attn_status sink_attn_bwd(const sink_attn_problem* p,
   a.dq = dq; a.dk = dk; a.dv = dv; a.dsink = dsink;
   a.items = meta_dev + meta_host[kBwdOff];
   a.n_items = meta_host[kNBwd];
+  a.items_q = meta_dev + meta_host[kFwdOff];
+  a.n_items_q = meta_host[kNFwd];
   a.pre_blocks = static_cast<int>(pre_blocks);
   a.dval = reinterpret_cast<float*>(base + w.dval_off);
   a.part = reinterpret_cast<float*>(base + w.part_off);
-  a.dq_acc = p->dtype == SINK_ATTN_BF16
-                 ? reinterpret_cast<float*>(base + w.dqacc_off) : nullptr;
   a.batch = p->batch; a.hq = p->num_heads_q; a.hk = p->num_heads_k;
   a.group = p->num_heads_q / p->num_heads_k;
   a.causal = p->causal; a.win_left = p->win_left; a.win_right = p->win_right;

@@ -9,16 +9,24 @@
 // Probabilities are recomputed from lse, never stored ("hf-attention-
 // normalizers", Important Limitations: recompute in the fused backward).
 //
-// Main kernel: one work item = 128 keys of one (sequence, kv-head); wave w
-// owns keys 32w..32w+31 and keeps its K and V fragments in registers and
-// its dK^T, dV^T accumulators in fp32. It walks the live 64-row query tiles
-// of every q-head of the GQA group:
-//   S  = Q K^T,  dP = dO V^T        (M = query, N = key; Q, dO from LDS)
-//   P  = 2^(S scale log2e - lse log2e), dS = scale P (dP - D)
-//   dV^T += dO^T P,  dK^T += Q^T dS (dO^T, Q^T by transposed LDS reads)
-//   dQ += dS K over the item's 128 keys (dS^T staged in LDS), added to an
-//   fp32 accumulator with atomics; a final pass converts it to bf16.
+// Two kernels, neither with atomics:
+//  * dK/dV (key-tile outer): one work item = 128 keys of one (sequence,
+//    kv-head), walking the live 64-row query tiles of every q-head of the
+//    GQA group; per step
+//      S = Q K^T, dP = dO V^T (M = query, N = key; Q, dO from LDS)
+//      P = 2^(S scale log2e - lse log2e), dS = scale P (dP - D)
+//      dV^T += dO^T P, dK^T += Q^T dS (dO^T, Q^T by transposed LDS reads)
+//    split over two wave roles (see bwd_dkdv_kernel).
+//  * dQ (query-tile outer, the shape of the forward kernel): one work item =
+//    128 query rows of one (sequence, q-head); each lane owns a query row,
+//    so lse and D are per-lane scalars; per 64-key tile
+//      S^T = K Q^T, dP^T = V dO^T, dS^T as above, dQ^T += K^T dS^T.
+//    Recomputing S and dP here costs 4*D more MFMA work per pair than an
+//    atomic dQ update inside the first kernel, and replaces 2.4e9 fp32
+//    atomics (plus a zeroed fp32 accumulator) on the long causal workloads;
+//    it also makes dQ deterministic.
 #include "bwd_common.h"
+#include "tile_common.h"
 
 namespace sinkattn {
 namespace {
@@ -26,24 +34,23 @@ namespace {
 using namespace dev;
 
 template <int D>
-struct BwdSmem {
-  static constexpr int kK = kBwdBN * D * 2;       // K tile [128][D]
+struct KvSmem {
   static constexpr int kQ = kBwdBM * D * 2;       // Q tile [64][D]
-  static constexpr int kDO = kBwdBM * D * 2;      // dO tile
-  static constexpr int kDS = kBwdBN * kBwdBM * 2; // dS^T tile [128 keys][64 q]
-  static constexpr int off_k = 0;
-  static constexpr int off_q = off_k + kK;
-  static constexpr int off_do = off_q + kQ;
-  static constexpr int off_ds = off_do + kDO;
-  static constexpr int off_lse = off_ds + kDS;    // [64] fp32, log2 domain
+  static constexpr int off_q = 0;
+  static constexpr int off_do = off_q + kQ;       // dO tile
+  static constexpr int off_lse = off_do + kQ;     // [64] fp32, log2 domain
   static constexpr int off_dv = off_lse + 256;    // [64] fp32
-  static constexpr int bytes = off_dv + 256;
+  static constexpr int stage = off_dv + 256;      // one buffer
+  static constexpr int off_p = 2 * stage;         // P^T [128 keys][64 q] fp32
+  static constexpr int bytes = off_p + kBwdBN * kBwdBM * 4;
 };
+
+constexpr int kKvThreads = 512;                   // 8 waves: 4 key slices x 2 roles
 
 // Registers holding the next (q-head, query tile) step's Q, dO, lse, D.
 template <int D>
 struct QTileLoader {
-  static constexpr int kPer = kBwdBM * D / 8 / 256;   // 16-byte chunks per thread
+  static constexpr int kPer = kBwdBM * D / 8 / kKvThreads;   // 16-byte chunks per thread
   u32x4 q[kPer], d[kPer];
   float lse2, dval;
   __device__ __forceinline__ void load(const BwdArgs& a, int h, int q0, int lq, int qt) {
@@ -52,7 +59,7 @@ struct QTileLoader {
     const bf16* dp = static_cast<const bf16*>(a.dout) + (int64_t)q0 * stride + h * D;
 #pragma unroll
     for (int s = 0; s < kPer; ++s) {
-      const int u = threadIdx.x + 256 * s;
+      const int u = threadIdx.x + kKvThreads * s;
       const int row = qt * kBwdBM + u / (D / 8), c = u % (D / 8);
       if (row < lq) {
         q[s] = ld16(qp + (int64_t)row * stride + c * 8);
@@ -75,24 +82,30 @@ struct QTileLoader {
       }
     }
   }
-  __device__ __forceinline__ void store(char* smem) const {
-    using S = BwdSmem<D>;
+  __device__ __forceinline__ void store(char* buf) const {
+    using S = KvSmem<D>;
 #pragma unroll
     for (int s = 0; s < kPer; ++s) {
-      const int u = threadIdx.x + 256 * s;
-      lds_store_chunk<D>(smem + S::off_q, u / (D / 8), u % (D / 8), q[s]);
-      lds_store_chunk<D>(smem + S::off_do, u / (D / 8), u % (D / 8), d[s]);
+      const int u = threadIdx.x + kKvThreads * s;
+      lds_store_chunk<D>(buf + S::off_q, u / (D / 8), u % (D / 8), q[s]);
+      lds_store_chunk<D>(buf + S::off_do, u / (D / 8), u % (D / 8), d[s]);
     }
     if (threadIdx.x < kBwdBM) {
-      reinterpret_cast<float*>(smem + S::off_lse)[threadIdx.x] = lse2;
-      reinterpret_cast<float*>(smem + S::off_dv)[threadIdx.x] = dval;
+      reinterpret_cast<float*>(buf + S::off_lse)[threadIdx.x] = lse2;
+      reinterpret_cast<float*>(buf + S::off_dv)[threadIdx.x] = dval;
     }
   }
 };
 
+// dK/dV, key-tile outer. Waves 0-3 (role 0) own keys 32w..32w+31 of the
+// item and compute S = Q K^T, P and dV^T += dO^T P; waves 4-7 (role 1) own
+// the same key slices and compute dP = dO V^T, dS = scale P (dP - D) with
+// the P that role 0 leaves in LDS, and dK^T += Q^T dS. Each wave holds one
+// operand fragment and one accumulator set, so two waves share every SIMD,
+// and per SIMD the two roles issue the same number of MFMAs.
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdArgs a) {
-  using S = BwdSmem<D>;
+__global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  using S = KvSmem<D>;
   constexpr int NT = D / 16;
   constexpr int NB = D / 32;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -107,54 +120,30 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdArgs a) {
   const int G = a.group;
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int role = w >> 2, kw = w & 3;
   const int hl = lane >> 5, c = lane & 31;
-  const int j = kt * kBwdBN + 32 * w + c;        // this lane's key
+  const int j = kt * kBwdBN + 32 * kw + c;       // this lane's key
 
   const int64_t kstride = (int64_t)a.hk * D;
-  const bf16* kp = static_cast<const bf16*>(a.k) + (int64_t)k0 * kstride + hk * D;
-  const bf16* vp = static_cast<const bf16*>(a.v) + (int64_t)k0 * kstride + hk * D;
-
-  // K, V fragments as B operands (lane (hl, c) holds row j, columns 16t+8hl..)
-  bf16x8 kf[NT], vf[NT];
+  // role 0 holds K rows (B operand of S = Q K^T), role 1 V rows (of dP = dO V^T)
+  const bf16* fp = static_cast<const bf16*>(role == 0 ? a.k : a.v) + (int64_t)k0 * kstride + hk * D;
+  bf16x8 frag[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    if (j < lk) {
-      kf[t] = __builtin_bit_cast(bf16x8, ld16(kp + (int64_t)j * kstride + 16 * t + 8 * hl));
-      vf[t] = __builtin_bit_cast(bf16x8, ld16(vp + (int64_t)j * kstride + 16 * t + 8 * hl));
-    } else {
-      kf[t] = bf16x8{};
-      vf[t] = bf16x8{};
-    }
-  }
-  // K tile in LDS for the dQ product (rows = keys)
-  {
-    constexpr int kPer = kBwdBN * D / 8 / 256;
-#pragma unroll
-    for (int s = 0; s < kPer; ++s) {
-      const int u = threadIdx.x + 256 * s;
-      const int row = u / (D / 8), cc = u % (D / 8);
-      const int jj = kt * kBwdBN + row;
-      u32x4 v = jj < lk ? ld16(kp + (int64_t)jj * kstride + cc * 8) : u32x4{0u, 0u, 0u, 0u};
-      lds_store_chunk<D>(smem + S::off_k, row, cc, v);
-    }
-  }
+  for (int t = 0; t < NT; ++t)
+    frag[t] = j < lk ? __builtin_bit_cast(bf16x8, ld16(fp + (int64_t)j * kstride + 16 * t + 8 * hl))
+                     : bf16x8{};
 
   int ilo, ihi;
   key_row_range(j, lq, lk, a.causal, a.win_left, a.win_right, ilo, ihi);
 
-  f32x16 dka[NB], dva[NB];
+  f32x16 acc[NB];                                // role 0: dV^T, role 1: dK^T
 #pragma unroll
-  for (int n = 0; n < NB; ++n) { dka[n] = f32x16{}; dva[n] = f32x16{}; }
+  for (int n = 0; n < NB; ++n) acc[n] = f32x16{};
 
   const int nq = qt_hi - qt_lo;
   const int steps = nq * G;
   const float c2 = a.scale * kLog2e;
-  const float* lse_l = reinterpret_cast<const float*>(smem + S::off_lse);
-  const float* dv_l = reinterpret_cast<const float*>(smem + S::off_dv);
-  const char* q_l = smem + S::off_q;
-  const char* do_l = smem + S::off_do;
-  char* ds_l = smem + S::off_ds;
-  const int qbw = w >> 1, dh = w & 1;            // this wave's dQ block
+  char* p_l = smem + S::off_p;
 
   QTileLoader<D> ld;
   if (steps > 0) {
@@ -164,116 +153,206 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdArgs a) {
   __syncthreads();
 
   for (int st = 0; st < steps; ++st) {
-    const int g = st / nq, qt = qt_lo + st % nq;
-    const int h = hk * G + g;
+    const int qt = qt_lo + st % nq;
     const bool more = st + 1 < steps;
-    if (more) {
-      const int g1 = (st + 1) / nq, qt1 = qt_lo + (st + 1) % nq;
-      ld.load(a, hk * G + g1, q0, lq, qt1);
-    }
-
-    // S = Q K^T and dP = dO V^T for the two 32-row query blocks
-    f32x16 sc[2], dp[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      sc[qb] = f32x16{};
-      dp[qb] = f32x16{};
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        sc[qb] = mfma32(lds_row_chunk<D>(q_l, 32 * qb + c, 2 * t + hl), kf[t], sc[qb]);
-        dp[qb] = mfma32(lds_row_chunk<D>(do_l, 32 * qb + c, 2 * t + hl), vf[t], dp[qb]);
-      }
-    }
-    // P and dS; query row of slot r is 32qb + 8(r/4) + 4hl + r%4
+    if (more) ld.load(a, hk * G + (st + 1) / nq, q0, lq, qt_lo + (st + 1) % nq);
+    const char* buf = smem + (st & 1) * S::stage;
+    const char* q_l = buf + S::off_q;
+    const char* do_l = buf + S::off_do;
+    const float* lse_l = reinterpret_cast<const float*>(buf + S::off_lse);
+    const float* dv_l = reinterpret_cast<const float*>(buf + S::off_dv);
     const bool partial = qt < qf_lo || qt >= qf_hi;
+
+    // phase 1: role 0 S = Q K^T -> P (to LDS); role 1 dP = dO V^T.
+    // Query row of result slot r of block qb is 32qb + 8(r/4) + 4hl + r%4.
+    const char* a_l = role == 0 ? q_l : do_l;
+    f32x16 x[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
+      x[qb] = f32x16{};
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int qq = 32 * qb + 8 * g4 + 4 * hl;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_l + qq);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dv_l + qq);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g4 + e;
-          float p = exp2_hw(__builtin_fmaf(sc[qb][r], c2, -l4[e]));
-          if (partial) {
-            const int i = qt * kBwdBM + qq + e;
-            if (i < ilo || i > ihi) p = 0.f;
-          }
-          sc[qb][r] = p;
-          dp[qb][r] = a.scale * p * (dp[qb][r] - d4[e]);
-        }
-      }
+      for (int t = 0; t < NT; ++t)
+        x[qb] = mfma32(lds_row_chunk<D>(a_l, 32 * qb + c, 2 * t + hl), frag[t], x[qb]);
     }
-    // dV^T += dO^T P, dK^T += Q^T dS over the 4 16-row query chunks
+    if (role == 0) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int qq = 32 * qb + 8 * g4 + 4 * hl;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_l + qq);
+          f32x4 p4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float p = exp2_hw(__builtin_fmaf(x[qb][4 * g4 + e], c2, -l4[e]));
+            if (partial) {
+              const int i = qt * kBwdBM + qq + e;
+              if (i < ilo || i > ihi) p = 0.f;
+            }
+            x[qb][4 * g4 + e] = p;
+            p4[e] = p;
+          }
+          *reinterpret_cast<f32x4*>(p_l + tile_off<128>(32 * kw + c, 2 * qq)) = p4;
+        }
+    }
+    __syncthreads();
+
+    // phase 2: role 0 dV^T += dO^T P; role 1 dS = scale P (dP - D), dK^T += Q^T dS
+    if (role == 1) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int qq = 32 * qb + 8 * g4 + 4 * hl;
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dv_l + qq);
+          const f32x4 p4 = *reinterpret_cast<const f32x4*>(p_l + tile_off<128>(32 * kw + c, 2 * qq));
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            x[qb][4 * g4 + e] = a.scale * p4[e] * (x[qb][4 * g4 + e] - d4[e]);
+        }
+    }
+    const char* t_l = role == 0 ? do_l : q_l;
 #pragma unroll
     for (int tq = 0; tq < 4; ++tq) {
-      const bf16x8 pf = frag_half(sc[tq >> 1], tq & 1);
-      const bf16x8 sf = frag_half(dp[tq >> 1], tq & 1);
+      const bf16x8 f = frag_half(x[tq >> 1], tq & 1);
 #pragma unroll
-      for (int n = 0; n < NB; ++n) {
-        dva[n] = mfma32(lds_col_operand<D>(do_l, 16 * tq, 32 * n), pf, dva[n]);
-        dka[n] = mfma32(lds_col_operand<D>(q_l, 16 * tq, 32 * n), sf, dka[n]);
-      }
+      for (int n = 0; n < NB; ++n)
+        acc[n] = mfma32(lds_col_operand<D>(t_l, 16 * tq, 32 * n), f, acc[n]);
     }
-    // dS^T -> LDS: row = key 32w + c, columns = query rows
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int qq = 32 * qb + 8 * g4 + 4 * hl;
-        *reinterpret_cast<u32x2*>(ds_l + tile_off<kBwdBM>(32 * w + c, qq)) =
-            pack4_bits(dp[qb][4 * g4], dp[qb][4 * g4 + 1], dp[qb][4 * g4 + 2],
-                       dp[qb][4 * g4 + 3]);
-      }
-    __syncthreads();
-    if (more) ld.store(smem);       // Q/dO of this step are no longer read
-
-    // dQ[32 rows of block qbw][D/2 columns of half dh] = dS K over 128 keys
-#pragma unroll
-    for (int nb = 0; nb < D / 64; ++nb) {
-      const int col = dh * (D / 2) + 32 * nb;
-      f32x16 acc = f32x16{};
-#pragma unroll
-      for (int tk = 0; tk < kBwdBN / 16; ++tk) {
-        const bf16x8 af = lds_col_operand<kBwdBM>(ds_l, 16 * tk, 32 * qbw);
-        const bf16x8 bfr = lds_col_operand<D>(smem + S::off_k, 16 * tk, col);
-        acc = mfma32(af, bfr, acc);
-      }
-      float* dqp = a.dq_acc + ((int64_t)q0 * a.hq + h) * D + col + c;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = qt * kBwdBM + 32 * qbw + 8 * (r >> 2) + 4 * hl + (r & 3);
-        if (i < lq) unsafeAtomicAdd(dqp + (int64_t)i * a.hq * D, acc[r]);
-      }
-    }
+    if (more) ld.store(smem + ((st + 1) & 1) * S::stage);
     __syncthreads();
   }
 
-  // dK, dV rows of this wave's keys
+  // role 0 writes dV, role 1 dK, for this wave's keys
   if (j < lk) {
-    bf16* dkp = static_cast<bf16*>(a.dk) + (int64_t)(k0 + j) * kstride + hk * D;
-    bf16* dvp = static_cast<bf16*>(a.dv) + (int64_t)(k0 + j) * kstride + hk * D;
+    bf16* dst = static_cast<bf16*>(role == 0 ? a.dv : a.dk) + (int64_t)(k0 + j) * kstride + hk * D;
 #pragma unroll
     for (int n = 0; n < NB; ++n)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d = 32 * n + 8 * g4 + 4 * hl;
-        *reinterpret_cast<u32x2*>(dkp + d) =
-            pack4_bits(dka[n][4 * g4], dka[n][4 * g4 + 1], dka[n][4 * g4 + 2], dka[n][4 * g4 + 3]);
-        *reinterpret_cast<u32x2*>(dvp + d) =
-            pack4_bits(dva[n][4 * g4], dva[n][4 * g4 + 1], dva[n][4 * g4 + 2], dva[n][4 * g4 + 3]);
+        *reinterpret_cast<u32x2*>(dst + d) =
+            pack4_bits(acc[n][4 * g4], acc[n][4 * g4 + 1], acc[n][4 * g4 + 2], acc[n][4 * g4 + 3]);
       }
   }
 }
 
-// dq = bf16(dq_acc), 8 elements per thread.
-__global__ __launch_bounds__(256) void dq_convert_kernel(const float* acc, bf16* dq, int64_t n8) {
-  for (int64_t u = blockIdx.x * 256 + threadIdx.x; u < n8; u += (int64_t)gridDim.x * 256) {
-    const f32x4 x = *reinterpret_cast<const f32x4*>(acc + 8 * u);
-    const f32x4 y = *reinterpret_cast<const f32x4*>(acc + 8 * u + 4);
-    *reinterpret_cast<bf16x8*>(dq + 8 * u) = pack8(x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]);
+// dQ, query-tile outer. Work items and block numbering are the forward's.
+template <int D>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int BN = kFwdBN;
+  constexpr int NT = D / 16;
+  constexpr int NB = D / 32;
+  constexpr int TILE = BN * D * 2;
+  __shared__ __attribute__((aligned(16))) char lds[2][2 * TILE];
+
+  const int item = blockIdx.x / a.hq;
+  const int h = head_of_slot(blockIdx.x % a.hq, a.hq);
+  const int* it = a.items_q + item * kItemWords;
+  const int b = it[0], qt = it[1], kt_lo = it[2], kt_hi = it[3];
+  const int kf_lo = it[4], kf_hi = it[5];
+  const int q0 = a.cu_q[b], lq = a.cu_q[b + 1] - q0;
+  const int k0 = a.cu_k[b], lk = a.cu_k[b + 1] - k0;
+  const int hk = h / a.group;
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int hl = lane >> 5, c = lane & 31;
+  const int i = qt * kFwdBM + w * 32 + c;     // this lane's query row
+
+  const int64_t qstride = (int64_t)a.hq * D;
+  const int64_t kstride = (int64_t)a.hk * D;
+  const bf16* kp = static_cast<const bf16*>(a.k) + (int64_t)k0 * kstride + hk * D;
+  const bf16* vp = static_cast<const bf16*>(a.v) + (int64_t)k0 * kstride + hk * D;
+
+  // Q and dO rows as B operands of S^T = K Q^T and dP^T = V dO^T
+  bf16x8 qf[NT], gf[NT];
+  const int64_t roff = (int64_t)(q0 + i) * qstride + h * D;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (i < lq) {
+      qf[t] = __builtin_bit_cast(bf16x8, ld16(static_cast<const bf16*>(a.q) + roff + 16 * t + 8 * hl));
+      gf[t] = __builtin_bit_cast(bf16x8, ld16(static_cast<const bf16*>(a.dout) + roff + 16 * t + 8 * hl));
+    } else {
+      qf[t] = bf16x8{};
+      gf[t] = bf16x8{};
+    }
+  }
+  float lse2 = __builtin_huge_valf(), dval = 0.f;
+  if (i < lq) {
+    const float l = a.lse[(int64_t)h * a.total_q + q0 + i];
+    lse2 = l == kNegInf ? __builtin_huge_valf() : l * kLog2e;
+    dval = a.dval[(int64_t)h * a.total_q + q0 + i];
+  }
+  const float c2 = a.scale * kLog2e;
+  int jlo, jhi;
+  row_key_range(i, lq, lk, a.causal, a.win_left, a.win_right, jlo, jhi);
+
+  f32x16 o[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) o[n] = f32x16{};
+
+  TileLoader<D> kl, vl;
+  if (kt_lo < kt_hi) {
+    kl.load(kp, kstride, kt_lo * BN, lk);
+    vl.load(vp, kstride, kt_lo * BN, lk);
+    kl.store(lds[0]);
+    vl.store(lds[0] + TILE);
+  }
+  __syncthreads();
+
+  for (int kt = kt_lo; kt < kt_hi; ++kt) {
+    const int cur = (kt - kt_lo) & 1;
+    const bool more = kt + 1 < kt_hi;
+    if (more) {
+      kl.load(kp, kstride, (kt + 1) * BN, lk);
+      vl.load(vp, kstride, (kt + 1) * BN, lk);
+    }
+    const char* kt_lds = lds[cur];
+    const char* vt_lds = lds[cur] + TILE;
+    const bool partial = kt < kf_lo || kt >= kf_hi;
+    // one 32-key block at a time: S^T, dP^T, dS^T, then its two dQ chunks
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        s = mfma32(lds_row_chunk<D>(kt_lds, kb * 32 + c, 2 * t + hl), qf[t], s);
+        dp = mfma32(lds_row_chunk<D>(vt_lds, kb * 32 + c, 2 * t + hl), gf[t], dp);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = exp2_hw(__builtin_fmaf(s[r], c2, -lse2));
+        if (partial) {
+          const int jj = kt * BN + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (jj < jlo || jj > jhi) p = 0.f;
+        }
+        dp[r] = a.scale * p * (dp[r] - dval);
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const bf16x8 sf = frag_half(dp, hh);
+#pragma unroll
+        for (int n = 0; n < NB; ++n)
+          o[n] = mfma32(lds_col_operand<D>(kt_lds, 32 * kb + 16 * hh, 32 * n), sf, o[n]);
+      }
+    }
+    if (more) {
+      kl.store(lds[cur ^ 1]);
+      vl.store(lds[cur ^ 1] + TILE);
+    }
+    __syncthreads();
+  }
+
+  if (i < lq) {
+    bf16* dqp = static_cast<bf16*>(a.dq) + roff;
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * n + 8 * g + 4 * hl;
+        *reinterpret_cast<u32x2*>(dqp + d) =
+            pack4_bits(o[n][4 * g], o[n][4 * g + 1], o[n][4 * g + 2], o[n][4 * g + 3]);
+      }
   }
 }
 
@@ -281,20 +360,18 @@ template <int D>
 hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s, const TimingHook& th) {
   hipError_t e = launch_bwd_pre<D, bf16>(a, s);
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_main_kernel<D>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, BwdSmem<D>::bytes);
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, KvSmem<D>::bytes);
   if (e != hipSuccess) return e;
   if (th.start) hipEventRecord(th.start, s);
   if (a.n_items > 0)
-    hipLaunchKernelGGL(bwd_main_kernel<D>, dim3(a.n_items * a.hk), dim3(256),
-                       BwdSmem<D>::bytes, s, a);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(a.n_items * a.hk), dim3(kKvThreads),
+                       KvSmem<D>::bytes, s, a);
   if (th.stop) hipEventRecord(th.stop, s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t n8 = (int64_t)a.total_q * a.hq * D / 8;
-  const int blocks = (int)std::min<int64_t>((n8 + 255) / 256, 8192);
-  hipLaunchKernelGGL(dq_convert_kernel, dim3(blocks), dim3(256), 0, s, a.dq_acc,
-                     static_cast<bf16*>(a.dq), n8);
+  if (a.n_items_q > 0)
+    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(a.n_items_q * a.hq), dim3(256), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_dsink_finalize(a, s);

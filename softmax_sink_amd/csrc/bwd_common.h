@@ -16,8 +16,7 @@ namespace sinkattn {
 namespace {
 
 // Block (token block bt, q-head h): D = rowsum(dO * out) for kPreRows
-// tokens, their -p_sink * D summed in a fixed order into part[h][bt], and
-// (bf16 path) the fp32 dQ accumulator rows of those tokens cleared.
+// tokens and their -p_sink * D summed in a fixed order into part[h][bt].
 template <int D, typename T>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   using namespace dev;
@@ -38,11 +37,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
       const T* op = static_cast<const T*>(a.out) + off;
 #pragma unroll
       for (int e = 0; e < 8; ++e) dot += (float)dop[e] * (float)op[e];
-      if (a.dq_acc) {
-        f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        *reinterpret_cast<f32x4*>(a.dq_acc + off) = z;
-        *reinterpret_cast<f32x4*>(a.dq_acc + off + 4) = z;
-      }
     }
 #pragma unroll
     for (int o = TPR / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o);

@@ -114,10 +114,9 @@ BwdWorkspace bwd_workspace_layout(int64_t total_q, int hq, int head_dim,
   BwdWorkspace w;
   w.dval_off = 0;
   w.part_off = align_up(total_q * hq * 4, 256);
-  w.dqacc_off = w.part_off + align_up(pre_blocks * hq * 4, 256);
-  w.bytes = w.dqacc_off;
-  if (dtype == SINK_ATTN_BF16)
-    w.bytes += align_up(total_q * hq * static_cast<int64_t>(head_dim) * 4, 256);
+  w.bytes = w.part_off + align_up(pre_blocks * hq * 4, 256);
+  (void)head_dim;
+  (void)dtype;
   return w;
 }
 

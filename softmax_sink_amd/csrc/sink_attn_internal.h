@@ -5,7 +5,7 @@
 #include <cstdint>
 #include <hip/hip_runtime_api.h>
 
-#include "../../include/sink_attn.h"
+#include "sink_attn.h"
 
 namespace sinkattn {
 
@@ -50,7 +50,7 @@ struct FwdWorkspace {
   int64_t o_off, m_off, l_off, bytes;
 };
 struct BwdWorkspace {
-  int64_t dval_off, part_off, dqacc_off, bytes;
+  int64_t dval_off, part_off, bytes;
 };
 FwdWorkspace fwd_workspace_layout(int64_t dec_rows, int head_dim, int dtype,
                                   int mode);
@@ -105,11 +105,11 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* dsink;
-  const int32_t* items;     // device: backward items
+  const int32_t* items;     // device: backward (key tile) items
+  const int32_t* items_q;   // device: forward (query tile) items, for dQ
   float* dval;              // [hq, total_q]
   float* part;              // [hq, pre_blocks]
-  float* dq_acc;            // [total_q, hq, head_dim] (bf16 path)
-  int n_items, pre_blocks;
+  int n_items, n_items_q, pre_blocks;
   int batch, hq, hk, group, causal, win_left, win_right;
   int total_q, total_k;
   float scale;
