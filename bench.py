@@ -60,34 +60,64 @@ def to_dev(p, name):
     return torch.from_numpy(x).cuda()
 
 
-def cpu_baseline(p, train, seconds_hint):
+def cpu_baseline(p, train, seconds):
     """The fp64 oracle on the host over a bounded sample of the workload:
-    one (sequence, q-head) slice, forward (+ backward for training)."""
+    whole (sequence, q-head) slices, forward (+ backward for training),
+    taken in a fixed order (median-length sequence first, heads in order)
+    until about `seconds` of work has been done."""
     import oracle as O
     from threadpoolctl import threadpool_info
     lens = np.diff(p.cu_q)
-    b = int(np.argsort(lens)[len(lens) // 2])        # a median-length sequence
-    sub = p.sub_batch([b])
-    h = 0
-    hk = h // (p.num_heads_q // p.num_heads_k)
-    args = (sub.as_f32("q")[:, h:h + 1], sub.as_f32("k")[:, hk:hk + 1],
-            sub.as_f32("v")[:, hk:hk + 1], sub.cu_q, sub.cu_k,
-            sub.sinks[h:h + 1].astype(np.float64), float(p.scale), p.causal,
-            p.win_left, p.win_right)
-    pairs = kept_pairs(sub.cu_q, sub.cu_k, p.causal, p.win_left, p.win_right)
+    order = list(np.argsort(lens, kind="stable"))
+    order = order[len(order) // 2:] + order[:len(order) // 2][::-1]
+    G = p.num_heads_q // p.num_heads_k
+    pairs = 0
+    done = []
     t0 = time.perf_counter()
-    if train:
-        O.sink_attention_backward(sub.as_f32("dout")[:, h:h + 1], *args)
-    else:
-        O.sink_attention_forward(*args)
+    for b in order:
+        sub = p.sub_batch([int(b)])
+        sp = kept_pairs(sub.cu_q, sub.cu_k, p.causal, p.win_left, p.win_right)
+        for h in range(p.num_heads_q):
+            hk = h // G
+            args = (sub.as_f32("q")[:, h:h + 1], sub.as_f32("k")[:, hk:hk + 1],
+                    sub.as_f32("v")[:, hk:hk + 1], sub.cu_q, sub.cu_k,
+                    sub.sinks[h:h + 1].astype(np.float64), float(p.scale), p.causal,
+                    p.win_left, p.win_right)
+            if train:
+                O.sink_attention_backward(sub.as_f32("dout")[:, h:h + 1], *args)
+            else:
+                O.sink_attention_forward(*args)
+            pairs += sp
+            done.append((int(b), h))
+            if time.perf_counter() - t0 >= seconds:
+                break
+        if time.perf_counter() - t0 >= seconds:
+            break
     dt = time.perf_counter() - t0
     flops = pairs * p.head_dim * (14 if train else 4)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    seqs = sorted({b for b, _ in done})
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"sequence {b} (Lq={int(lens[b])}), q-head {h}: "
+            "sample": f"{len(done)} (sequence, q-head) slices from sequences {seqs}: "
                       f"{'forward+backward' if train else 'forward'}, {pairs} kept pairs, "
-                      f"{dt:.1f} s on {os.cpu_count()} host cpus"}
+                      f"{dt:.1f} s (FLOPs counted as in value)"}
+
+
+def traffic_record(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    if it was taken on the current kernel source; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(workload)
+    if not rec or rec.get("kernel") != kernel:
+        return None
+    src = os.path.join(ROOT, "softmax_sink_amd", "csrc", rec["source"])
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["hbm_bytes_per_launch"]
 
 
 def main():
@@ -97,6 +127,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="train_varlen")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="first run a plain device-to-device copy of BYTES bytes "
+                         "three times (reference for HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -108,6 +142,13 @@ def main():
     from softmax_sink_amd import workloads as W
 
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        src = torch.empty(args.calibrate_copy, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     p = W.config(args.workload)
     train = args.workload in TRAIN
     decode = args.workload == "decode_softmax_n"
@@ -195,15 +236,20 @@ def main():
         achieved = alg_bytes / (kavg["fwd"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": "fwd_split_kernel", "achieved": achieved,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                "traffic": None, "launch_ms": kavg["fwd"]}
+                "traffic": traffic_record(args.workload, "fwd_split_kernel"),
+                "launch_ms": kavg["fwd"], "bytes_per_launch": alg_bytes}
     else:
+        # dominant kernel: the dK/dV loop (S, dP, dV, dK: 8*D per kept pair)
+        # for training, the prefill tile loop (QK^T, PV: 4*D) otherwise
         name = "bwd" if train else "fwd"
-        flops = bwd_flops if train else fwd_flops
+        flops = (8.0 * D * pairs) if train else fwd_flops
+        kname = "bwd_dkdv_kernel" if train else "fwd_prefill_kernel"
         peak = PEAK_BF16_TFLOPS if p.dtype == "bf16" else PEAK_FP32_TFLOPS
         achieved = flops / (kavg[name] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": "bwd_main_kernel" if train else "fwd_prefill_kernel",
-                "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": achieved / peak, "traffic": None, "launch_ms": kavg[name]}
+        roof = {"bound": "mfma", "kernel": kname, "achieved": achieved, "peak": peak,
+                "unit": "TFLOP/s", "frac": achieved / peak,
+                "traffic": traffic_record(args.workload, kname),
+                "launch_ms": kavg[name], "flop_per_launch": flops}
     res = {
         "metric": METRIC if train else f"sink-attention forward {'GB/s' if decode else 'TFLOP/s'}",
         "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -222,7 +268,7 @@ def main():
         res["value_gbs"] = alg_bytes / (ms * 1e-3) / 1e9
     if not args.no_cpu_baseline:
         print("# timing the oracle on the host", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(p, train, 20)
+        res["cpu_baseline"] = cpu_baseline(p, train, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 

@@ -52,7 +52,7 @@ template <int D>
 struct QTileLoader {
   static constexpr int kPer = kBwdBM * D / 8 / kKvThreads;   // 16-byte chunks per thread
   u32x4 q[kPer], d[kPer];
-  float lse2, dval;
+  float lse, dval;
   __device__ __forceinline__ void load(const BwdArgs& a, int h, int q0, int lq, int qt) {
     const int64_t stride = (int64_t)a.hq * D;
     const bf16* qp = static_cast<const bf16*>(a.q) + (int64_t)q0 * stride + h * D;
@@ -71,13 +71,12 @@ struct QTileLoader {
     }
     if (threadIdx.x < kBwdBM) {
       const int row = qt * kBwdBM + threadIdx.x;
+      // raw values only: converting here would wait for the loads at once
       if (row < lq) {
-        const float l = a.lse[(int64_t)h * a.total_q + q0 + row];
-        // a row with lse = -inf keeps no key: make every P of it 0
-        lse2 = l == kNegInf ? __builtin_huge_valf() : l * kLog2e;
+        lse = a.lse[(int64_t)h * a.total_q + q0 + row];
         dval = a.dval[(int64_t)h * a.total_q + q0 + row];
       } else {
-        lse2 = __builtin_huge_valf();
+        lse = kNegInf;      // rows past the sequence keep no key
         dval = 0.f;
       }
     }
@@ -91,7 +90,9 @@ struct QTileLoader {
       lds_store_chunk<D>(buf + S::off_do, u / (D / 8), u % (D / 8), d[s]);
     }
     if (threadIdx.x < kBwdBM) {
-      reinterpret_cast<float*>(buf + S::off_lse)[threadIdx.x] = lse2;
+      // log2-domain lse; a row with lse = -inf keeps no key: make its P 0
+      reinterpret_cast<float*>(buf + S::off_lse)[threadIdx.x] =
+          lse == kNegInf ? __builtin_huge_valf() : lse * kLog2e;
       reinterpret_cast<float*>(buf + S::off_dv)[threadIdx.x] = dval;
     }
   }
@@ -150,6 +151,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     ld.load(a, hk * G, q0, lq, qt_lo);
     ld.store(smem);
   }
+  wait_vmem();
   __syncthreads();
 
   for (int st = 0; st < steps; ++st) {
@@ -298,6 +300,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     kl.store(lds[0]);
     vl.store(lds[0] + TILE);
   }
+  wait_vmem();
   __syncthreads();
 
   for (int kt = kt_lo; kt < kt_hi; ++kt) {

@@ -140,6 +140,13 @@ __device__ __forceinline__ u32x2 pack4_bits(float a, float b, float c, float d) 
   return __builtin_bit_cast(u32x2, v);
 }
 
+// Wait for every outstanding vector-memory load (s_waitcnt vmcnt(0), other
+// counters untouched). Placed before a tile loop whose entry can be reached
+// with loads still in flight on some path, so that the compiler does not
+// carry a conservative vmcnt(0) into every iteration, where it would also
+// wait for the prefetch of the next tile.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Global 16-byte load / store helpers.
 __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);

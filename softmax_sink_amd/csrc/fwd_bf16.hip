@@ -84,6 +84,7 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdArgs a) {
     kl.store(lds[0]);
     vl.store(lds[0] + TILE);
   }
+  wait_vmem();
   __syncthreads();
 
   for (int kt = kt_lo; kt < kt_hi; ++kt) {
@@ -240,6 +241,7 @@ __global__ __launch_bounds__(256, 2) void fwd_split_kernel(FwdArgs a) {
     kl.store(lds[0]);
     vl.store(lds[0] + TILE);
   }
+  wait_vmem();
   __syncthreads();
 
   for (int n_t = 0; n_t < nt; ++n_t) {
