@@ -25,6 +25,8 @@
 //    atomic dQ update inside the first kernel, and replaces 2.4e9 fp32
 //    atomics (plus a zeroed fp32 accumulator) on the long causal workloads;
 //    it also makes dQ deterministic.
+#include <type_traits>
+
 #include "bwd_common.h"
 #include "tile_common.h"
 
@@ -47,53 +49,44 @@ struct KvSmem {
 
 constexpr int kKvThreads = 512;                   // 8 waves: 4 key slices x 2 roles
 
-// Registers holding the next (q-head, query tile) step's Q, dO, lse, D.
+// The next (q-head, query tile) step's Q and dO go straight to LDS; its lse
+// and D rows (64 floats each) go through registers.
 template <int D>
 struct QTileLoader {
-  static constexpr int kPer = kBwdBM * D / 8 / kKvThreads;   // 16-byte chunks per thread
-  u32x4 q[kPer], d[kPer];
+  TileDma<D, kKvThreads> q, d;
   float lse, dval;
-  __device__ __forceinline__ void load(const BwdArgs& a, int h, int q0, int lq, int qt) {
-    const int64_t stride = (int64_t)a.hq * D;
+  bool live;
+  int64_t stride;
+  __device__ __forceinline__ void init(const BwdArgs& a) {
+    stride = (int64_t)a.hq * D;
+    q.init();
+    d.init();
+  }
+  __device__ __forceinline__ void load(const BwdArgs& a, int h, int q0, int lq, int qt,
+                                       char* buf) {
+    using S = KvSmem<D>;
     const bf16* qp = static_cast<const bf16*>(a.q) + (int64_t)q0 * stride + h * D;
     const bf16* dp = static_cast<const bf16*>(a.dout) + (int64_t)q0 * stride + h * D;
-#pragma unroll
-    for (int s = 0; s < kPer; ++s) {
-      const int u = threadIdx.x + kKvThreads * s;
-      const int row = qt * kBwdBM + u / (D / 8), c = u % (D / 8);
-      if (row < lq) {
-        q[s] = ld16(qp + (int64_t)row * stride + c * 8);
-        d[s] = ld16(dp + (int64_t)row * stride + c * 8);
-      } else {
-        q[s] = u32x4{0u, 0u, 0u, 0u};
-        d[s] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
+    q.load(qp, stride, qt * kBwdBM, lq, buf + S::off_q);
+    d.load(dp, stride, qt * kBwdBM, lq, buf + S::off_do);
     if (threadIdx.x < kBwdBM) {
+      // raw values only (converting here would wait for the load at once);
+      // rows past the sequence read its last row and are flagged
       const int row = qt * kBwdBM + threadIdx.x;
-      // raw values only: converting here would wait for the loads at once
-      if (row < lq) {
-        lse = a.lse[(int64_t)h * a.total_q + q0 + row];
-        dval = a.dval[(int64_t)h * a.total_q + q0 + row];
-      } else {
-        lse = kNegInf;      // rows past the sequence keep no key
-        dval = 0.f;
-      }
+      live = row < lq;
+      const int64_t at = (int64_t)h * a.total_q + q0 + min(row, lq - 1);
+      lse = a.lse[at];
+      dval = a.dval[at];
     }
   }
   __device__ __forceinline__ void store(char* buf) const {
     using S = KvSmem<D>;
-#pragma unroll
-    for (int s = 0; s < kPer; ++s) {
-      const int u = threadIdx.x + kKvThreads * s;
-      lds_store_chunk<D>(buf + S::off_q, u / (D / 8), u % (D / 8), q[s]);
-      lds_store_chunk<D>(buf + S::off_do, u / (D / 8), u % (D / 8), d[s]);
-    }
     if (threadIdx.x < kBwdBM) {
-      // log2-domain lse; a row with lse = -inf keeps no key: make its P 0
+      // log2-domain lse; rows past the sequence, and rows with lse = -inf
+      // (no kept key), get +inf so that every P of them is 0
       reinterpret_cast<float*>(buf + S::off_lse)[threadIdx.x] =
-          lse == kNegInf ? __builtin_huge_valf() : lse * kLog2e;
-      reinterpret_cast<float*>(buf + S::off_dv)[threadIdx.x] = dval;
+          (!live || lse == kNegInf) ? __builtin_huge_valf() : lse * kLog2e;
+      reinterpret_cast<float*>(buf + S::off_dv)[threadIdx.x] = live ? dval : 0.f;
     }
   }
 };
@@ -147,18 +140,23 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   char* p_l = smem + S::off_p;
 
   QTileLoader<D> ld;
+  ld.init(a);
   if (steps > 0) {
-    ld.load(a, hk * G, q0, lq, qt_lo);
+    ld.load(a, hk * G, q0, lq, qt_lo, smem);
     ld.store(smem);
   }
   wait_vmem();
   __syncthreads();
 
+  // (one copy of the loop body with a run-time buffer offset measures faster
+  // here than two copies with constant offsets)
   for (int st = 0; st < steps; ++st) {
+    const int stage = st & 1;
     const int qt = qt_lo + st % nq;
     const bool more = st + 1 < steps;
-    if (more) ld.load(a, hk * G + (st + 1) / nq, q0, lq, qt_lo + (st + 1) % nq);
-    const char* buf = smem + (st & 1) * S::stage;
+    if (more) ld.load(a, hk * G + (st + 1) / nq, q0, lq, qt_lo + (st + 1) % nq,
+                      smem + (stage ^ 1) * S::stage);
+    const char* buf = smem + stage * S::stage;
     const char* q_l = buf + S::off_q;
     const char* do_l = buf + S::off_do;
     const float* lse_l = reinterpret_cast<const float*>(buf + S::off_lse);
@@ -210,7 +208,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
           const f32x4 p4 = *reinterpret_cast<const f32x4*>(p_l + tile_off<128>(32 * kw + c, 2 * qq));
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            x[qb][4 * g4 + e] = a.scale * p4[e] * (x[qb][4 * g4 + e] - d4[e]);
+            x[qb][4 * g4 + e] = p4[e] * (x[qb][4 * g4 + e] - d4[e]);   // dK scaled at the end
         }
     }
     const char* t_l = role == 0 ? do_l : q_l;
@@ -221,20 +219,23 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       for (int n = 0; n < NB; ++n)
         acc[n] = mfma32(lds_col_operand<D>(t_l, 16 * tq, 32 * n), f, acc[n]);
     }
-    if (more) ld.store(smem + ((st + 1) & 1) * S::stage);
+    if (more) ld.store(smem + (stage ^ 1) * S::stage);
+    wait_vmem();        // the next Q/dO tile has landed in LDS
     __syncthreads();
   }
 
-  // role 0 writes dV, role 1 dK, for this wave's keys
+  // role 0 writes dV, role 1 dK (times the softmax scale), for this wave's keys
   if (j < lk) {
     bf16* dst = static_cast<bf16*>(role == 0 ? a.dv : a.dk) + (int64_t)(k0 + j) * kstride + hk * D;
+    const float sc = role == 0 ? 1.f : a.scale;
 #pragma unroll
     for (int n = 0; n < NB; ++n)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d = 32 * n + 8 * g4 + 4 * hl;
         *reinterpret_cast<u32x2*>(dst + d) =
-            pack4_bits(acc[n][4 * g4], acc[n][4 * g4 + 1], acc[n][4 * g4 + 2], acc[n][4 * g4 + 3]);
+            pack4_bits(acc[n][4 * g4] * sc, acc[n][4 * g4 + 1] * sc, acc[n][4 * g4 + 2] * sc,
+                       acc[n][4 * g4 + 3] * sc);
       }
   }
 }
@@ -246,7 +247,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   constexpr int NT = D / 16;
   constexpr int NB = D / 32;
   constexpr int TILE = BN * D * 2;
-  __shared__ __attribute__((aligned(16))) char lds[2][2 * TILE];
+  // two buffers as two objects, so that the compiler can tell a prefetch
+  // into one from reads of the other and does not wait for the prefetch
+  __shared__ __attribute__((aligned(16))) char lds0[2 * TILE];
+  __shared__ __attribute__((aligned(16))) char lds1[2 * TILE];
 
   const int item = blockIdx.x / a.hq;
   const int h = head_of_slot(blockIdx.x % a.hq, a.hq);
@@ -293,25 +297,25 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int n = 0; n < NB; ++n) o[n] = f32x16{};
 
-  TileLoader<D> kl, vl;
+  TileDma<D> kl, vl;
+  kl.init();
+  vl.init();
   if (kt_lo < kt_hi) {
-    kl.load(kp, kstride, kt_lo * BN, lk);
-    vl.load(vp, kstride, kt_lo * BN, lk);
-    kl.store(lds[0]);
-    vl.store(lds[0] + TILE);
+    kl.load(kp, kstride, kt_lo * BN, lk, lds0);
+    vl.load(vp, kstride, kt_lo * BN, lk, lds0 + TILE);
   }
   wait_vmem();
   __syncthreads();
 
-  for (int kt = kt_lo; kt < kt_hi; ++kt) {
-    const int cur = (kt - kt_lo) & 1;
+  auto tile_step = [&](auto cur_c, int kt) __attribute__((always_inline)) {
+    constexpr int cur = decltype(cur_c)::value;
     const bool more = kt + 1 < kt_hi;
     if (more) {
-      kl.load(kp, kstride, (kt + 1) * BN, lk);
-      vl.load(vp, kstride, (kt + 1) * BN, lk);
+      kl.load(kp, kstride, (kt + 1) * BN, lk, cur == 0 ? lds1 : lds0);
+      vl.load(vp, kstride, (kt + 1) * BN, lk, (cur == 0 ? lds1 : lds0) + TILE);
     }
-    const char* kt_lds = lds[cur];
-    const char* vt_lds = lds[cur] + TILE;
+    const char* kt_lds = cur == 0 ? lds0 : lds1;
+    const char* vt_lds = (cur == 0 ? lds0 : lds1) + TILE;
     const bool partial = kt < kf_lo || kt >= kf_hi;
     // one 32-key block at a time: S^T, dP^T, dS^T, then its two dQ chunks
 #pragma unroll
@@ -329,7 +333,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
           const int jj = kt * BN + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
           if (jj < jlo || jj > jhi) p = 0.f;
         }
-        dp[r] = a.scale * p * (dp[r] - dval);
+        dp[r] = p * (dp[r] - dval);          // scale is applied to dQ at the end
       }
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
@@ -339,22 +343,27 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
           o[n] = mfma32(lds_col_operand<D>(kt_lds, 32 * kb + 16 * hh, 32 * n), sf, o[n]);
       }
     }
-    if (more) {
-      kl.store(lds[cur ^ 1]);
-      vl.store(lds[cur ^ 1] + TILE);
-    }
+    wait_vmem();        // the next tile has landed in LDS
     __syncthreads();
+  };
+  int kt = kt_lo;
+  for (; kt + 1 < kt_hi; kt += 2) {
+    tile_step(std::integral_constant<int, 0>{}, kt);
+    tile_step(std::integral_constant<int, 1>{}, kt + 1);
   }
+  if (kt < kt_hi) tile_step(std::integral_constant<int, 0>{}, kt);
 
   if (i < lq) {
     bf16* dqp = static_cast<bf16*>(a.dq) + roff;
+    const float sc = a.scale;
 #pragma unroll
     for (int n = 0; n < NB; ++n)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = 32 * n + 8 * g + 4 * hl;
         *reinterpret_cast<u32x2*>(dqp + d) =
-            pack4_bits(o[n][4 * g], o[n][4 * g + 1], o[n][4 * g + 2], o[n][4 * g + 3]);
+            pack4_bits(o[n][4 * g] * sc, o[n][4 * g + 1] * sc, o[n][4 * g + 2] * sc,
+                       o[n][4 * g + 3] * sc);
       }
   }
 }

@@ -24,6 +24,8 @@
 // 64, share every K/V tile, which is read from HBM exactly once. Each item
 // writes unnormalised partial (O, m, l) without the sink; the combine kernel
 // merges the chunks by their maxima and adds e^(sink) once.
+#include <type_traits>
+
 #include "tile_common.h"
 
 namespace sinkattn {
@@ -31,13 +33,17 @@ namespace {
 
 using namespace dev;
 
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdArgs a) {
   constexpr int BN = kFwdBN;
   constexpr int NT = D / 16;            // K chunks of the QK^T product
   constexpr int NB = D / 32;            // 32-column blocks of O^T
   constexpr int TILE = BN * D * 2;      // bytes per K or V tile
-  __shared__ __attribute__((aligned(16))) char lds[2][2 * TILE];
+  // two buffers as two objects, so that the compiler can tell a prefetch
+  // into one from reads of the other and does not wait for the prefetch
+  __shared__ __attribute__((aligned(16))) char lds0[2 * TILE];
+  __shared__ __attribute__((aligned(16))) char lds1[2 * TILE];
 
   const int item = blockIdx.x / a.hq;
   const int h = head_of_slot(blockIdx.x % a.hq, a.hq);
@@ -77,35 +83,35 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdArgs a) {
   int jlo, jhi;
   row_key_range(i, lq, lk, a.causal, a.win_left, a.win_right, jlo, jhi);
 
-  TileLoader<D> kl, vl;
+  TileDma<D> kl, vl;
+  kl.init();
+  vl.init();
   if (kt_lo < kt_hi) {
-    kl.load(kp, kstride, kt_lo * BN, lk);
-    vl.load(vp, kstride, kt_lo * BN, lk);
-    kl.store(lds[0]);
-    vl.store(lds[0] + TILE);
+    kl.load(kp, kstride, kt_lo * BN, lk, lds0);
+    vl.load(vp, kstride, kt_lo * BN, lk, lds0 + TILE);
   }
   wait_vmem();
   __syncthreads();
 
-  for (int kt = kt_lo; kt < kt_hi; ++kt) {
-    const int cur = (kt - kt_lo) & 1;
+  // One 64-key tile; CUR (the LDS buffer) is a compile-time constant so that
+  // every LDS address is a per-lane base plus an immediate.
+  auto tile_step = [&](auto cur_c, int kt) __attribute__((always_inline)) {
+    constexpr int CUR = decltype(cur_c)::value;
     const bool more = kt + 1 < kt_hi;
     if (more) {
-      kl.load(kp, kstride, (kt + 1) * BN, lk);
-      vl.load(vp, kstride, (kt + 1) * BN, lk);
+      kl.load(kp, kstride, (kt + 1) * BN, lk, CUR == 0 ? lds1 : lds0);
+      vl.load(vp, kstride, (kt + 1) * BN, lk, (CUR == 0 ? lds1 : lds0) + TILE);
     }
-    const char* kt_lds = lds[cur];
-    const char* vt_lds = lds[cur] + TILE;
+    const char* kt_lds = CUR == 0 ? lds0 : lds1;
+    const char* vt_lds = (CUR == 0 ? lds0 : lds1) + TILE;
 
     // S^T for the two 32-key blocks of the tile
     f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        bf16x8 kf = lds_row_chunk<D>(kt_lds, kb * 32 + c, 2 * t + hl);
-        s[kb] = mfma32(kf, qf[t], s[kb]);
-      }
+      for (int kb = 0; kb < 2; ++kb)
+        s[kb] = mfma32(lds_row_chunk<D>(kt_lds, kb * 32 + c, 2 * t + hl), qf[t], s[kb]);
     }
 
     // mask (partial tiles only): key of slot r is kt*BN + 32kb + 8(r/4) + 4hl + r%4
@@ -125,42 +131,54 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = half_max(mx);
+    // The running max follows the exact row max, so the largest P of a row
+    // is exactly 1 in bf16 (few-key rows keep their accuracy); O and l are
+    // rescaled only when some lane's max moved.
     const float m_new = fmaxf(m, mx * c2);
+    const bool move = m_new > m;
     const float m_use = m_new == kNegInf ? 0.f : m_new;
     const float alpha = exp2_hw(m - m_use);
     m = m_new;
+    // P (fp32 row sum, so that lse keeps fp32 accuracy; bf16 as the B
+    // operand of the PV product)
+    bf16x8 pf[4];
     float psum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int t = 0; t < 4; ++t) {
+      f32x16& st = s[t >> 1];
+      const int o8 = 8 * (t & 1);
+      float e[8];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2_hw(__builtin_fmaf(s[kb][r], c2, -m_use));
-        s[kb][r] = p;
-        psum += p;
+      for (int u = 0; u < 8; ++u) {
+        e[u] = exp2_hw(__builtin_fmaf(st[o8 + u], c2, -m_use));
+        psum += e[u];
       }
-    l = l * alpha + psum;
-    if (!__all(alpha == 1.f)) {
+      pf[t] = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+    }
+    if (__any(move)) {
+      l *= alpha;
 #pragma unroll
       for (int n = 0; n < NB; ++n) o[n] *= alpha;
     }
+    l += psum;
 
     // O^T += V^T P^T over the 4 16-key chunks of the tile
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const bf16x8 pf = frag_half(s[t >> 1], t & 1);
 #pragma unroll
-      for (int n = 0; n < NB; ++n) {
-        const bf16x8 vf = lds_col_operand<D>(vt_lds, 16 * t, 32 * n);
-        o[n] = mfma32(vf, pf, o[n]);
-      }
+      for (int n = 0; n < NB; ++n)
+        o[n] = mfma32(lds_col_operand<D>(vt_lds, 16 * t, 32 * n), pf[t], o[n]);
     }
 
-    if (more) {
-      kl.store(lds[cur ^ 1]);
-      vl.store(lds[cur ^ 1] + TILE);
-    }
+    wait_vmem();        // the next tile has landed in LDS
     __syncthreads();
+  };
+  int kt = kt_lo;
+  for (; kt + 1 < kt_hi; kt += 2) {
+    tile_step(std::integral_constant<int, 0>{}, kt);
+    tile_step(std::integral_constant<int, 1>{}, kt + 1);
   }
+  if (kt < kt_hi) tile_step(std::integral_constant<int, 0>{}, kt);
 
   // epilogue: out = O / l, lse = m + log2(l) (natural log), sink included
   const float lt = l + half_partner(l);
@@ -193,7 +211,9 @@ __global__ __launch_bounds__(256, 2) void fwd_split_kernel(FwdArgs a) {
   constexpr int NT = D / 16;
   constexpr int NB = D / 32;
   constexpr int TILE = BN * D * 2;
-  __shared__ __attribute__((aligned(16))) char lds[2][2 * TILE];
+  // two buffers as two objects (see fwd_prefill_kernel)
+  __shared__ __attribute__((aligned(16))) char lds0[2 * TILE];
+  __shared__ __attribute__((aligned(16))) char lds1[2 * TILE];
 
   const int item = blockIdx.x / a.hk;
   const int hk = blockIdx.x % a.hk;
@@ -234,26 +254,26 @@ __global__ __launch_bounds__(256, 2) void fwd_split_kernel(FwdArgs a) {
   for (int n = 0; n < NB; ++n) o[n] = f32x16{};
 
   const int nt = (k_hi - k_lo + BN - 1) / BN;
-  TileLoader<D> kl, vl;
+  TileDma<D> kl, vl;
+  kl.init();
+  vl.init();
   if (nt > 0) {
-    kl.load(kp, kstride, k_lo, k_hi);
-    vl.load(vp, kstride, k_lo, k_hi);
-    kl.store(lds[0]);
-    vl.store(lds[0] + TILE);
+    kl.load(kp, kstride, k_lo, k_hi, lds0);
+    vl.load(vp, kstride, k_lo, k_hi, lds0 + TILE);
   }
   wait_vmem();
   __syncthreads();
 
-  for (int n_t = 0; n_t < nt; ++n_t) {
-    const int cur = n_t & 1;
+  auto tile_step = [&](auto cur_c, int n_t) __attribute__((always_inline)) {
+    constexpr int cur = decltype(cur_c)::value;
     const bool more = n_t + 1 < nt;
     const int base = k_lo + n_t * BN;
     if (more) {
-      kl.load(kp, kstride, base + BN, k_hi);
-      vl.load(vp, kstride, base + BN, k_hi);
+      kl.load(kp, kstride, base + BN, k_hi, cur == 0 ? lds1 : lds0);
+      vl.load(vp, kstride, base + BN, k_hi, (cur == 0 ? lds1 : lds0) + TILE);
     }
-    const char* kt_lds = lds[cur];
-    const char* vt_lds = lds[cur] + TILE;
+    const char* kt_lds = cur == 0 ? lds0 : lds1;
+    const char* vt_lds = (cur == 0 ? lds0 : lds1) + TILE;
     f32x16 s = f32x16{};
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -263,7 +283,7 @@ __global__ __launch_bounds__(256, 2) void fwd_split_kernel(FwdArgs a) {
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       const int j = base + kh * 32 + 8 * (rr >> 2) + 4 * hl + (rr & 3);
-      if (j < jlo || j > jhi) s[rr] = kNegInf;
+      if (j < jlo || j > jhi || j >= k_hi) s[rr] = kNegInf;
     }
     float mx = kNegInf;
 #pragma unroll
@@ -294,16 +314,19 @@ __global__ __launch_bounds__(256, 2) void fwd_split_kernel(FwdArgs a) {
         o[n] = mfma32(vf, pf, o[n]);
       }
     }
-    if (more) {
-      kl.store(lds[cur ^ 1]);
-      vl.store(lds[cur ^ 1] + TILE);
-    }
+    wait_vmem();        // the next tile has landed in LDS
     __syncthreads();
+  };
+  int n_t = 0;
+  for (; n_t + 1 < nt; n_t += 2) {
+    tile_step(std::integral_constant<int, 0>{}, n_t);
+    tile_step(std::integral_constant<int, 1>{}, n_t + 1);
   }
+  if (n_t < nt) tile_step(std::integral_constant<int, 0>{}, n_t);
 
   // merge the two key halves: waves 2,3 hand (m, l, O) to waves 0,1
   l = l + half_partner(l);
-  float* xo = reinterpret_cast<float*>(lds[0]);        // [2 waves][NB*16][64 lanes]
+  float* xo = reinterpret_cast<float*>(lds0);        // [2 waves][NB*16][64 lanes]
   float* xm = xo + 2 * NB * 16 * 64;                   // [2 waves][64 lanes]
   float* xl = xm + 2 * 64;
   if (kh == 1) {

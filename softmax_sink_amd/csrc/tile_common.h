@@ -8,30 +8,44 @@
 namespace sinkattn {
 namespace dev {
 
-// Stage a [64 x D] bf16 tile of rows [row0, row0 + 64) of a THD tensor
-// (row stride `stride` elements) into registers; rows >= nrows read as 0.
-template <int D>
-struct TileLoader {
-  static constexpr int kChunks = 64 * D / 8;           // 16-byte chunks per tile
-  static constexpr int kPerThread = kChunks / 256;     // 4 (D=128) or 2 (D=64)
-  u32x4 r[kPerThread];
-  __device__ __forceinline__ void load(const bf16* base, int64_t stride, int row0,
-                                       int nrows) {
-#pragma unroll
-    for (int s = 0; s < kPerThread; ++s) {
-      const int u = threadIdx.x + 256 * s;
-      const int row = u / (D / 8), c = u % (D / 8);
-      if (row0 + row < nrows)
-        r[s] = ld16(base + (int64_t)(row0 + row) * stride + c * 8);
-      else
-        r[s] = u32x4{0u, 0u, 0u, 0u};
-    }
+// Copy a [64 x D] bf16 tile of a THD tensor (row stride `stride` elements)
+// straight from global memory into a swizzled LDS tile with gfx950's
+// global_load_lds_dwordx4: no registers hold the data, so the next tile can
+// be in flight during a whole step of MFMA work. Each such instruction
+// writes 16 bytes per lane to consecutive LDS addresses (wave-uniform base
+// + 16 * lane, checked on the hardware), i.e. one 1 KB run per wave. A lane
+// therefore fetches the logical chunk that belongs at its physical position:
+// chunk (lane % (D/8)) ^ swz(row). Every pass advances the row by a multiple
+// of 16, which leaves swz(row) unchanged, so one offset per lane serves all
+// passes. Rows at or past the end of the sequence fetch its last row (finite,
+// in bounds; every consumer gives them zero weight). Completion is waited
+// for with wait_vmem() before the barrier that publishes the tile.
+template <int D, int THREADS = 256>
+struct TileDma {
+  static constexpr int kPer = 64 * D / 8 / THREADS;      // passes per tile
+  static constexpr int kRowsPerPass = THREADS / (D / 8);
+  static_assert(kRowsPerPass % 16 == 0, "a pass must keep the row swizzle");
+  int lrow;             // this lane's row in pass 0
+  int lcol;             // byte offset of the logical chunk this lane fetches
+  int wave_off;         // byte offset of this wave's 1 KB run within a pass
+  __device__ __forceinline__ void init() {
+    lrow = threadIdx.x / (D / 8);
+    lcol = (((threadIdx.x % (D / 8)) ^ swz<D>(lrow)) * 16);
+    wave_off = __builtin_amdgcn_readfirstlane((threadIdx.x / 64) * 1024);
   }
-  __device__ __forceinline__ void store(char* tile) const {
+  // rows [row0, row0 + 64) of the tensor at `base` into `tile`; the caller
+  // guarantees row0 < nrows
+  __device__ __forceinline__ void load(const bf16* base, int64_t stride, int row0, int nrows,
+                                       char* tile) const {
+    const char* p = reinterpret_cast<const char*>(base + (int64_t)row0 * stride);
+    const int lim = nrows - row0 - 1;
+    const int stride2 = (int)(stride * 2);
 #pragma unroll
-    for (int s = 0; s < kPerThread; ++s) {
-      const int u = threadIdx.x + 256 * s;
-      lds_store_chunk<D>(tile, u / (D / 8), u % (D / 8), r[s]);
+    for (int s = 0; s < kPer; ++s) {
+      const int row = min(lrow + s * kRowsPerPass, lim);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(p + (uint32_t)(row * stride2 + lcol)),
+          (__attribute__((address_space(3))) void*)(tile + s * THREADS * 16 + wave_off), 16, 0, 0);
     }
   }
 };
