@@ -366,12 +366,22 @@ def _full_span(live_lo, cls_line):
     return lo, hi
 
 
+def _dispatch_order(items):
+    """Sequences by their total live tile count (descending, ties: lower b
+    first); inside a sequence live tile count descending, then tile index."""
+    work = {}
+    for it in items:
+        work[it[0]] = work.get(it[0], 0) + (it[3] - it[2])
+    items.sort(key=lambda it: (-work[it[0]], it[0], -(it[3] - it[2]), it[1]))
+    return items
+
+
 def forward_items(cu_q, cu_k, tile_q, tile_k, causal, win_left, win_right):
     """One item per (sequence b, q tile qt), including items with no live key
     tile (their rows still produce out = 0, lse = sink). Item =
     (b, qt, kt_lo, kt_hi, kf_lo, kf_hi): live key tiles [kt_lo, kt_hi), of
     which [kf_lo, kf_hi) are FULL (empty full range = (kt_lo, kt_lo); empty
-    live range = (0, 0)). Order: live tile count descending, then b, then qt."""
+    live range = (0, 0)). Order: _dispatch_order."""
     items = []
     for b in range(len(cu_q) - 1):
         Lq, Lk = int(cu_q[b + 1] - cu_q[b]), int(cu_k[b + 1] - cu_k[b])
@@ -383,15 +393,14 @@ def forward_items(cu_q, cu_k, tile_q, tile_k, causal, win_left, win_right):
             lo, hi = _span(cls[qt] != DEAD) if cls.shape[1] else (0, 0)
             flo, fhi = _full_span(lo, cls[qt]) if cls.shape[1] else (0, 0)
             items.append((b, qt, lo, hi, flo, fhi))
-    items.sort(key=lambda it: (-(it[3] - it[2]), it[0], it[1]))
-    return items
+    return _dispatch_order(items)
 
 
 def backward_items(cu_q, cu_k, tile_q, tile_k, causal, win_left, win_right):
     """One item per (sequence b, key tile kt), including key tiles that no
     query sees (their dK, dV are still written as 0). Item =
     (b, kt, qt_lo, qt_hi, qf_lo, qf_hi) over q tiles of tile_q rows, same
-    conventions and order (live count desc, b, kt) as forward_items."""
+    conventions and order as forward_items."""
     items = []
     for b in range(len(cu_q) - 1):
         Lq, Lk = int(cu_q[b + 1] - cu_q[b]), int(cu_k[b + 1] - cu_k[b])
@@ -404,8 +413,7 @@ def backward_items(cu_q, cu_k, tile_q, tile_k, causal, win_left, win_right):
             lo, hi = _span(col != DEAD) if cls.shape[0] else (0, 0)
             flo, fhi = _full_span(lo, col) if cls.shape[0] else (0, 0)
             items.append((b, kt, lo, hi, flo, fhi))
-    items.sort(key=lambda it: (-(it[3] - it[2]), it[0], it[1]))
-    return items
+    return _dispatch_order(items)
 
 
 def decode_items(cu_q, cu_k, tile_k, chunk_keys, causal, win_left, win_right):

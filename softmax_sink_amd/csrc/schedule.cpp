@@ -80,12 +80,19 @@ void spans(const std::vector<int>& cls, int32_t* out4) {
   out4[0] = lo; out4[1] = hi; out4[2] = flo; out4[3] = fhi;
 }
 
-void sort_items(std::vector<Item>& v) {
-  // live count descending, then sequence, then tile (the pair is unique)
-  std::sort(v.begin(), v.end(), [](const Item& x, const Item& y) {
-    int lx = x.w[3] - x.w[2], ly = y.w[3] - y.w[2];
-    if (lx != ly) return lx > ly;
+// Dispatch order: sequences by their total live tile count, descending
+// (ties: lower index first); inside a sequence, live tile count descending,
+// then tile index. Heavy work starts first, and the blocks that run at the
+// same time mostly belong to one sequence, so they share its K/V (forward)
+// or Q/dO (backward) tiles in L2.
+void sort_items(std::vector<Item>& v, int batch) {
+  std::vector<int64_t> work(static_cast<size_t>(batch), 0);
+  for (const Item& it : v) work[it.w[0]] += it.w[3] - it.w[2];
+  std::sort(v.begin(), v.end(), [&](const Item& x, const Item& y) {
+    if (work[x.w[0]] != work[y.w[0]]) return work[x.w[0]] > work[y.w[0]];
     if (x.w[0] != y.w[0]) return x.w[0] < y.w[0];
+    const int lx = x.w[3] - x.w[2], ly = y.w[3] - y.w[2];
+    if (lx != ly) return lx > ly;
     return x.w[1] < y.w[1];
   });
 }
@@ -231,8 +238,8 @@ sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
     }
     dec_seq[2 * b + 1] = static_cast<int32_t>(dec.size()) - dec_seq[2 * b];
   }
-  sort_items(fwd);
-  sort_items(bwd);
+  sort_items(fwd, B);
+  sort_items(bwd, B);
 
   const int32_t mode =
       (static_cast<int64_t>(p.max_seqlen_q) * G <= kDecMaxRows) ? kModeDecode

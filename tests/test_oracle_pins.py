@@ -409,8 +409,12 @@ def test_items_cover_every_kept_element():
             if fhi > flo:
                 assert blk.shape == (tq, (fhi - flo) * tk) and blk.all()
         assert covered == O.count_kept_pairs(cu_q, cu_k, causal, wl, wr)
-        keys = [(-(it[3] - it[2]), it[0], it[1]) for it in items]
+        work = {}
+        for it in items:
+            work[it[0]] = work.get(it[0], 0) + it[3] - it[2]
+        keys = [(-work[it[0]], it[0], -(it[3] - it[2]), it[1]) for it in items]
         assert keys == sorted(keys)
+        assert len({(it[0], it[1]) for it in items}) == len(items)
         bitems = O.backward_items(cu_q, cu_k, tq, tk, causal, wl, wr)
         covered = 0
         for b, kt, lo, hi, flo, fhi in bitems:
