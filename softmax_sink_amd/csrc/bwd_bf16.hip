@@ -35,68 +35,44 @@ namespace {
 
 using namespace dev;
 
+// LDS of the dK/dV kernel. Step j of a work item is one (q-head, 64-row
+// query tile). Role 1 works one step behind role 0, so three Q tiles are
+// live at once (role 0's, role 1's and the one in flight) and two dO tiles;
+// lse and D rows travel with their Q and dO stages. P of a step is handed
+// from role 0 to role 1 as bf16 MFMA fragments ("dumps", one per parity).
 template <int D>
 struct KvSmem {
-  static constexpr int kQ = kBwdBM * D * 2;       // Q tile [64][D]
-  static constexpr int off_q = 0;
-  static constexpr int off_do = off_q + kQ;       // dO tile
-  static constexpr int off_lse = off_do + kQ;     // [64] fp32, log2 domain
-  static constexpr int off_dv = off_lse + 256;    // [64] fp32
-  static constexpr int stage = off_dv + 256;      // one buffer
-  static constexpr int off_p = 2 * stage;         // P^T [128 keys][64 q] fp32
-  static constexpr int bytes = off_p + kBwdBN * kBwdBM * 4;
+  static constexpr int kTile = kBwdBM * D * 2;          // one [64][D] bf16 tile
+  static constexpr int off_q = 0;                       // Q of step j: stage j % 3
+  static constexpr int off_do = off_q + 3 * kTile;      // dO of step j: stage j % 2
+  static constexpr int off_lse = off_do + 2 * kTile;    // 3 x [64] fp32, log2 domain
+  static constexpr int off_dval = off_lse + 3 * 256;    // 2 x [64] fp32
+  static constexpr int kHalfDump = 8 * 64 * 16;         // 8 fragments x 64 lanes x 16 B
+  static constexpr int off_p = off_dval + 2 * 256;      // P of step j: dump j % 2
+  static constexpr int bytes = off_p + 2 * 2 * kHalfDump;
 };
 
-constexpr int kKvThreads = 512;                   // 8 waves: 4 key slices x 2 roles
+constexpr int kKvThreads = 256;                   // 4 waves: 2 roles x 2 key halves
 
-// The next (q-head, query tile) step's Q and dO go straight to LDS; its lse
-// and D rows (64 floats each) go through registers.
-template <int D>
-struct QTileLoader {
-  TileDma<D, kKvThreads> q, d;
-  float lse, dval;
-  bool live;
-  int64_t stride;
-  __device__ __forceinline__ void init(const BwdArgs& a) {
-    stride = (int64_t)a.hq * D;
-    q.init();
-    d.init();
-  }
-  __device__ __forceinline__ void load(const BwdArgs& a, int h, int q0, int lq, int qt,
-                                       char* buf) {
-    using S = KvSmem<D>;
-    const bf16* qp = static_cast<const bf16*>(a.q) + (int64_t)q0 * stride + h * D;
-    const bf16* dp = static_cast<const bf16*>(a.dout) + (int64_t)q0 * stride + h * D;
-    q.load(qp, stride, qt * kBwdBM, lq, buf + S::off_q);
-    d.load(dp, stride, qt * kBwdBM, lq, buf + S::off_do);
-    if (threadIdx.x < kBwdBM) {
-      // raw values only (converting here would wait for the load at once);
-      // rows past the sequence read its last row and are flagged
-      const int row = qt * kBwdBM + threadIdx.x;
-      live = row < lq;
-      const int64_t at = (int64_t)h * a.total_q + q0 + min(row, lq - 1);
-      lse = a.lse[at];
-      dval = a.dval[at];
-    }
-  }
-  __device__ __forceinline__ void store(char* buf) const {
-    using S = KvSmem<D>;
-    if (threadIdx.x < kBwdBM) {
-      // log2-domain lse; rows past the sequence, and rows with lse = -inf
-      // (no kept key), get +inf so that every P of them is 0
-      reinterpret_cast<float*>(buf + S::off_lse)[threadIdx.x] =
-          (!live || lse == kNegInf) ? __builtin_huge_valf() : lse * kLog2e;
-      reinterpret_cast<float*>(buf + S::off_dv)[threadIdx.x] = live ? dval : 0.f;
-    }
+// (q-head offset g, query tile t) of consecutive steps: t runs fastest.
+struct StepIdx {
+  int g = 0, t = 0;
+  __device__ __forceinline__ void next(int nq) {
+    if (++t == nq) { t = 0; ++g; }
   }
 };
 
-// dK/dV, key-tile outer. Waves 0-3 (role 0) own keys 32w..32w+31 of the
-// item and compute S = Q K^T, P and dV^T += dO^T P; waves 4-7 (role 1) own
-// the same key slices and compute dP = dO V^T, dS = scale P (dP - D) with
-// the P that role 0 leaves in LDS, and dK^T += Q^T dS. Each wave holds one
-// operand fragment and one accumulator set, so two waves share every SIMD,
-// and per SIMD the two roles issue the same number of MFMAs.
+// dK/dV, key-tile outer, one wave per SIMD. Wave w owns the 64 keys
+// 64(w&1)..64(w&1)+63 of the item in role w>>1:
+//   role 0: S = Q K^T, P = 2^(S scale log2e - lse log2e), dV^T += dO^T P
+//   role 1: dP = dO V^T, dS = P (dP - D),                  dK^T += Q^T dS
+// A wave covers two 32-key MFMA blocks, so every operand read from LDS feeds
+// two MFMAs (one per key block): 1 LDS read per MFMA in total, against ~4.7
+// cycles of LDS issue per wave-instruction and 8 cycles of MFMA per CU.
+// In iteration i, role 0 computes S and P of step i and the dV update of
+// step i-1 (whose P it still holds), so the exponentials of step i can issue
+// between the dV MFMAs; role 1 computes all of step i-1 with the P that
+// role 0 left in LDS. One barrier per iteration; steps + 1 iterations.
 template <int D>
 __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using S = KvSmem<D>;
@@ -106,137 +82,251 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
   const int item = blockIdx.x / a.hk;
   const int hk = blockIdx.x % a.hk;
-  const int* it = a.items + item * kItemWords;
-  const int b = it[0], kt = it[1], qt_lo = it[2], qt_hi = it[3];
-  const int qf_lo = it[4], qf_hi = it[5];
+  const int* itw = a.items + item * kItemWords;
+  const int b = itw[0], kt = itw[1], qt_lo = itw[2], qt_hi = itw[3];
+  const int qf_lo = itw[4], qf_hi = itw[5];
   const int q0 = a.cu_q[b], lq = a.cu_q[b + 1] - q0;
   const int k0 = a.cu_k[b], lk = a.cu_k[b + 1] - k0;
   const int G = a.group;
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int role = w >> 2, kw = w & 3;
+  const int role = w >> 1, kh = w & 1;
   const int hl = lane >> 5, c = lane & 31;
-  const int j = kt * kBwdBN + 32 * kw + c;       // this lane's key
+  const int jbase = kt * kBwdBN + 64 * kh + c;   // this lane's key in block kb: jbase + 32 kb
 
   const int64_t kstride = (int64_t)a.hk * D;
+  const int64_t qstride = (int64_t)a.hq * D;
   // role 0 holds K rows (B operand of S = Q K^T), role 1 V rows (of dP = dO V^T)
   const bf16* fp = static_cast<const bf16*>(role == 0 ? a.k : a.v) + (int64_t)k0 * kstride + hk * D;
-  bf16x8 frag[NT];
+  bf16x8 frag[2][NT];
+  int ilo[2], ihi[2];
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
-    frag[t] = j < lk ? __builtin_bit_cast(bf16x8, ld16(fp + (int64_t)j * kstride + 16 * t + 8 * hl))
-                     : bf16x8{};
-
-  int ilo, ihi;
-  key_row_range(j, lq, lk, a.causal, a.win_left, a.win_right, ilo, ihi);
-
-  f32x16 acc[NB];                                // role 0: dV^T, role 1: dK^T
+  for (int kb = 0; kb < 2; ++kb) {
+    const int j = jbase + 32 * kb;
 #pragma unroll
-  for (int n = 0; n < NB; ++n) acc[n] = f32x16{};
+    for (int t = 0; t < NT; ++t)
+      frag[kb][t] = j < lk ? __builtin_bit_cast(bf16x8, ld16(fp + (int64_t)j * kstride + 16 * t + 8 * hl))
+                           : bf16x8{};
+    key_row_range(j, lq, lk, a.causal, a.win_left, a.win_right, ilo[kb], ihi[kb]);
+  }
 
+  f32x16 acc[NB][2];                             // role 0: dV^T, role 1: dK^T
+#pragma unroll
+  for (int n = 0; n < NB; ++n) acc[n][0] = acc[n][1] = f32x16{};
   const int nq = qt_hi - qt_lo;
   const int steps = nq * G;
   const float c2 = a.scale * kLog2e;
-  char* p_l = smem + S::off_p;
+  const bf16* qg = static_cast<const bf16*>(a.q) + (int64_t)q0 * qstride + (int64_t)hk * G * D;
+  const bf16* dg = static_cast<const bf16*>(a.dout) + (int64_t)q0 * qstride + (int64_t)hk * G * D;
+  const int64_t rbase = ((int64_t)hk * G) * a.total_q + q0;   // lse / D row of (g = 0, row 0)
 
-  QTileLoader<D> ld;
-  ld.init(a);
+  TileDma<D, kKvThreads> dma;
+  dma.init();
+  // lse / D rows of a step: raw values in registers of wave 0 (converting at
+  // once would wait for the load), written to LDS at the end of the iteration
+  float lse_raw = 0.f, dval_raw = 0.f;
+  bool lse_live = false, dval_live = false;
+
   if (steps > 0) {
-    ld.load(a, hk * G, q0, lq, qt_lo, smem);
-    ld.store(smem);
+    dma.load(qg, qstride, qt_lo * kBwdBM, lq, smem + S::off_q);
+    if (threadIdx.x < kBwdBM) {
+      const int row = qt_lo * kBwdBM + threadIdx.x;
+      const float l = a.lse[rbase + min(row, lq - 1)];
+      reinterpret_cast<float*>(smem + S::off_lse)[threadIdx.x] =
+          (row >= lq || l == kNegInf) ? __builtin_huge_valf() : l * kLog2e;
+    }
+    // dO stage 1 is read by role 0's (empty) dV update in iteration 0
+    for (int o = threadIdx.x * 16; o < S::kTile; o += kKvThreads * 16)
+      *reinterpret_cast<u32x4*>(smem + S::off_do + S::kTile + o) = u32x4{};
   }
   wait_vmem();
   __syncthreads();
 
-  // (one copy of the loop body with a run-time buffer offset measures faster
-  // here than two copies with constant offsets)
-  for (int st = 0; st < steps; ++st) {
-    const int stage = st & 1;
-    const int qt = qt_lo + st % nq;
-    const bool more = st + 1 < steps;
-    if (more) ld.load(a, hk * G + (st + 1) / nq, q0, lq, qt_lo + (st + 1) % nq,
-                      smem + (stage ^ 1) * S::stage);
-    const char* buf = smem + stage * S::stage;
-    const char* q_l = buf + S::off_q;
-    const char* do_l = buf + S::off_do;
-    const float* lse_l = reinterpret_cast<const float*>(buf + S::off_lse);
-    const float* dv_l = reinterpret_cast<const float*>(buf + S::off_dv);
-    const bool partial = qt < qf_lo || qt >= qf_hi;
-
-    // phase 1: role 0 S = Q K^T -> P (to LDS); role 1 dP = dO V^T.
-    // Query row of result slot r of block qb is 32qb + 8(r/4) + 4hl + r%4.
-    const char* a_l = role == 0 ? q_l : do_l;
-    f32x16 x[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      x[qb] = f32x16{};
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-        x[qb] = mfma32(lds_row_chunk<D>(a_l, 32 * qb + c, 2 * t + hl), frag[t], x[qb]);
+  StepIdx sq, sd;                                // steps it + 1 (Q) and it (dO)
+  sq.next(nq);
+  // Start of iteration it: prefetch Q of step it + 1 (into Q stage
+  // (it + 1) % 3) and dO of step it (into dO stage it % 2), with their lse
+  // and D rows.
+  auto prefetch = [&](int it, int qs_next, int ds) __attribute__((always_inline)) {
+    if (it + 1 < steps) {
+      const int qt = qt_lo + sq.t;
+      dma.load(qg + sq.g * D, qstride, qt * kBwdBM, lq, smem + S::off_q + qs_next * S::kTile);
+      if (threadIdx.x < kBwdBM) {
+        const int row = qt * kBwdBM + threadIdx.x;
+        lse_live = row < lq;
+        lse_raw = a.lse[rbase + (int64_t)sq.g * a.total_q + min(row, lq - 1)];
+      }
     }
-    if (role == 0) {
+    if (it < steps) {
+      const int qt = qt_lo + sd.t;
+      dma.load(dg + sd.g * D, qstride, qt * kBwdBM, lq, smem + S::off_do + ds * S::kTile);
+      if (threadIdx.x < kBwdBM) {
+        const int row = qt * kBwdBM + threadIdx.x;
+        dval_live = row < lq;
+        dval_raw = a.dval[rbase + (int64_t)sd.g * a.total_q + min(row, lq - 1)];
+      }
+    }
+  };
+  // End of iteration it: lse / D rows of the prefetched steps (log2-domain
+  // lse, +inf for rows past the sequence or with no kept key, so that their
+  // P is 0), then wait for the tiles and publish everything.
+  auto finish = [&](int it, int qs_next, int ds) __attribute__((always_inline)) {
+    if (threadIdx.x < kBwdBM) {
+      if (it + 1 < steps)
+        reinterpret_cast<float*>(smem + S::off_lse + qs_next * 256)[threadIdx.x] =
+            (!lse_live || lse_raw == kNegInf) ? __builtin_huge_valf() : lse_raw * kLog2e;
+      if (it < steps)
+        reinterpret_cast<float*>(smem + S::off_dval + ds * 256)[threadIdx.x] = dval_live ? dval_raw : 0.f;
+    }
+    wait_vmem();
+    __syncthreads();
+    sq.next(nq);
+    sd.next(nq);
+  };
+
+  // The two roles run separate loops with the same barrier sequence (one
+  // per iteration), so that each is register-allocated on its own.
+  if (steps > 0 && role == 0) {
+    bf16x8 pf[2][2][2];                          // P of the previous step [qb][kb][half]
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+    for (int f = 0; f < 8; ++f) pf[f >> 2][(f >> 1) & 1][f & 1] = bf16x8{};
+    int qs = 0;                                  // it % 3
+    for (int it = 0; it <= steps; ++it) {
+      const int qs_next = qs == 2 ? 0 : qs + 1;
+      const int ds = it & 1;
+      prefetch(it, qs_next, ds);
+      const char* q_l = smem + S::off_q + qs * S::kTile;
+      const float* lse_l = reinterpret_cast<const float*>(smem + S::off_lse + qs * 256);
+      const char* dop_l = smem + S::off_do + (ds ^ 1) * S::kTile;
+      char* dump = smem + S::off_p + (2 * ds + kh) * S::kHalfDump;
+      const int qt = qt_lo + sd.t;
+      const bool partial = it < steps && (qt < qf_lo || qt >= qf_hi);
+      // One 32-row query block at a time: S and P of step it, and the half
+      // of the dV update of step it - 1 that uses the same P registers (in
+      // iteration 0: zero P against a zeroed tile). Query row of slot r of
+      // block qb is 32qb + 8(r/4) + 4hl + r%4. After the last step the Q
+      // stage holds stale (or never written) data; that P is never read.
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x16 x0 = f32x16{}, x1 = f32x16{};
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const bf16x8 qa = lds_row_chunk<D>(q_l, 32 * qb + c, 2 * t + hl);
+          x0 = mfma32(qa, frag[0][t], x0);
+          x1 = mfma32(qa, frag[1][t], x1);
+        }
+        sched_mfma_pipeline<2 * NT, 2, 1, 3>();
+        if (partial) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int i = qt * kBwdBM + 32 * qb + 8 * (r >> 2) + 4 * hl + (r & 3);
+            if (i < ilo[0] || i > ihi[0]) x0[r] = kNegInf;
+            if (i < ilo[1] || i > ihi[1]) x1[r] = kNegInf;
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int db = 0; db < NB; ++db) {
+            const bf16x8 da = lds_col_operand<D>(dop_l, 16 * (2 * qb + h), 32 * db);
+            acc[db][0] = mfma32(da, pf[qb][0][h], acc[db][0]);
+            acc[db][1] = mfma32(da, pf[qb][1][h], acc[db][1]);
+          }
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const int qq = 32 * qb + 8 * g4 + 4 * hl;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_l + qq);
-          f32x4 p4;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_l + 32 * qb + 8 * g4 + 4 * hl);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            float p = exp2_hw(__builtin_fmaf(x[qb][4 * g4 + e], c2, -l4[e]));
-            if (partial) {
-              const int i = qt * kBwdBM + qq + e;
-              if (i < ilo || i > ihi) p = 0.f;
-            }
-            x[qb][4 * g4 + e] = p;
-            p4[e] = p;
+            x0[4 * g4 + e] = exp2_hw(__builtin_fmaf(x0[4 * g4 + e], c2, -l4[e]));
+            x1[4 * g4 + e] = exp2_hw(__builtin_fmaf(x1[4 * g4 + e], c2, -l4[e]));
           }
-          *reinterpret_cast<f32x4*>(p_l + tile_off<128>(32 * kw + c, 2 * qq)) = p4;
         }
-    }
-    __syncthreads();
-
-    // phase 2: role 0 dV^T += dO^T P; role 1 dS = scale P (dP - D), dK^T += Q^T dS
-    if (role == 1) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int qq = 32 * qb + 8 * g4 + 4 * hl;
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dv_l + qq);
-          const f32x4 p4 = *reinterpret_cast<const f32x4*>(p_l + tile_off<128>(32 * kw + c, 2 * qq));
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            x[qb][4 * g4 + e] = p4[e] * (x[qb][4 * g4 + e] - d4[e]);   // dK scaled at the end
+        for (int h = 0; h < 2; ++h) {
+          pf[qb][0][h] = frag_half(x0, h);
+          pf[qb][1][h] = frag_half(x1, h);
+          *reinterpret_cast<bf16x8*>(dump + ((4 * qb + h) * 64 + lane) * 16) = pf[qb][0][h];
+          *reinterpret_cast<bf16x8*>(dump + ((4 * qb + 2 + h) * 64 + lane) * 16) = pf[qb][1][h];
         }
+      }
+      finish(it, qs_next, ds);
+      qs = qs_next;
     }
-    const char* t_l = role == 0 ? do_l : q_l;
+  } else if (steps > 0) {
+    int qs = 0;
+    for (int it = 0; it <= steps; ++it) {
+      const int qs_next = qs == 2 ? 0 : qs + 1;
+      const int qs_prev = qs == 0 ? 2 : qs - 1;  // (it - 1) % 3
+      const int ds = it & 1;
+      prefetch(it, qs_next, ds);
+      if (it > 0) {
+        // step it - 1, one 32-row query block at a time:
+        // dP = dO V^T, dS = P (dP - D), dK^T += Q^T dS
+        const char* do_l = smem + S::off_do + (ds ^ 1) * S::kTile;
+        const float* dv_l = reinterpret_cast<const float*>(smem + S::off_dval + (ds ^ 1) * 256);
+        const char* qq_l = smem + S::off_q + qs_prev * S::kTile;
+        const char* dump = smem + S::off_p + (2 * (ds ^ 1) + kh) * S::kHalfDump;
 #pragma unroll
-    for (int tq = 0; tq < 4; ++tq) {
-      const bf16x8 f = frag_half(x[tq >> 1], tq & 1);
+        for (int qb = 0; qb < 2; ++qb) {
+          f32x16 x0 = f32x16{}, x1 = f32x16{};
 #pragma unroll
-      for (int n = 0; n < NB; ++n)
-        acc[n] = mfma32(lds_col_operand<D>(t_l, 16 * tq, 32 * n), f, acc[n]);
+          for (int t = 0; t < NT; ++t) {
+            const bf16x8 ga = lds_row_chunk<D>(do_l, 32 * qb + c, 2 * t + hl);
+            x0 = mfma32(ga, frag[0][t], x0);
+            x1 = mfma32(ga, frag[1][t], x1);
+          }
+          sched_mfma_pipeline<2 * NT, 2, 1, 3>();
+          bf16x8 pp[4];                          // [kb][half]
+#pragma unroll
+          for (int f = 0; f < 4; ++f)
+            pp[f] = *reinterpret_cast<const bf16x8*>(dump + ((4 * qb + f) * 64 + lane) * 16);
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(dv_l + 32 * qb + 8 * g4 + 4 * hl);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * g4 + e;
+              // dK is scaled at the end
+              x0[r] = (float)pp[r >> 3][r & 7] * (x0[r] - d4[e]);
+              x1[r] = (float)pp[2 + (r >> 3)][r & 7] * (x1[r] - d4[e]);
+            }
+          }
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const bf16x8 s0 = frag_half(x0, h);
+            const bf16x8 s1 = frag_half(x1, h);
+#pragma unroll
+            for (int db = 0; db < NB; ++db) {
+              const bf16x8 qa = lds_col_operand<D>(qq_l, 16 * (2 * qb + h), 32 * db);
+              acc[db][0] = mfma32(qa, s0, acc[db][0]);
+              acc[db][1] = mfma32(qa, s1, acc[db][1]);
+            }
+          }
+          sched_mfma_pipeline<4 * NB, 2, 2, 2>();
+        }
+      }
+      finish(it, qs_next, ds);
+      qs = qs_next;
     }
-    if (more) ld.store(smem + (stage ^ 1) * S::stage);
-    wait_vmem();        // the next Q/dO tile has landed in LDS
-    __syncthreads();
   }
 
-  // role 0 writes dV, role 1 dK (times the softmax scale), for this wave's keys
-  if (j < lk) {
-    bf16* dst = static_cast<bf16*>(role == 0 ? a.dv : a.dk) + (int64_t)(k0 + j) * kstride + hk * D;
-    const float sc = role == 0 ? 1.f : a.scale;
+  // role 0 writes dV, role 1 dK (times the softmax scale)
+  const float sc = role == 0 ? 1.f : a.scale;
 #pragma unroll
-    for (int n = 0; n < NB; ++n)
+  for (int kb = 0; kb < 2; ++kb) {
+    const int j = jbase + 32 * kb;
+    if (j < lk) {
+      bf16* dst = static_cast<bf16*>(role == 0 ? a.dv : a.dk) + (int64_t)(k0 + j) * kstride + hk * D;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = 32 * n + 8 * g4 + 4 * hl;
-        *reinterpret_cast<u32x2*>(dst + d) =
-            pack4_bits(acc[n][4 * g4] * sc, acc[n][4 * g4 + 1] * sc, acc[n][4 * g4 + 2] * sc,
-                       acc[n][4 * g4 + 3] * sc);
-      }
+      for (int db = 0; db < NB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = 32 * db + 8 * g4 + 4 * hl;
+          *reinterpret_cast<u32x2*>(dst + d) =
+              pack4_bits(acc[db][kb][4 * g4] * sc, acc[db][kb][4 * g4 + 1] * sc,
+                         acc[db][kb][4 * g4 + 2] * sc, acc[db][kb][4 * g4 + 3] * sc);
+        }
+    }
   }
 }
 

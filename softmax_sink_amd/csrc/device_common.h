@@ -147,6 +147,35 @@ __device__ __forceinline__ u32x2 pack4_bits(float a, float b, float c, float d) 
 // wait for the prefetch of the next tile.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Instruction-group directives for the machine scheduler
+// (llvm.amdgcn.sched.group.barrier): the instructions of one scheduling
+// region are placed in the order of the groups requested, e.g. "3 LDS
+// reads, then 2 MFMAs and 1 LDS read, repeated", which keeps operand reads
+// a few MFMAs ahead of their use instead of waiting on each one.
+enum SchedMask : int {
+  kSchedValu = 0x002,
+  kSchedMfma = 0x008,
+  kSchedDsRead = 0x100,
+  kSchedDsWrite = 0x200,
+};
+template <int MASK, int N>
+__device__ __forceinline__ void sched_group() {
+  __builtin_amdgcn_sched_group_barrier(MASK, N, 0);
+}
+// LEAD groups of READS LDS reads up front, then (MFMAS MFMAs, READS reads)
+// until the reads run out, then the remaining MFMAs.
+template <int NMFMA, int MFMAS, int READS, int LEAD>
+__device__ __forceinline__ void sched_mfma_pipeline() {
+  constexpr int kGroups = NMFMA / MFMAS;
+  sched_group<kSchedDsRead, LEAD * READS>();
+#pragma unroll
+  for (int g = 0; g < kGroups - LEAD; ++g) {
+    sched_group<kSchedMfma, MFMAS>();
+    sched_group<kSchedDsRead, READS>();
+  }
+  sched_group<kSchedMfma, LEAD * MFMAS>();
+}
+
 // Global 16-byte load / store helpers.
 __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);

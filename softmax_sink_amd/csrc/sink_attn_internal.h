@@ -37,7 +37,7 @@ enum Mode : int32_t { kModePrefill = 0, kModeDecode = 1 };
 constexpr int kFwdBM = 128;    // query rows per forward work item (4 waves x 32)
 constexpr int kFwdBN = 64;     // keys per forward tile step
 constexpr int kBwdBM = 64;     // query rows per backward tile step
-constexpr int kBwdBN = 128;    // keys per backward work item (4 waves x 32)
+constexpr int kBwdBN = 128;    // keys per backward work item (2 halves of 64)
 constexpr int kDecBN = 64;     // keys per split-KV tile step
 constexpr int kDecChunk = 2048;// keys per split-KV work item
 constexpr int kDecMaxRows = 64;// (query rows x GQA group) handled per split item

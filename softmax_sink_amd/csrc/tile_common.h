@@ -8,12 +8,27 @@
 namespace sinkattn {
 namespace dev {
 
+// Word 3 of a raw buffer descriptor on gfx9-family parts: 32-bit data
+// format, no swizzle, no index stride.
+constexpr int kBufferWord3 = 0x00020000;
+
 // Copy a [64 x D] bf16 tile of a THD tensor (row stride `stride` elements)
 // straight from global memory into a swizzled LDS tile with gfx950's
-// global_load_lds_dwordx4: no registers hold the data, so the next tile can
-// be in flight during a whole step of MFMA work. Each such instruction
+// buffer_load_dwordx4 ... lds: no registers hold the data, so the next tile
+// can be in flight during a whole step of MFMA work. Each such instruction
 // writes 16 bytes per lane to consecutive LDS addresses (wave-uniform base
-// + 16 * lane, checked on the hardware), i.e. one 1 KB run per wave. A lane
+// in M0 + 16 * lane, checked on the hardware), i.e. one 1 KB run per wave.
+//
+// The instruction is issued from inline assembly, invisible to the
+// compiler's wait-count tracking. Through the builtin, the compiler cannot
+// tell the tile in flight from the tiles being read (the transposed LDS
+// reads carry no alias information), so it waits for the whole prefetch
+// (vmcnt(0)) before the first such read of every step, and a FLAT-encoded
+// form additionally turns every LDS wait into lgkmcnt(0). The kernels
+// instead wait for their prefetches explicitly (wait_vmem() before the
+// barrier that publishes a tile) and never touch a tile in flight. The
+// assembly has no outputs; its address operands are read at issue, and it
+// clobbers M0 and memory. A lane
 // therefore fetches the logical chunk that belongs at its physical position:
 // chunk (lane % (D/8)) ^ swz(row). Every pass advances the row by a multiple
 // of 16, which leaves swz(row) unchanged, so one offset per lane serves all
@@ -33,20 +48,49 @@ struct TileDma {
     lcol = (((threadIdx.x % (D / 8)) ^ swz<D>(lrow)) * 16);
     wave_off = __builtin_amdgcn_readfirstlane((threadIdx.x / 64) * 1024);
   }
+  // One tile transfer, prepared (uniform values only) and then issued in
+  // parts, so that a kernel can spread the issue over its MFMA work: the
+  // issue of a wave stalls while the memory pipeline is backed up.
+  struct Tile {
+    __amdgpu_buffer_rsrc_t rsrc;
+    uint32_t lds;       // LDS address of this wave's run in pass 0
+    int lim;            // last valid row, relative to the tile's first row
+    int stride2;        // row stride in bytes
+  };
   // rows [row0, row0 + 64) of the tensor at `base` into `tile`; the caller
   // guarantees row0 < nrows
+  __device__ __forceinline__ Tile prepare(const bf16* base, int64_t stride, int row0, int nrows,
+                                          char* tile) const {
+    Tile t;
+    // raw buffer over the tile's first row; rows are clamped to lim, so the
+    // range check (2 GiB) never trims a load
+    t.rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16*>(base + (int64_t)row0 * stride), (short)0, 0x7FFFFFFF, kBufferWord3);
+    t.lds = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(tile + wave_off));
+    t.lim = nrows - row0 - 1;
+    t.stride2 = (int)(stride * 2);
+    return t;
+  }
+  // passes [S0, S1) of a prepared tile
+  template <int S0, int S1>
+  __device__ __forceinline__ void issue(const Tile& t) const {
+#pragma unroll
+    for (int s = S0; s < S1; ++s) {
+      const int row = min(lrow + s * kRowsPerPass, t.lim);
+      const uint32_t voff = (uint32_t)(row * t.stride2 + lcol);
+      asm volatile(
+          "s_mov_b32 m0, %2\n\t"
+          "s_nop 0\n\t"
+          "buffer_load_dwordx4 %1, %0, 0 offen lds"
+          :
+          : "s"(t.rsrc), "v"(voff), "s"(t.lds + s * THREADS * 16)
+          : "memory", "m0");
+    }
+  }
   __device__ __forceinline__ void load(const bf16* base, int64_t stride, int row0, int nrows,
                                        char* tile) const {
-    const char* p = reinterpret_cast<const char*>(base + (int64_t)row0 * stride);
-    const int lim = nrows - row0 - 1;
-    const int stride2 = (int)(stride * 2);
-#pragma unroll
-    for (int s = 0; s < kPer; ++s) {
-      const int row = min(lrow + s * kRowsPerPass, lim);
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(p + (uint32_t)(row * stride2 + lcol)),
-          (__attribute__((address_space(3))) void*)(tile + s * THREADS * 16 + wave_off), 16, 0, 0);
-    }
+    issue<0, kPer>(prepare(base, stride, row0, nrows, tile));
   }
 };
 
