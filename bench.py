@@ -4,9 +4,10 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                 [--no-cpu-baseline]
 
 One step = the whole hot path over one batch: the host tile schedule
-(sink_attn_metadata) and its copy to the device, the forward
-(sink_attn_fwd) and, for training workloads, the backward (sink_attn_bwd),
-all through the C ABI on torch's current stream. Inputs are resident in HBM
+(sink_attn_metadata, or sink_attn_metadata_paged) and its copy to the
+device, the forward (sink_attn_fwd, or sink_attn_fwd_paged reading a paged
+K/V cache) and, for training workloads, the backward (sink_attn_bwd), all
+through the C ABI on torch's current stream. Inputs are resident in HBM
 before timing starts. Prints one JSON line.
 
 FLOPs count only kept (query row, key, q-head) pairs: 4*D per pair forward,
@@ -151,9 +152,23 @@ def main():
         del src, dst
     p = W.config(args.workload)
     train = args.workload in TRAIN
-    decode = args.workload == "decode_softmax_n"
+    paged = args.workload == "decode_paged"
+    decode = args.workload in ("decode_softmax_n", "decode_paged")
     D, Hq, Hk = p.head_dim, p.num_heads_q, p.num_heads_k
-    q, k, v = to_dev(p, "q"), to_dev(p, "k"), to_dev(p, "v")
+    q = to_dev(p, "q")
+    if paged:
+        layout = p.meta["paged"]
+        kv_desc = B.PagedKV(layout.block_size, layout.block_table.shape[1], layout.num_blocks)
+        k = torch.from_numpy(W.scatter_to_pages(p.k, p.cu_k, layout).view(np.int16)).view(
+            torch.bfloat16).cuda()
+        v = torch.from_numpy(W.scatter_to_pages(p.v, p.cu_k, layout).view(np.int16)).view(
+            torch.bfloat16).cuda()
+        bt_host = np.ascontiguousarray(layout.block_table, dtype=np.int32)
+        used_host = np.ascontiguousarray(layout.seqused, dtype=np.int32)
+        bt_dev = torch.from_numpy(bt_host).cuda()
+        used_dev = torch.from_numpy(used_host).cuda()
+    else:
+        k, v = to_dev(p, "k"), to_dev(p, "v")
     dout = to_dev(p, "dout") if train else None
     sinks = torch.from_numpy(p.sinks).cuda()
     scale = float(p.scale)
@@ -162,7 +177,13 @@ def main():
                              dtype_code)
     cu_q_dev = torch.from_numpy(p.cu_q).cuda()
     cu_k_dev = torch.from_numpy(p.cu_k).cuda()
-    meta0, fws, bws = B.sink_attn_metadata(problem, p.cu_q, p.cu_k)
+    if paged:
+        problem = B.make_problem_paged(p.cu_q, used_host, Hq, Hk, D, p.causal, p.win_left,
+                                       p.win_right, dtype_code)
+        meta0, fws = B.sink_attn_metadata_paged(problem, kv_desc, p.cu_q, used_host, bt_host)
+        bws = 0
+    else:
+        meta0, fws, bws = B.sink_attn_metadata(problem, p.cu_q, p.cu_k)
     # two pinned host / device metadata buffers, alternated across steps
     meta_host = [torch.empty(len(meta0), dtype=torch.int32).pin_memory() for _ in range(2)]
     meta_dev = [torch.empty(len(meta0), dtype=torch.int32, device="cuda") for _ in range(2)]
@@ -183,7 +204,10 @@ def main():
         if copied[slot] is not None:
             copied[slot].synchronize()       # the host buffer is free again
         mh = meta_host[slot].numpy()
-        m, _, _ = B.sink_attn_metadata(problem, cq, ck)
+        if paged:
+            m, _ = B.sink_attn_metadata_paged(problem, kv_desc, cq, used_host, bt_host)
+        else:
+            m, _, _ = B.sink_attn_metadata(problem, cq, ck)
         mh[:] = m
         meta_dev[slot].copy_(meta_host[slot], non_blocking=True)
         ev = torch.cuda.Event()
@@ -192,8 +216,12 @@ def main():
         if timed:
             s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             B.sink_attn_arm_timing(s0, s1)
-        B.sink_attn_fwd(problem, mh, meta_dev[slot], q, k, v, cu_q_dev, cu_k_dev, sinks,
-                        scale, out, lse, fwd_ws, fws)
+        if paged:
+            B.sink_attn_fwd_paged(problem, kv_desc, mh, meta_dev[slot], q, k, v, bt_dev,
+                                  cu_q_dev, used_dev, sinks, scale, out, lse, fwd_ws, fws)
+        else:
+            B.sink_attn_fwd(problem, mh, meta_dev[slot], q, k, v, cu_q_dev, cu_k_dev, sinks,
+                            scale, out, lse, fwd_ws, fws)
         if timed and not train:
             main_events.append(("fwd", s0, s1))
         if train:
@@ -233,6 +261,8 @@ def main():
         kv_bytes = 2.0 * p.total_k * Hk * D * esize
         qo_bytes = 2.0 * p.total_q * Hq * D * esize + 4.0 * p.total_q * Hq
         alg_bytes = kv_bytes + qo_bytes
+        if paged:   # the block-table entries of the pages in use
+            alg_bytes += 4.0 * int(((used_host + layout.block_size - 1) // layout.block_size).sum())
         achieved = alg_bytes / (kavg["fwd"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": "fwd_split_kernel", "achieved": achieved,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
@@ -251,7 +281,9 @@ def main():
                 "traffic": traffic_record(args.workload, kname),
                 "launch_ms": kavg[name], "flop_per_launch": flops}
     res = {
-        "metric": METRIC if train else f"sink-attention forward {'GB/s' if decode else 'TFLOP/s'}",
+        "metric": METRIC if train else
+        ("sink-attention decode forward TFLOP/s (split-KV" + (", paged K/V)" if paged else ")")
+         if decode else "sink-attention forward TFLOP/s"),
         "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": p.dtype, "data": "synthetic",
@@ -259,7 +291,9 @@ def main():
                    "total_k": p.total_k, "heads_q": Hq, "heads_kv": Hk, "head_dim": D,
                    "causal": p.causal, "window": [p.win_left, p.win_right],
                    "seed": p.seed, "kept_pairs": pairs,
-                   "passes": "metadata+fwd+bwd" if train else "metadata+fwd"},
+                   "passes": "metadata+fwd+bwd" if train else "metadata+fwd",
+                   **({"kv_pages": {"block_size": layout.block_size,
+                                    "num_blocks": layout.num_blocks}} if paged else {})},
         "frac_of_bf16_peak": value / PEAK_BF16_TFLOPS,
         "main_kernel_ms": kavg,
         "roofline": roof,

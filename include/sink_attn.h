@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define SINK_ATTN_ABI_VERSION 1
+#define SINK_ATTN_ABI_VERSION 2
 
 typedef enum {
   SINK_ATTN_OK = 0,
@@ -143,9 +143,9 @@ sink_attn_status sink_attn_fwd(const sink_attn_problem* p,
  * sink_attn_fwd wrote for the same inputs; dout has the layout of out.
  * Writes dq, dk, dv (dtype) and dsink ([num_heads_q] fp32). dsink must be
  * NULL exactly when sink_logits is NULL. workspace must hold
- * bwd_workspace_bytes. dq accumulates through fp32 atomics, so its last bits
- * may differ from run to run; dk, dv and dsink are deterministic.
- * Errors: as sink_attn_fwd. */
+ * bwd_workspace_bytes. Every output is deterministic: dq is computed by a
+ * query-tile-outer pass, not accumulated with atomics.
+ * Errors: as sink_attn_fwd; E_META_MISMATCH for a paged table. */
 sink_attn_status sink_attn_bwd(const sink_attn_problem* p,
                                const int32_t* meta_host,
                                const int32_t* meta_dev,
@@ -158,11 +158,69 @@ sink_attn_status sink_attn_bwd(const sink_attn_problem* p,
                                void* workspace, int64_t workspace_bytes,
                                hipStream_t stream);
 
+/* Paged K/V cache: the keys and values of a sequence live in fixed-size
+ * pages of one cache tensor, found through a block table ("CANN
+ * ops-transformer: flash_attn", Paged Attention parameter group and the
+ * PA_BBND k/v layout; "hf-attention-normalizers", Differentiable Paged
+ * Attention: the kernel reads physical pages through the block table and
+ * never gathers a copy). Layouts:
+ *   k_cache, v_cache : [num_blocks, block_size, num_heads_k, head_dim] (dtype)
+ *   block_table      : [batch, max_blocks_per_seq] int32
+ *   seqused_kv       : [batch] int32, keys of sequence b
+ * Key row r < seqused_kv[b] of sequence b is slot r % block_size of page
+ * block_table[b][r / block_size]. Pages may be shared between sequences and
+ * appear in any order. Only the forward is paged. */
+typedef struct {
+  int32_t block_size;          /* 16..1024 and a multiple of 16 (CANN page) */
+  int32_t max_blocks_per_seq;  /* columns of block_table, > 0              */
+  int32_t num_blocks;          /* pages in each cache tensor, > 0          */
+} sink_attn_paged_kv;
+
+/* Tile schedule for a paged forward. As sink_attn_metadata, with the key
+ * lengths given as seqused_kv_host ([batch] int32; p->total_k must be their
+ * sum and p->max_seqlen_k their maximum) and the HOST copy of the block
+ * table, whose entries for the pages in use must lie in [0, num_blocks):
+ * they are checked here and hashed into the header, and the device copy
+ * passed to sink_attn_fwd_paged must equal it (not checked there). Only
+ * short query groups are supported (max_seqlen_q * num_heads_q /
+ * num_heads_k <= 64, the split-KV path) and only bf16: otherwise
+ * E_UNSUPPORTED. The table can only be used with sink_attn_fwd_paged.
+ * Errors: E_INVALID, E_UNSUPPORTED, E_BUFFER_TOO_SMALL. */
+sink_attn_status sink_attn_metadata_paged(const sink_attn_problem* p,
+                                          const sink_attn_paged_kv* kv,
+                                          const int32_t* cu_seqlens_q_host,
+                                          const int32_t* seqused_kv_host,
+                                          const int32_t* block_table_host,
+                                          int32_t* meta_host,
+                                          int64_t meta_capacity_words,
+                                          int64_t* meta_words,
+                                          int64_t* fwd_workspace_bytes);
+
+/* Paged forward. As sink_attn_fwd, with k_cache, v_cache, block_table and
+ * seqused_kv (device pointers, layouts above) in place of k, v and
+ * cu_seqlens_k. meta_host must come from sink_attn_metadata_paged for this
+ * problem and this *kv (E_META_MISMATCH otherwise). The results equal those
+ * of sink_attn_fwd on the gathered contiguous keys and values, bit for bit.
+ * Errors: as sink_attn_fwd. */
+sink_attn_status sink_attn_fwd_paged(const sink_attn_problem* p,
+                                     const sink_attn_paged_kv* kv,
+                                     const int32_t* meta_host,
+                                     const int32_t* meta_dev, const void* q,
+                                     const void* k_cache, const void* v_cache,
+                                     const int32_t* block_table,
+                                     const int32_t* cu_seqlens_q,
+                                     const int32_t* seqused_kv,
+                                     const float* sink_logits, float scale,
+                                     void* out, float* lse, void* workspace,
+                                     int64_t workspace_bytes,
+                                     hipStream_t stream);
+
 /* Measurement aid: the next sink_attn_fwd or sink_attn_bwd made on this host
  * thread records `start` just before and `stop` just after its main kernel
  * (forward: the attention tile loop, or the split-KV kernel for short query
- * groups; backward: the dQ/dK/dV tile loop), on its stream, and then
- * disarms. Pass NULL, NULL to disarm. The events belong to the caller. */
+ * groups; backward: the dK/dV tile loop), on its stream, and then disarms.
+ * sink_attn_fwd_paged counts as a forward. Pass NULL, NULL to disarm. The
+ * events belong to the caller. */
 sink_attn_status sink_attn_arm_timing(hipEvent_t start, hipEvent_t stop);
 
 /* Static text for a status code. */

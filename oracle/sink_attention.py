@@ -28,7 +28,9 @@ Sources (pages; each function below cites the passage it follows):
   decode example.
 * "hf-attention-normalizers 0.1.0 (project description)" -- Important
   Limitations: the softmax1 kernel treats the extra denominator term as a
-  virtual logit-0 / value-0 sink and recomputes probabilities in backward.
+  virtual logit-0 / value-0 sink and recomputes probabilities in backward;
+  Differentiable Paged Attention: the paged path reads K/V pages through a
+  block table (the CANN page gives the page layout and the table).
 
 Readings where the pages are silent (each is also listed in the design doc):
 
@@ -438,6 +440,23 @@ def decode_items(cu_q, cu_k, tile_k, chunk_keys, causal, win_left, win_right):
                     split += 1
         per_seq.append((first, len(items) - first))
     return items, per_seq
+
+
+def gather_paged(cache, block_table, seqused, block_size):
+    """Keys (or values) of a paged cache as packed rows. "CANN ops-transformer:
+    flash_attn", Paged Attention parameter group and the PA_BBND k/v layout
+    (num_blocks, block_size, KV_N, D): row r of sequence b is slot
+    r % block_size of page block_table[b, r // block_size], for r <
+    seqused[b]. Returns (rows [sum(seqused), ...], cu_seqlens [B+1] int32)."""
+    parts, cu = [], [0]
+    for b, used in enumerate(np.asarray(seqused, dtype=np.int64)):
+        pages = np.asarray(block_table[b][:(used + block_size - 1) // block_size])
+        rows = np.asarray(cache)[pages].reshape((-1,) + np.asarray(cache).shape[2:])
+        parts.append(rows[:used])
+        cu.append(cu[-1] + int(used))
+    shape = (0,) + np.asarray(cache).shape[2:]
+    packed = np.concatenate(parts, axis=0) if parts else np.zeros(shape, np.asarray(cache).dtype)
+    return packed, np.asarray(cu, dtype=np.int32)
 
 
 def count_kept_pairs(cu_q, cu_k, causal, win_left, win_right):

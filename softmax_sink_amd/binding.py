@@ -2,11 +2,12 @@
 
 Argument marshalling only: every step of the computation runs in the
 library's HIP kernels; torch provides device memory and the stream. The
-functions ``sink_attn_metadata``, ``sink_attn_fwd``, ``sink_attn_bwd`` and
+functions ``sink_attn_metadata``, ``sink_attn_fwd``, ``sink_attn_bwd``,
+``sink_attn_metadata_paged``, ``sink_attn_fwd_paged`` and
 ``sink_attn_arm_timing`` mirror the C entry points one to one. ``Plan``,
-``forward``, ``backward``, ``SinkAttnFunction`` and
-``learnable_sink_attn_varlen`` are conveniences that allocate outputs and
-workspace with torch and call them.
+``PagedPlan``, ``forward``, ``forward_paged``, ``backward``,
+``SinkAttnFunction`` and ``learnable_sink_attn_varlen`` are conveniences that
+allocate outputs and workspace with torch and call them.
 
 If the library has not been built the first call raises: there is no other
 path.
@@ -37,6 +38,10 @@ class Problem(ctypes.Structure):
         "causal", "win_left", "win_right", "dtype")]
 
 
+class PagedKV(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("block_size", "max_blocks_per_seq", "num_blocks")]
+
+
 _lib = None
 
 
@@ -61,6 +66,14 @@ def lib():
                                     vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp,
                                     ctypes.c_int64, vp]
         L.sink_attn_bwd.restype = ctypes.c_int
+        L.sink_attn_metadata_paged.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(PagedKV),
+                                               i32p, i32p, i32p, i32p, ctypes.c_int64, i64p,
+                                               i64p]
+        L.sink_attn_metadata_paged.restype = ctypes.c_int
+        L.sink_attn_fwd_paged.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(PagedKV), i32p,
+                                          vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp,
+                                          vp, vp, ctypes.c_int64, vp]
+        L.sink_attn_fwd_paged.restype = ctypes.c_int
         L.sink_attn_arm_timing.argtypes = [vp, vp]
         L.sink_attn_arm_timing.restype = ctypes.c_int
         L.sink_attn_status_string.argtypes = [ctypes.c_int]
@@ -123,6 +136,36 @@ def sink_attn_metadata(problem, cu_seqlens_q_host, cu_seqlens_k_host):
     return meta, fws.value, bws.value
 
 
+def make_problem_paged(cu_q, seqused_kv, num_heads_q, num_heads_k, head_dim, causal,
+                       win_left=-1, win_right=-1, dtype=BF16):
+    """Problem struct for a paged forward: key lengths from seqused_kv."""
+    used = np.asarray(seqused_kv, dtype=np.int64)
+    return make_problem(cu_q, np.concatenate([[0], np.cumsum(used)]), num_heads_q,
+                        num_heads_k, head_dim, causal, win_left, win_right, dtype)
+
+
+def sink_attn_metadata_paged(problem, kv, cu_seqlens_q_host, seqused_kv_host,
+                             block_table_host):
+    """-> (meta int32 array, fwd_workspace_bytes)."""
+    L = lib()
+    cq = np.ascontiguousarray(cu_seqlens_q_host, dtype=np.int32)
+    su = np.ascontiguousarray(seqused_kv_host, dtype=np.int32)
+    bt = np.ascontiguousarray(block_table_host, dtype=np.int32)
+    words, fws = ctypes.c_int64(), ctypes.c_int64()
+    st = L.sink_attn_metadata_paged(ctypes.byref(problem), ctypes.byref(kv), _i32p(cq),
+                                    _i32p(su), _i32p(bt), None, 0, ctypes.byref(words),
+                                    ctypes.byref(fws))
+    if st != OK:
+        raise SinkAttnError(st, "sink_attn_metadata_paged")
+    meta = np.zeros(words.value, dtype=np.int32)
+    st = L.sink_attn_metadata_paged(ctypes.byref(problem), ctypes.byref(kv), _i32p(cq),
+                                    _i32p(su), _i32p(bt), _i32p(meta), words.value,
+                                    ctypes.byref(words), ctypes.byref(fws))
+    if st != OK:
+        raise SinkAttnError(st, "sink_attn_metadata_paged")
+    return meta, fws.value
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -139,6 +182,19 @@ def sink_attn_fwd(problem, meta_host, meta_dev, q, k, v, cu_q, cu_k, sinks, scal
                              _ptr(workspace), int(workspace_bytes), _stream(stream))
     if check and st != OK:
         raise SinkAttnError(st, "sink_attn_fwd")
+    return st
+
+
+def sink_attn_fwd_paged(problem, kv, meta_host, meta_dev, q, k_cache, v_cache, block_table,
+                        cu_q, seqused_kv, sinks, scale, out, lse, workspace=None,
+                        workspace_bytes=0, stream=None, check=True):
+    st = lib().sink_attn_fwd_paged(ctypes.byref(problem), ctypes.byref(kv), _i32p(meta_host),
+                                   _ptr(meta_dev), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                   _ptr(block_table), _ptr(cu_q), _ptr(seqused_kv),
+                                   _ptr(sinks), float(scale), _ptr(out), _ptr(lse),
+                                   _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if check and st != OK:
+        raise SinkAttnError(st, "sink_attn_fwd_paged")
     return st
 
 
@@ -195,6 +251,29 @@ class Plan:
         return int(self.meta[14])
 
 
+class PagedPlan:
+    """Metadata for a paged forward over one batch (host block table and
+    key lengths); the device copies are made here."""
+
+    def __init__(self, cu_seqlens_q, seqused_kv, block_table, block_size, num_blocks,
+                 num_heads_q, num_heads_k, head_dim, causal, window=(-1, -1),
+                 device="cuda"):
+        import torch
+        self.cu_q_host = np.asarray(cu_seqlens_q, dtype=np.int32)
+        self.seqused_host = np.asarray(seqused_kv, dtype=np.int32)
+        self.block_table_host = np.ascontiguousarray(block_table, dtype=np.int32)
+        self.kv = PagedKV(int(block_size), int(self.block_table_host.shape[1]), int(num_blocks))
+        self.problem = make_problem_paged(self.cu_q_host, self.seqused_host, num_heads_q,
+                                          num_heads_k, head_dim, causal, window[0],
+                                          window[1], BF16)
+        self.meta, self.fwd_ws_bytes = sink_attn_metadata_paged(
+            self.problem, self.kv, self.cu_q_host, self.seqused_host, self.block_table_host)
+        self.meta_dev = torch.from_numpy(self.meta).to(device)
+        self.cu_q = torch.from_numpy(self.cu_q_host).to(device)
+        self.seqused = torch.from_numpy(self.seqused_host).to(device)
+        self.block_table = torch.from_numpy(self.block_table_host).to(device)
+
+
 def _workspace(nbytes, device):
     import torch
     if nbytes == 0:
@@ -211,6 +290,20 @@ def forward(plan, q, k, v, sinks, scale):
     ws = _workspace(plan.fwd_ws_bytes, q.device)
     sink_attn_fwd(plan.problem, plan.meta, plan.meta_dev, q, k, v, plan.cu_q, plan.cu_k,
                   sinks, scale, out, lse, ws, plan.fwd_ws_bytes)
+    return out, lse
+
+
+def forward_paged(plan, q, k_cache, v_cache, sinks, scale):
+    """Paged forward -> out, lse (k_cache, v_cache: [num_blocks, block_size,
+    Hk, D] bf16)."""
+    import torch
+    out = torch.empty_like(q)
+    lse = torch.empty(plan.problem.num_heads_q, plan.problem.total_q,
+                      dtype=torch.float32, device=q.device)
+    ws = _workspace(plan.fwd_ws_bytes, q.device)
+    sink_attn_fwd_paged(plan.problem, plan.kv, plan.meta, plan.meta_dev, q, k_cache, v_cache,
+                        plan.block_table, plan.cu_q, plan.seqused, sinks, scale, out, lse,
+                        ws, plan.fwd_ws_bytes)
     return out, lse
 
 

@@ -2,6 +2,7 @@
 // dispatch. Declarations and the contract are in include/sink_attn.h.
 #include <cmath>
 #include <cstdint>
+#include <vector>
 
 #include "sink_attn_internal.h"
 
@@ -28,12 +29,44 @@ int64_t header_i64(const int32_t* h, int lo, int hi) {
 
 sink_attn_status common_checks(const sink_attn_problem* p,
                                const int32_t* meta_host,
-                               const int32_t* meta_dev, float scale) {
+                               const int32_t* meta_dev, float scale,
+                               const sink_attn_paged_kv* kv = nullptr) {
   sink_attn_status st = validate_problem(p);
   if (st != SINK_ATTN_OK) return st;
   if (!meta_host || !meta_dev) return SINK_ATTN_E_INVALID;
   if (!std::isfinite(scale) || !(scale > 0.f)) return SINK_ATTN_E_INVALID;
-  return check_header(*p, meta_host);
+  return check_header(*p, meta_host, kv);
+}
+
+FwdArgs fwd_args(const sink_attn_problem* p, const void* q, const void* k,
+                 const void* v, const int32_t* cu_q, const int32_t* cu_k,
+                 const float* sinks, float scale, void* out, float* lse) {
+  FwdArgs a{};
+  a.q = q; a.k = k; a.v = v;
+  a.cu_q = cu_q; a.cu_k = cu_k;
+  a.sinks = sinks;
+  a.out = out; a.lse = lse;
+  a.batch = p->batch; a.hq = p->num_heads_q; a.hk = p->num_heads_k;
+  a.group = p->num_heads_q / p->num_heads_k;
+  a.causal = p->causal; a.win_left = p->win_left; a.win_right = p->win_right;
+  a.total_q = p->total_q; a.total_k = p->total_k;
+  a.scale = scale;
+  return a;
+}
+
+// Split-KV items, per-sequence table and partials workspace of a decode-mode
+// table.
+void decode_args(FwdArgs& a, const sink_attn_problem* p, const int32_t* meta_host,
+                 const int32_t* meta_dev, void* workspace) {
+  const FwdWorkspace w = fwd_workspace_layout(meta_host[kDecRows], p->head_dim,
+                                              p->dtype, kModeDecode);
+  char* base = static_cast<char*>(workspace);
+  a.items = meta_dev + meta_host[kDecOff];
+  a.n_items = meta_host[kNDec];
+  a.dec_seq = meta_dev + meta_host[kDecSeqOff];
+  a.ws_o = reinterpret_cast<float*>(base + w.o_off);
+  a.ws_m = reinterpret_cast<float*>(base + w.m_off);
+  a.ws_l = reinterpret_cast<float*>(base + w.l_off);
 }
 
 }  // namespace
@@ -55,9 +88,36 @@ sink_attn_status sink_attn_metadata(const sink_attn_problem* p,
   st = validate_cu_seqlens(*p, cu_seqlens_q_host, cu_seqlens_k_host);
   if (st != SINK_ATTN_OK) return st;
   if (meta_host && meta_capacity_words < 0) return SINK_ATTN_E_INVALID;
-  return build_metadata(*p, cu_seqlens_q_host, cu_seqlens_k_host, meta_host,
+  return build_metadata(*p, cu_seqlens_q_host, cu_seqlens_k_host, nullptr, meta_host,
                         meta_capacity_words, meta_words, fwd_workspace_bytes,
                         bwd_workspace_bytes);
+}
+
+sink_attn_status sink_attn_metadata_paged(const sink_attn_problem* p,
+                                          const sink_attn_paged_kv* kv,
+                                          const int32_t* cu_seqlens_q_host,
+                                          const int32_t* seqused_kv_host,
+                                          const int32_t* block_table_host,
+                                          int32_t* meta_host,
+                                          int64_t meta_capacity_words,
+                                          int64_t* meta_words,
+                                          int64_t* fwd_workspace_bytes) {
+  sink_attn_status st = validate_problem(p);
+  if (st != SINK_ATTN_OK) return st;
+  if (!meta_words || !fwd_workspace_bytes) return SINK_ATTN_E_INVALID;
+  std::vector<int32_t> cu_k(static_cast<size_t>(p->batch) + 1);
+  st = validate_paged(*p, kv, seqused_kv_host, block_table_host, cu_k.data());
+  if (st != SINK_ATTN_OK) return st;
+  st = validate_cu_seqlens(*p, cu_seqlens_q_host, cu_k.data());
+  if (st != SINK_ATTN_OK) return st;
+  if (p->dtype != SINK_ATTN_BF16 ||
+      static_cast<int64_t>(p->max_seqlen_q) * (p->num_heads_q / p->num_heads_k) > kDecMaxRows)
+    return SINK_ATTN_E_UNSUPPORTED;
+  if (meta_host && meta_capacity_words < 0) return SINK_ATTN_E_INVALID;
+  const PagedInfo info{*kv, block_table_host};
+  int64_t bwd_bytes = 0;
+  return build_metadata(*p, cu_seqlens_q_host, cu_k.data(), &info, meta_host,
+                        meta_capacity_words, meta_words, fwd_workspace_bytes, &bwd_bytes);
 }
 
 sink_attn_status sink_attn_fwd(const sink_attn_problem* p,
@@ -81,36 +141,59 @@ sink_attn_status sink_attn_fwd(const sink_attn_problem* p,
   if (need > 0 && (!workspace || !aligned16(workspace))) return SINK_ATTN_E_INVALID;
 
   const int mode = meta_host[kMode];
-  FwdArgs a{};
-  a.q = q; a.k = k; a.v = v;
-  a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
-  a.sinks = sink_logits;
-  a.out = out; a.lse = lse;
-  a.batch = p->batch; a.hq = p->num_heads_q; a.hk = p->num_heads_k;
-  a.group = p->num_heads_q / p->num_heads_k;
-  a.causal = p->causal; a.win_left = p->win_left; a.win_right = p->win_right;
-  a.total_q = p->total_q; a.total_k = p->total_k;
-  a.scale = scale;
+  FwdArgs a = fwd_args(p, q, k, v, cu_seqlens_q, cu_seqlens_k, sink_logits, scale, out, lse);
   const TimingHook t = take_timing();
   hipError_t e;
   if (p->dtype == SINK_ATTN_FP32) {
     e = launch_fwd_f32(a, p->head_dim, stream, t);
   } else if (mode == kModeDecode) {
-    const FwdWorkspace w = fwd_workspace_layout(meta_host[kDecRows], p->head_dim,
-                                                p->dtype, mode);
-    char* base = static_cast<char*>(workspace);
-    a.items = meta_dev + meta_host[kDecOff];
-    a.n_items = meta_host[kNDec];
-    a.dec_seq = meta_dev + meta_host[kDecSeqOff];
-    a.ws_o = reinterpret_cast<float*>(base + w.o_off);
-    a.ws_m = reinterpret_cast<float*>(base + w.m_off);
-    a.ws_l = reinterpret_cast<float*>(base + w.l_off);
+    decode_args(a, p, meta_host, meta_dev, workspace);
     e = launch_fwd_bf16(a, p->head_dim, mode, stream, t);
   } else {
     a.items = meta_dev + meta_host[kFwdOff];
     a.n_items = meta_host[kNFwd];
     e = launch_fwd_bf16(a, p->head_dim, mode, stream, t);
   }
+  return e == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_E_HIP;
+}
+
+sink_attn_status sink_attn_fwd_paged(const sink_attn_problem* p,
+                                     const sink_attn_paged_kv* kv,
+                                     const int32_t* meta_host,
+                                     const int32_t* meta_dev, const void* q,
+                                     const void* k_cache, const void* v_cache,
+                                     const int32_t* block_table,
+                                     const int32_t* cu_seqlens_q,
+                                     const int32_t* seqused_kv,
+                                     const float* sink_logits, float scale,
+                                     void* out, float* lse, void* workspace,
+                                     int64_t workspace_bytes,
+                                     hipStream_t stream) {
+  if (!kv) return SINK_ATTN_E_INVALID;
+  sink_attn_status st = common_checks(p, meta_host, meta_dev, scale, kv);
+  if (st != SINK_ATTN_OK) return st;
+  if (!q || !k_cache || !v_cache || !block_table || !out || !lse || !cu_seqlens_q ||
+      !seqused_kv)
+    return SINK_ATTN_E_INVALID;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      !aligned16(lse) || !aligned16(block_table))
+    return SINK_ATTN_E_INVALID;
+  const int64_t need = header_i64(meta_host, kFwdWsLo, kFwdWsHi);
+  if (workspace_bytes < need) return SINK_ATTN_E_BUFFER_TOO_SMALL;
+  if (need > 0 && (!workspace || !aligned16(workspace))) return SINK_ATTN_E_INVALID;
+  if (meta_host[kMode] != kModeDecode) return SINK_ATTN_E_UNSUPPORTED;
+
+  FwdArgs a = fwd_args(p, q, k_cache, v_cache, cu_seqlens_q, nullptr, sink_logits, scale,
+                       out, lse);
+  decode_args(a, p, meta_host, meta_dev, workspace);
+  a.block_table = block_table;
+  a.seqused_k = seqused_kv;
+  a.page_size = kv->block_size;
+  a.page_cols = kv->max_blocks_per_seq;
+  a.page_magic = static_cast<uint32_t>(((uint64_t(1) << 32) + kv->block_size - 1) /
+                                       static_cast<uint64_t>(kv->block_size));
+  const TimingHook t = take_timing();
+  const hipError_t e = launch_fwd_bf16(a, p->head_dim, kModeDecode, stream, t);
   return e == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_E_HIP;
 }
 

@@ -203,9 +203,13 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdArgs a) {
 // Split-KV forward for short query groups.
 // Wave w: query block qb = w & 1 (rows 32qb..32qb+31 of the group), key half
 // kh = w >> 1 (keys 32kh..32kh+31 of each 64-key tile). Group row r = g*Lq+i
-// is query row i of q-head hk*G + g.
+// is query row i of q-head hk*G + g. PAGED: keys and values come from paged
+// caches through the block table (only the tile addresses change).
 // ---------------------------------------------------------------------------
-template <int D>
+constexpr int kMaxItemPages = 132;  // pages a kDecChunk-key item can touch (block size >= 16)
+static_assert(kMaxItemPages >= 1 + (kDecChunk + 14) / 16, "page list too short");
+
+template <int D, bool PAGED>
 __global__ __launch_bounds__(256, 2) void fwd_split_kernel(FwdArgs a) {
   constexpr int BN = kDecBN;
   constexpr int NT = D / 16;
@@ -214,13 +218,16 @@ __global__ __launch_bounds__(256, 2) void fwd_split_kernel(FwdArgs a) {
   // two buffers as two objects (see fwd_prefill_kernel)
   __shared__ __attribute__((aligned(16))) char lds0[2 * TILE];
   __shared__ __attribute__((aligned(16))) char lds1[2 * TILE];
+  __shared__ int pages[PAGED ? kMaxItemPages : 1];
 
   const int item = blockIdx.x / a.hk;
   const int hk = blockIdx.x % a.hk;
   const int* it = a.items + item * kItemWords;
   const int b = it[0], k_lo = it[2], k_hi = it[3], row_base = it[4];
   const int q0 = a.cu_q[b], lq = a.cu_q[b + 1] - q0;
-  const int k0 = a.cu_k[b], lk = a.cu_k[b + 1] - k0;
+  int k0 = 0, lk;
+  if constexpr (PAGED) lk = a.seqused_k[b];
+  else { k0 = a.cu_k[b]; lk = a.cu_k[b + 1] - k0; }
   const int G = a.group;
   const int rows = lq * G;
 
@@ -254,13 +261,33 @@ __global__ __launch_bounds__(256, 2) void fwd_split_kernel(FwdArgs a) {
   for (int n = 0; n < NB; ++n) o[n] = f32x16{};
 
   const int nt = (k_hi - k_lo + BN - 1) / BN;
-  TileDma<D> kl, vl;
+  TileDma<D> kl;
+  PagedTileDma<D> pl;
   kl.init();
-  vl.init();
-  if (nt > 0) {
-    kl.load(kp, kstride, k_lo, k_hi, lds0);
-    vl.load(vp, kstride, k_lo, k_hi, lds0 + TILE);
+  pl.init();
+  int off0 = 0;
+  if constexpr (PAGED) {
+    // block-table entries of the pages holding keys [k_lo, k_hi)
+    const int p0 = k_lo / a.page_size;
+    off0 = k_lo - p0 * a.page_size;
+    const int np = (off0 + k_hi - k_lo + a.page_size - 1) / a.page_size;
+    const int* bt = a.block_table + (int64_t)b * a.page_cols + p0;
+    for (int t = threadIdx.x; t < np; t += 256) pages[t] = bt[t];
+    __syncthreads();
   }
+  // K and V rows [row0, row0 + BN) of the item into one LDS buffer
+  auto load_kv = [&](int row0, char* dst) __attribute__((always_inline)) {
+    if constexpr (PAGED) {
+      pl.load(static_cast<const bf16*>(a.k), (int64_t)hk * D, kstride, pages, off0, k_lo, row0,
+              k_hi - 1, a.page_size, a.page_magic, dst);
+      pl.load(static_cast<const bf16*>(a.v), (int64_t)hk * D, kstride, pages, off0, k_lo, row0,
+              k_hi - 1, a.page_size, a.page_magic, dst + TILE);
+    } else {
+      kl.load(kp, kstride, row0, k_hi, dst);
+      kl.load(vp, kstride, row0, k_hi, dst + TILE);
+    }
+  };
+  if (nt > 0) load_kv(k_lo, lds0);
   wait_vmem();
   __syncthreads();
 
@@ -268,10 +295,7 @@ __global__ __launch_bounds__(256, 2) void fwd_split_kernel(FwdArgs a) {
     constexpr int cur = decltype(cur_c)::value;
     const bool more = n_t + 1 < nt;
     const int base = k_lo + n_t * BN;
-    if (more) {
-      kl.load(kp, kstride, base + BN, k_hi, cur == 0 ? lds1 : lds0);
-      vl.load(vp, kstride, base + BN, k_hi, (cur == 0 ? lds1 : lds0) + TILE);
-    }
+    if (more) load_kv(base + BN, cur == 0 ? lds1 : lds0);
     const char* kt_lds = cur == 0 ? lds0 : lds1;
     const char* vt_lds = (cur == 0 ? lds0 : lds1) + TILE;
     f32x16 s = f32x16{};
@@ -411,8 +435,12 @@ template <int D>
 hipError_t launch_fwd_d(const FwdArgs& a, int mode, hipStream_t s, const TimingHook& th) {
   if (mode == kModeDecode) {
     if (th.start) hipEventRecord(th.start, s);
-    if (a.n_items > 0)
-      hipLaunchKernelGGL(fwd_split_kernel<D>, dim3(a.n_items * a.hk), dim3(256), 0, s, a);
+    if (a.n_items > 0) {
+      if (a.block_table)
+        hipLaunchKernelGGL((fwd_split_kernel<D, true>), dim3(a.n_items * a.hk), dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((fwd_split_kernel<D, false>), dim3(a.n_items * a.hk), dim3(256), 0, s, a);
+    }
     if (th.stop) hipEventRecord(th.stop, s);
     const int rows = a.total_q * a.hq;
     hipLaunchKernelGGL(fwd_combine_kernel<D>, dim3((rows + 3) / 4), dim3(256), 0, s, a);

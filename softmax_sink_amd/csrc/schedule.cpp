@@ -167,9 +167,32 @@ sink_attn_status validate_cu_seqlens(const sink_attn_problem& p,
   return SINK_ATTN_OK;
 }
 
+sink_attn_status validate_paged(const sink_attn_problem& p,
+                                const sink_attn_paged_kv* kv,
+                                const int32_t* seqused_kv,
+                                const int32_t* block_table, int32_t* cu_k_out) {
+  if (!kv || !seqused_kv || !block_table || !cu_k_out) return SINK_ATTN_E_INVALID;
+  const int64_t bs = kv->block_size;
+  if (bs < 16 || bs > 1024 || bs % 16 != 0) return SINK_ATTN_E_INVALID;
+  if (kv->max_blocks_per_seq <= 0 || kv->num_blocks <= 0) return SINK_ATTN_E_INVALID;
+  int64_t acc = 0;
+  cu_k_out[0] = 0;
+  for (int b = 0; b < p.batch; ++b) {
+    const int64_t used = seqused_kv[b];
+    if (used < 0 || used > bs * kv->max_blocks_per_seq) return SINK_ATTN_E_INVALID;
+    const int32_t* row = block_table + static_cast<int64_t>(b) * kv->max_blocks_per_seq;
+    for (int64_t pg = 0; pg < (used + bs - 1) / bs; ++pg)
+      if (row[pg] < 0 || row[pg] >= kv->num_blocks) return SINK_ATTN_E_INVALID;
+    acc += used;
+    if (acc > std::numeric_limits<int32_t>::max()) return SINK_ATTN_E_INVALID;
+    cu_k_out[b + 1] = static_cast<int32_t>(acc);
+  }
+  return SINK_ATTN_OK;
+}
+
 sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
-                                const int32_t* cu_k, int32_t* out,
-                                int64_t capacity, int64_t* words,
+                                const int32_t* cu_k, const PagedInfo* paged,
+                                int32_t* out, int64_t capacity, int64_t* words,
                                 int64_t* fwd_ws, int64_t* bwd_ws) {
   const int B = p.batch;
   const int G = p.num_heads_q / p.num_heads_k;
@@ -301,6 +324,20 @@ sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
       fnv1a(cu_k, B + 1, fnv1a(cu_q, B + 1, 2166136261u)));
   h[kMetaWords] = static_cast<int32_t>(total);
   h[kBwdPreBlocks] = static_cast<int32_t>(pre_blocks);
+  if (paged) {
+    const int64_t bs = paged->kv.block_size;
+    uint32_t hash = 2166136261u;
+    for (int b = 0; b < B; ++b) {
+      const int64_t used = cu_k[b + 1] - cu_k[b];
+      hash = fnv1a(paged->block_table + static_cast<int64_t>(b) * paged->kv.max_blocks_per_seq,
+                   (used + bs - 1) / bs, hash);
+    }
+    h[kPaged] = 1;
+    h[kPageSize] = paged->kv.block_size;
+    h[kPageMaxBlocks] = paged->kv.max_blocks_per_seq;
+    h[kPageNumBlocks] = paged->kv.num_blocks;
+    h[kPageHash] = static_cast<int32_t>(hash);
+  }
   int32_t* w = out + fwd_off;
   for (const Item& it : fwd) { std::memcpy(w, it.w, sizeof(it.w)); w += kItemWords; }
   for (const Item& it : bwd) { std::memcpy(w, it.w, sizeof(it.w)); w += kItemWords; }
@@ -309,7 +346,8 @@ sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
   return SINK_ATTN_OK;
 }
 
-sink_attn_status check_header(const sink_attn_problem& p, const int32_t* h) {
+sink_attn_status check_header(const sink_attn_problem& p, const int32_t* h,
+                              const sink_attn_paged_kv* kv) {
   if (!h) return SINK_ATTN_E_INVALID;
   if (h[kMagic] != kMagicValue || h[kVersion] != SINK_ATTN_ABI_VERSION)
     return SINK_ATTN_E_META_MISMATCH;
@@ -322,6 +360,10 @@ sink_attn_status check_header(const sink_attn_problem& p, const int32_t* h) {
     return SINK_ATTN_E_META_MISMATCH;
   if (h[kWordFwdBM] != kFwdBM || h[kWordFwdBN] != kFwdBN || h[kWordBwdBM] != kBwdBM ||
       h[kWordBwdBN] != kBwdBN || h[kWordDecBN] != kDecBN || h[kWordDecChunk] != kDecChunk)
+    return SINK_ATTN_E_META_MISMATCH;
+  if (h[kPaged] != (kv ? 1 : 0)) return SINK_ATTN_E_META_MISMATCH;
+  if (kv && (h[kPageSize] != kv->block_size || h[kPageMaxBlocks] != kv->max_blocks_per_seq ||
+             h[kPageNumBlocks] != kv->num_blocks))
     return SINK_ATTN_E_META_MISMATCH;
   return SINK_ATTN_OK;
 }

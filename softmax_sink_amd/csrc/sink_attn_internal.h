@@ -19,6 +19,7 @@ enum MetaWord : int {
   kNFwd, kFwdOff, kNBwd, kBwdOff, kNDec, kDecOff, kDecSeqOff, kDecRows,
   kFwdWsLo, kFwdWsHi, kBwdWsLo, kBwdWsHi, kCuHash, kMetaWords,
   kBwdPreBlocks,
+  kPaged, kPageSize, kPageMaxBlocks, kPageNumBlocks, kPageHash,
   kHeaderWords = 48
 };
 
@@ -57,16 +58,32 @@ FwdWorkspace fwd_workspace_layout(int64_t dec_rows, int head_dim, int dtype,
 BwdWorkspace bwd_workspace_layout(int64_t total_q, int hq, int head_dim,
                                   int dtype, int64_t pre_blocks);
 
+// Paged K/V as seen by the schedule builder: the sizes and the host block
+// table (hashed into the header).
+struct PagedInfo {
+  sink_attn_paged_kv kv;
+  const int32_t* block_table;
+};
+
 // Host checks and the schedule builder (schedule.cpp).
 sink_attn_status validate_problem(const sink_attn_problem* p);
 sink_attn_status validate_cu_seqlens(const sink_attn_problem& p,
                                      const int32_t* cu_q, const int32_t* cu_k);
+// Checks a paged layout against the problem and the host tables, and
+// writes the key-length prefix sums (batch + 1 words) into cu_k_out.
+sink_attn_status validate_paged(const sink_attn_problem& p,
+                                const sink_attn_paged_kv* kv,
+                                const int32_t* seqused_kv,
+                                const int32_t* block_table, int32_t* cu_k_out);
 // Builds the table; writes it when `out` is non-null and capacity allows.
+// `paged` is null for contiguous keys and values.
 sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
-                                const int32_t* cu_k, int32_t* out,
-                                int64_t capacity, int64_t* words,
+                                const int32_t* cu_k, const PagedInfo* paged,
+                                int32_t* out, int64_t capacity, int64_t* words,
                                 int64_t* fwd_ws, int64_t* bwd_ws);
-sink_attn_status check_header(const sink_attn_problem& p, const int32_t* meta);
+// Header against the call; `kv` is null for the contiguous calls.
+sink_attn_status check_header(const sink_attn_problem& p, const int32_t* meta,
+                              const sink_attn_paged_kv* kv);
 
 // ---------------------------------------------------------------------------
 // Kernel arguments and launchers (kernels_*.hip).
@@ -85,6 +102,11 @@ struct FwdArgs {
   float* ws_o;              // decode partials
   float* ws_m;
   float* ws_l;
+  // paged K/V (split-KV path only); k, v are then the caches
+  const int32_t* block_table;
+  const int32_t* seqused_k;
+  int page_size, page_cols;  // block_size, max_blocks_per_seq
+  uint32_t page_magic;       // ceil(2^32 / block_size)
   int n_items;
   int batch, hq, hk, group, causal, win_left, win_right;
   int total_q, total_k;

@@ -94,6 +94,53 @@ struct TileDma {
   }
 };
 
+// The same [64 x D] tile transfer for keys or values that live in a paged
+// cache ([num_blocks, block_size, Hk, D]): row r of the sequence is slot
+// (r - k_lo + off0) % block_size of the page pages[(r - k_lo + off0) /
+// block_size], where `pages` is an LDS copy of the block-table entries of
+// the work item, starting with the page that holds its first key k_lo at
+// slot off0. Rows past `row_last` fetch row_last. Each lane computes its own
+// 64-bit row address, so the FLAT form global_load_lds_dwordx4 is used, again
+// from inline assembly (no outputs; clobbers M0 and memory). The division by
+// block_size is a multiply-high with magic = ceil(2^32 / block_size), exact
+// here because the numerator stays below 2^12.
+template <int D, int THREADS = 256>
+struct PagedTileDma {
+  static constexpr int kPer = 64 * D / 8 / THREADS;
+  static constexpr int kRowsPerPass = THREADS / (D / 8);
+  static_assert(kRowsPerPass % 16 == 0, "a pass must keep the row swizzle");
+  int lrow, lcol, wave_off;
+  __device__ __forceinline__ void init() {
+    lrow = threadIdx.x / (D / 8);
+    lcol = (((threadIdx.x % (D / 8)) ^ swz<D>(lrow)) * 16);
+    wave_off = __builtin_amdgcn_readfirstlane((threadIdx.x / 64) * 1024);
+  }
+  __device__ __forceinline__ void load(const bf16* cache, int64_t head_off, int64_t row_stride,
+                                       const int* pages, int off0, int k_lo, int row0,
+                                       int row_last, int block_size, uint32_t magic,
+                                       char* tile) const {
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(tile + wave_off));
+#pragma unroll
+    for (int s = 0; s < kPer; ++s) {
+      const int row = min(row0 + lrow + s * kRowsPerPass, row_last);
+      const uint32_t num = (uint32_t)(row - k_lo + off0);
+      const uint32_t pi = __umulhi(num, magic);
+      const int slot = (int)(num - pi * (uint32_t)block_size);
+      const int64_t phys = pages[pi];
+      const char* src = reinterpret_cast<const char*>(
+                            cache + (phys * block_size + slot) * row_stride + head_off) + lcol;
+      asm volatile(
+          "s_mov_b32 m0, %1\n\t"
+          "s_nop 0\n\t"
+          "global_load_lds_dwordx4 %0, off"
+          :
+          : "v"(src), "s"(lds0 + s * THREADS * 16)
+          : "memory", "m0");
+    }
+  }
+};
+
 // Head index for the j-th slot of the head-fastest block numbering. Blocks
 // are spread over the 8 XCDs round robin (block id mod 8); with this map the
 // q-heads of one kv group -- which read the same K/V -- share an XCD and

@@ -22,7 +22,9 @@ tokens, lengths uniform in [1024, 8192], 32/32 heads, D 128, causal,
 forward + backward), ``gqa_window`` (4 x 8192, 64/8 heads, D 128, causal
 with window (1024, 0), forward + backward) and ``decode_softmax_n`` (64
 sequences, q length uniform in [1, 16], kv length uniform in [512, 32768],
-32/8 heads, D 128, bottom-right causal, n = 0.5).
+32/8 heads, D 128, bottom-right causal, n = 0.5), plus ``decode_paged``:
+the same draw with its keys and values scattered into 16-row pages of a
+paged cache in random page order (``paged_layout``, ``scatter_to_pages``).
 """
 
 import math
@@ -156,6 +158,45 @@ def make_problem(seed, lens_q, lens_k, num_heads_q, num_heads_k, head_dim,
                    np.float32(scale), s, q, k, v, dout, seed)
 
 
+@dataclass
+class PagedLayout:
+    """Where the key rows of each sequence live in a paged cache."""
+    block_size: int
+    block_table: np.ndarray        # int32 [B, max_blocks_per_seq]
+    seqused: np.ndarray            # int32 [B], key rows per sequence
+    num_blocks: int
+
+
+def paged_layout(cu_k, block_size, seed, spare=0):
+    """Sequence b gets ceil(L_b / block_size) distinct pages, taken in order
+    from one random permutation of all num_blocks pages (no page shared);
+    unused table entries are 0. `spare` extra pages stay unused."""
+    lens = np.diff(np.asarray(cu_k, dtype=np.int64))
+    need = (lens + block_size - 1) // block_size
+    num_blocks = int(need.sum()) + int(spare)
+    perm = np.random.default_rng(seed).permutation(num_blocks).astype(np.int32)
+    table = np.zeros((len(lens), max(1, int(need.max()) if len(need) else 1)), np.int32)
+    at = 0
+    for b, n in enumerate(need):
+        table[b, :n] = perm[at:at + n]
+        at += int(n)
+    return PagedLayout(int(block_size), table, lens.astype(np.int32), num_blocks)
+
+
+def scatter_to_pages(x, cu_k, layout):
+    """Packed rows x [Tk, ...] -> cache [num_blocks, block_size, ...] with
+    row r of sequence b in slot r % block_size of page
+    block_table[b, r // block_size]; slots no row maps to are 0."""
+    bs = layout.block_size
+    cache = np.zeros((layout.num_blocks, bs) + x.shape[1:], dtype=x.dtype)
+    for b in range(len(cu_k) - 1):
+        rows = x[int(cu_k[b]):int(cu_k[b + 1])]
+        for pg in range((len(rows) + bs - 1) // bs):
+            chunk = rows[pg * bs:(pg + 1) * bs]
+            cache[layout.block_table[b, pg], :len(chunk)] = chunk
+    return cache
+
+
 def _train_lengths(rng, n=8, total=32768, lo=1024, hi=8192):
     """n lengths uniform in [lo, hi] summing to total: draw n-1, set the last
     to the remainder, redraw all until the last is in range."""
@@ -168,6 +209,8 @@ def _train_lengths(rng, n=8, total=32768, lo=1024, hi=8192):
 
 CONFIG_NAMES = ("softmax1_fp32", "prefill_varlen", "train_varlen",
                 "gqa_window", "decode_softmax_n")
+DECODE_PAGE_ROWS = 16      # block size of the paged decode workload
+DECODE_PAGE_SEED = 55
 
 
 def config(name):
@@ -190,11 +233,14 @@ def config(name):
         lens = np.full(4, 8192)
         return make_problem(4, lens, lens, 64, 8, 128, causal=True,
                             win_left=1024, win_right=0, name=name)
-    if name == "decode_softmax_n":
+    if name in ("decode_softmax_n", "decode_paged"):
         rng = np.random.default_rng(5)
         lq = rng.integers(1, 17, 64)
         lk = rng.integers(512, 32769, 64)
-        return make_problem(5, lq, lk, 32, 8, 128, causal=True,
-                            sinks=np.float32(math.log(0.5)), name=name,
-                            rng=rng)
+        p = make_problem(5, lq, lk, 32, 8, 128, causal=True,
+                         sinks=np.float32(math.log(0.5)), name=name,
+                         rng=rng)
+        if name == "decode_paged":
+            p.meta["paged"] = paged_layout(p.cu_k, DECODE_PAGE_ROWS, DECODE_PAGE_SEED)
+        return p
     raise KeyError(name)

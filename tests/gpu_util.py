@@ -72,3 +72,21 @@ def rel_l2(a, b):
 # tolerances stated for the method: fp32 out/lse max abs 1e-5; bf16 out max
 # abs 1e-2, lse max abs 1e-3, gradients relative L2 2e-2
 TOL = {"fp32": dict(out=1e-5, lse=1e-5, grad=1e-5), "bf16": dict(out=1e-2, lse=1e-3, grad=2e-2)}
+
+
+def sampled_rows_error(p, out, lse, n, seed):
+    """Max abs error of out and lse against the oracle on n random (token,
+    q-head) rows plus the first and last row of every sequence."""
+    rng = np.random.default_rng(seed)
+    rows = [(int(rng.integers(0, p.total_q)), int(rng.integers(0, p.num_heads_q)))
+            for _ in range(n)]
+    for b in range(p.batch):
+        if p.cu_q[b + 1] > p.cu_q[b]:
+            rows.append((int(p.cu_q[b]), b % p.num_heads_q))
+            rows.append((int(p.cu_q[b + 1] - 1), (3 * b) % p.num_heads_q))
+    ref = O.sink_attention_rows(p.as_f32("q"), p.as_f32("k"), p.as_f32("v"), p.cu_q, p.cu_k,
+                                p.sinks.astype(np.float64), float(p.scale), p.causal,
+                                p.win_left, p.win_right, rows)
+    e_out = max(max_abs(out[t, h], r["out"]) for (t, h), r in zip(rows, ref))
+    e_lse = max(max_abs(lse[h, t], r["lse"]) for (t, h), r in zip(rows, ref))
+    return e_out, e_lse

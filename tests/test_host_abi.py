@@ -28,11 +28,12 @@ def test_exports_every_declared_symbol(L):
     text = open(HDR).read()
     names = set(re.findall(r"\b(sink_attn_[a-z_]+)\s*\(", text))
     assert {"sink_attn_metadata", "sink_attn_fwd", "sink_attn_bwd",
+            "sink_attn_metadata_paged", "sink_attn_fwd_paged",
             "sink_attn_status_string", "sink_attn_abi_version",
             "sink_attn_arm_timing"} <= names
     for n in names:
         assert hasattr(L, n), n
-    assert B.abi_version() == 1
+    assert B.abi_version() == 2
     for s in range(6):
         assert isinstance(B.status_string(s), str)
 
@@ -112,7 +113,7 @@ def test_metadata_two_call_protocol_and_sizes(L):
                               ctypes.byref(words), ctypes.byref(fws), ctypes.byref(bws))
     assert st == B.E_BUFFER_TOO_SMALL
     meta, f, b = B.sink_attn_metadata(p, cu, cu)
-    assert meta[0] == 0x4B4E4953 and meta[1] == 1 and len(meta) == words.value
+    assert meta[0] == 0x4B4E4953 and meta[1] == 2 and len(meta) == words.value
     # bwd workspace: D [Hq,Tq] fp32 + per-block dsink partials (no dQ accumulator)
     assert 300 * 8 * 4 <= b < 300 * 8 * 4 + 4096
     assert f == 0       # prefill mode needs no forward scratch
@@ -202,3 +203,102 @@ def test_fwd_bwd_argument_checks():
     assert _fwd(p2, meta2, workspace=None, workspace_bytes=fws2) == B.E_INVALID
     assert B.lib().sink_attn_arm_timing(FAKE, None) == B.E_INVALID
     assert B.lib().sink_attn_arm_timing(None, None) == B.OK
+
+
+# ---------------------------------------------------------------------------
+# paged K/V
+# ---------------------------------------------------------------------------
+W_PAGED = 36   # header words: paged flag, block size, table columns, pages, table hash
+
+
+def _paged_case(bs=16, seed=3, lq=(1, 3, 2), lk=(40, 0, 100), hq=8, hk=2):
+    rng = np.random.default_rng(seed)
+    need = [(n + bs - 1) // bs for n in lk]
+    table = np.zeros((len(lk), max(need) + 1), np.int32)
+    perm = rng.permutation(sum(need) + 3).astype(np.int32)
+    at = 0
+    for b, n in enumerate(need):
+        table[b, :n] = perm[at:at + n]
+        at += n
+    cu_q = np.r_[0, np.cumsum(lq)].astype(np.int32)
+    used = np.asarray(lk, np.int32)
+    kv = B.PagedKV(bs, table.shape[1], len(perm))
+    p = B.make_problem_paged(cu_q, used, hq, hk, 128, True)
+    return p, kv, cu_q, used, table
+
+
+def test_paged_metadata_matches_oracle_schedule():
+    for bs in (16, 48, 1024):
+        p, kv, cu_q, used, table = _paged_case(bs)
+        meta, fws = B.sink_attn_metadata_paged(p, kv, cu_q, used, table)
+        assert fws > 0 and meta[W_MODE] == 1
+        assert meta[W_PAGED:W_PAGED + 4].tolist() == [1, bs, table.shape[1], kv.num_blocks]
+        cu_k = np.r_[0, np.cumsum(used)].astype(np.int32)
+        ditems, per_seq = O.decode_items(cu_q, cu_k, meta[W_DECBN], meta[W_DECCHUNK], True, -1, -1)
+        assert _items(meta, W_NDEC, W_DECOFF, 4) == ditems
+        # the same problem through the contiguous call gives the same schedule
+        meta_c, _, _ = B.sink_attn_metadata(p, cu_q, cu_k)
+        assert meta_c[W_PAGED] == 0
+        n = meta[W_NDEC]
+        assert np.array_equal(meta[meta[W_DECOFF]:meta[W_DECOFF] + 8 * n],
+                              meta_c[meta_c[W_DECOFF]:meta_c[W_DECOFF] + 8 * n])
+
+
+def test_paged_metadata_rejects():
+    p, kv, cu_q, used, table = _paged_case()
+    def status(**kw):
+        args = dict(p=p, kv=kv, cu_q=cu_q, used=used, table=table)
+        args.update(kw)
+        with pytest.raises(B.SinkAttnError) as e:
+            B.sink_attn_metadata_paged(args["p"], args["kv"], args["cu_q"], args["used"],
+                                       args["table"])
+        return e.value.status
+    for bs in (0, 8, 24, 2048):
+        assert status(kv=B.PagedKV(bs, kv.max_blocks_per_seq, kv.num_blocks)) == B.E_INVALID
+    assert status(kv=B.PagedKV(16, kv.max_blocks_per_seq, 0)) == B.E_INVALID
+    bad = table.copy(); bad[2, 0] = kv.num_blocks
+    assert status(table=bad) == B.E_INVALID
+    bad = table.copy(); bad[0, 0] = -1
+    assert status(table=bad) == B.E_INVALID
+    too_long = used.copy(); too_long[2] = 16 * kv.max_blocks_per_seq + 1
+    p2 = B.make_problem_paged(cu_q, too_long, 8, 2, 128, True)
+    assert status(p=p2, used=too_long) == B.E_INVALID
+    wrong_total = B.make_problem_paged(cu_q, used, 8, 2, 128, True)
+    wrong_total.total_k += 1
+    assert status(p=wrong_total) == B.E_INVALID
+    long_q = np.array([0, 40, 41, 42], np.int32)           # 40 rows x 4 heads > 64
+    assert status(p=B.make_problem_paged(long_q, used, 8, 2, 128, True), cu_q=long_q) == \
+        B.E_UNSUPPORTED
+    assert status(p=B.make_problem_paged(cu_q, used, 8, 2, 128, True, dtype=B.FP32)) == \
+        B.E_UNSUPPORTED
+
+
+def test_paged_entries_only_checked_where_used():
+    # table entries past a sequence's last page are never read, so need not be valid
+    p, kv, cu_q, used, table = _paged_case()
+    table[:, -1] = 99999
+    B.sink_attn_metadata_paged(p, kv, cu_q, used, table)
+
+
+def test_paged_fwd_argument_checks():
+    p, kv, cu_q, used, table = _paged_case()
+    meta, fws = B.sink_attn_metadata_paged(p, kv, cu_q, used, table)
+    cu_k = np.r_[0, np.cumsum(used)].astype(np.int32)
+    meta_c, fws_c, bws_c = B.sink_attn_metadata(p, cu_q, cu_k)
+
+    def fwdp(meta_host, kv_=kv, **kw):
+        args = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cu_q=FAKE, used=FAKE, sinks=FAKE,
+                    out=FAKE, lse=FAKE, ws=FAKE, wsb=1 << 40)
+        args.update(kw)
+        a = args
+        return B.sink_attn_fwd_paged(p, kv_, meta_host, FAKE, a["q"], a["k"], a["v"], a["bt"],
+                                     a["cu_q"], a["used"], a["sinks"], 0.1, a["out"],
+                                     a["lse"], a["ws"], a["wsb"], stream=0, check=False)
+    assert fwdp(meta_c) == B.E_META_MISMATCH                  # contiguous table
+    assert fwdp(meta, kv_=B.PagedKV(32, kv.max_blocks_per_seq, kv.num_blocks)) == B.E_META_MISMATCH
+    assert fwdp(meta, bt=None) == B.E_INVALID
+    assert fwdp(meta, used=None) == B.E_INVALID
+    assert fwdp(meta, wsb=fws - 1) == B.E_BUFFER_TOO_SMALL
+    # a paged table is refused by the contiguous calls
+    assert _fwd(p, meta, workspace=FAKE, workspace_bytes=1 << 40) == B.E_META_MISMATCH
+    assert _bwd(p, meta) == B.E_META_MISMATCH

@@ -443,3 +443,39 @@ def test_dsink_only_matches_full_backward():
     full = O.sink_attention_backward(dout, q, k, v, cu, cu, sinks, 0.4, True, 3, 0)[3]
     only = O.sink_attention_dsink(dout, q, k, v, cu, cu, sinks, 0.4, True, 3, 0, block_rows=4)
     np.testing.assert_allclose(only, full, rtol=1e-12, atol=1e-15)
+
+
+def test_gather_paged_hand_example():
+    """CANN page, PA_BBND layout: row r of sequence b is slot r % bs of page
+    block_table[b, r // bs]. Block size 2, four pages whose slot values name
+    (page, slot); sequence 0 uses pages 2 then 0 (3 rows), sequence 1 pages 3
+    then 1 (2 rows): the gathered rows are read off by hand."""
+    cache = np.array([[[0.0], [1.0]], [[10.0], [11.0]], [[20.0], [21.0]], [[30.0], [31.0]]])
+    table = np.array([[2, 0], [3, 1]], np.int32)
+    rows, cu = O.gather_paged(cache, table, [3, 2], 2)
+    assert cu.tolist() == [0, 3, 5]
+    assert rows[:, 0].tolist() == [20.0, 21.0, 0.0, 30.0, 31.0]
+
+
+def test_gather_paged_inverts_a_page_scatter():
+    """Rows written into pages one by one (a loop written here, slot by slot)
+    come back in order, for a random page permutation, block sizes that do
+    and do not divide the lengths, and an empty sequence."""
+    rng = np.random.default_rng(11)
+    for bs in (1, 3, 16):
+        lens = [5, 0, 17, 16]
+        need = [(n + bs - 1) // bs for n in lens]
+        perm = rng.permutation(sum(need) + 2)
+        table = np.zeros((len(lens), max(need)), np.int32)
+        cache = np.full((len(perm), bs, 2), -1.0)
+        at, want = 0, []
+        for b, n in enumerate(lens):
+            table[b, :need[b]] = perm[at:at + need[b]]
+            at += need[b]
+            for r in range(n):
+                val = rng.standard_normal(2)
+                cache[table[b, r // bs], r % bs] = val
+                want.append(val)
+        rows, cu = O.gather_paged(cache, table, lens, bs)
+        assert cu.tolist() == np.concatenate([[0], np.cumsum(lens)]).tolist()
+        assert np.array_equal(rows, np.array(want))
