@@ -121,6 +121,70 @@ def traffic_record(workload, kernel):
     return rec["hbm_bytes_per_launch"]
 
 
+def bench_merge(args):
+    """Context-parallel merge: 4 sink-free bf16 partials of the prefill
+    workload's shape (16 sequences, 16640 tokens, 32 heads, D 128) merged into
+    one bf16 output. HBM-bound: the bytes are the partials and their lse read
+    once, the output and lse written once."""
+    import torch
+    from softmax_sink_amd import binding as B
+    from softmax_sink_amd import workloads as W
+    import oracle as O
+    P, Hq, D = 4, 32, 128
+    Tq = W.config("prefill_varlen").total_q
+    outs, lses, sinks = W.merge_inputs(61, P, Tq, Hq, D)
+    po = torch.from_numpy(outs.view(np.int16)).view(torch.bfloat16).cuda()
+    pl = torch.from_numpy(lses).cuda()
+    sk = torch.from_numpy(sinks).cuda()
+    out = torch.empty(Tq, Hq, D, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(Hq, Tq, dtype=torch.float32, device="cuda")
+    ev = []
+    def step(timed):
+        if timed:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            B.sink_attn_arm_timing(e0, e1)
+            ev.append((e0, e1))
+        B.sink_attn_merge(P, Tq, Hq, D, B.BF16, B.BF16, po, pl, sk, out, lse)
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(args.steps):
+        step(True)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    kms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    nbytes = float(P * Tq * Hq * D * 2 + P * Hq * Tq * 4 + Tq * Hq * D * 2 + Hq * Tq * 4 + Hq * 4)
+    res = {"metric": "context-parallel merge GB/s (sink-free partials -> sink attention)",
+           "value": nbytes / (ms * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic",
+           "config": {"workload": "cp_merge", "parts": P, "total_q": Tq, "heads_q": Hq,
+                      "head_dim": D, "seed": 61},
+           "main_kernel_ms": {"merge": kms},
+           "roofline": {"bound": "hbm", "kernel": "merge_kernel",
+                        "achieved": nbytes / (kms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": nbytes / (kms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                        "traffic": None, "launch_ms": kms, "bytes_per_launch": nbytes}}
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+        rows, t = 0, time.perf_counter()
+        while time.perf_counter() - t < min(args.cpu_seconds, 5.0):
+            a = rows % Tq
+            b = min(Tq, a + 1024)
+            O.merge_partials(W.bf16_bits_to_f32(outs[:, a:b]), lses[:, :, a:b], sinks)
+            rows += b - a
+        dt = time.perf_counter() - t
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        res["cpu_baseline"] = {"value": nbytes * rows / Tq / dt / 1e9, "unit": "GB/s",
+                               "cores": int(threads), "kind": "oracle",
+                               "sample": f"{rows} of {Tq} token rows (all heads), {dt:.1f} s"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -143,6 +207,9 @@ def main():
     from softmax_sink_amd import workloads as W
 
     torch.cuda.set_device(0)
+    if args.workload == "cp_merge":
+        bench_merge(args)
+        return
     if args.calibrate_copy:
         src = torch.empty(args.calibrate_copy, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)

@@ -215,12 +215,40 @@ sink_attn_status sink_attn_fwd_paged(const sink_attn_problem* p,
                                      int64_t workspace_bytes,
                                      hipStream_t stream);
 
+/* Context-parallel merge. "CANN ops-transformer: flash_attn", Note on
+ * softmax_lse: ring attention combines partial results through their lse.
+ * Each of num_parts partials is the attention of the same queries over a
+ * disjoint part of the keys, computed WITHOUT the sink (sink_logits NULL):
+ * its output out_p and its lse_p = ln sum e^S over that part. The merge
+ * returns the attention over the union of the parts with the sink added
+ * exactly once:
+ *   lse = ln(e^{s_h} + sum_p e^{lse_p}),  out = sum_p e^{lse_p - lse} out_p.
+ * Parts with lse_p = -inf (no kept key) contribute nothing. Layouts (device
+ * pointers, contiguous): partial_out [num_parts, total_q, num_heads_q,
+ * head_dim] in part_dtype (16-byte aligned); partial_lse [num_parts,
+ * num_heads_q, total_q] fp32; sink_logits [num_heads_q] fp32 or NULL; out
+ * [total_q, num_heads_q, head_dim] in out_dtype (16-byte aligned); lse
+ * [num_heads_q, total_q] fp32, sink inclusive. Arithmetic is fp32; a bf16
+ * part_dtype adds that rounding of each partial to the result. Enqueues on
+ * `stream`; allocates nothing. Errors: E_INVALID (num_parts outside
+ * [1, 4096], total_q or num_heads_q <= 0, NULL or misaligned pointers),
+ * E_UNSUPPORTED (head_dim not 64 or 128, unknown dtype, more than 2^40
+ * elements), E_HIP. */
+sink_attn_status sink_attn_merge(int32_t num_parts, int32_t total_q,
+                                 int32_t num_heads_q, int32_t head_dim,
+                                 int32_t part_dtype, int32_t out_dtype,
+                                 const void* partial_out,
+                                 const float* partial_lse,
+                                 const float* sink_logits, void* out,
+                                 float* lse, hipStream_t stream);
+
 /* Measurement aid: the next sink_attn_fwd or sink_attn_bwd made on this host
  * thread records `start` just before and `stop` just after its main kernel
  * (forward: the attention tile loop, or the split-KV kernel for short query
  * groups; backward: the dK/dV tile loop), on its stream, and then disarms.
- * sink_attn_fwd_paged counts as a forward. Pass NULL, NULL to disarm. The
- * events belong to the caller. */
+ * sink_attn_fwd_paged counts as a forward, sink_attn_merge records around
+ * its merge kernel. Pass NULL, NULL to disarm. The events belong to the
+ * caller. */
 sink_attn_status sink_attn_arm_timing(hipEvent_t start, hipEvent_t stop);
 
 /* Static text for a status code. */

@@ -442,6 +442,26 @@ def decode_items(cu_q, cu_k, tile_k, chunk_keys, causal, win_left, win_right):
     return items, per_seq
 
 
+def merge_partials(outs, lses, sinks):
+    """Attention over the union of disjoint key parts from the parts' own
+    sink-free results ("CANN ops-transformer: flash_attn", Note on
+    softmax_lse, which ring attention merges by; the sink enters once, as in
+    the Formula section): lse = ln(e^s + sum_p e^{lse_p}) and out =
+    sum_p e^{lse_p - lse} out_p. outs [P, Tq, Hq, D], lses [P, Hq, Tq],
+    sinks [Hq] (-inf: none). Returns (out [Tq, Hq, D], lse [Hq, Tq])."""
+    outs = np.asarray(outs, dtype=np.float64)
+    lses = np.asarray(lses, dtype=np.float64)
+    s = np.asarray(sinks, dtype=np.float64)[None, :, None]          # [1, Hq, 1]
+    terms = np.concatenate([np.broadcast_to(s, (1,) + lses.shape[1:]), lses], axis=0)
+    m = terms.max(axis=0)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    total = np.exp(terms - m_safe).sum(axis=0)                     # [Hq, Tq]
+    lse = np.where(total > 0, m_safe + np.log(np.where(total > 0, total, 1.0)), -np.inf)
+    w = np.where(np.isfinite(lse)[None], np.exp(lses - np.where(np.isfinite(lse), lse, 0.0)[None]), 0.0)
+    out = np.einsum("pht,pthd->thd", w, outs)
+    return out, lse
+
+
 def gather_paged(cache, block_table, seqused, block_size):
     """Keys (or values) of a paged cache as packed rows. "CANN ops-transformer:
     flash_attn", Paged Attention parameter group and the PA_BBND k/v layout

@@ -3,8 +3,8 @@
 Argument marshalling only: every step of the computation runs in the
 library's HIP kernels; torch provides device memory and the stream. The
 functions ``sink_attn_metadata``, ``sink_attn_fwd``, ``sink_attn_bwd``,
-``sink_attn_metadata_paged``, ``sink_attn_fwd_paged`` and
-``sink_attn_arm_timing`` mirror the C entry points one to one. ``Plan``,
+``sink_attn_metadata_paged``, ``sink_attn_fwd_paged``, ``sink_attn_merge``
+and ``sink_attn_arm_timing`` mirror the C entry points one to one. ``Plan``,
 ``PagedPlan``, ``forward``, ``forward_paged``, ``backward``,
 ``SinkAttnFunction`` and ``learnable_sink_attn_varlen`` are conveniences that
 allocate outputs and workspace with torch and call them.
@@ -74,6 +74,8 @@ def lib():
                                           vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp,
                                           vp, vp, ctypes.c_int64, vp]
         L.sink_attn_fwd_paged.restype = ctypes.c_int
+        L.sink_attn_merge.argtypes = [ctypes.c_int32] * 6 + [vp, vp, vp, vp, vp, vp]
+        L.sink_attn_merge.restype = ctypes.c_int
         L.sink_attn_arm_timing.argtypes = [vp, vp]
         L.sink_attn_arm_timing.restype = ctypes.c_int
         L.sink_attn_status_string.argtypes = [ctypes.c_int]
@@ -196,6 +198,32 @@ def sink_attn_fwd_paged(problem, kv, meta_host, meta_dev, q, k_cache, v_cache, b
     if check and st != OK:
         raise SinkAttnError(st, "sink_attn_fwd_paged")
     return st
+
+
+def sink_attn_merge(num_parts, total_q, num_heads_q, head_dim, part_dtype, out_dtype,
+                    partial_out, partial_lse, sinks, out, lse, stream=None, check=True):
+    st = lib().sink_attn_merge(int(num_parts), int(total_q), int(num_heads_q), int(head_dim),
+                               int(part_dtype), int(out_dtype), _ptr(partial_out),
+                               _ptr(partial_lse), _ptr(sinks), _ptr(out), _ptr(lse),
+                               _stream(stream))
+    if check and st != OK:
+        raise SinkAttnError(st, "sink_attn_merge")
+    return st
+
+
+def merge(partial_out, partial_lse, sinks, out_dtype=None):
+    """Merge sink-free partials: partial_out [P, Tq, Hq, D], partial_lse
+    [P, Hq, Tq] fp32 -> out [Tq, Hq, D] (out_dtype, default the partials'),
+    lse [Hq, Tq] (sink inclusive)."""
+    import torch
+    P, Tq, Hq, D = partial_out.shape
+    out_dtype = out_dtype or partial_out.dtype
+    code = lambda dt: BF16 if dt == torch.bfloat16 else FP32
+    out = torch.empty(Tq, Hq, D, dtype=out_dtype, device=partial_out.device)
+    lse = torch.empty(Hq, Tq, dtype=torch.float32, device=partial_out.device)
+    sink_attn_merge(P, Tq, Hq, D, code(partial_out.dtype), code(out_dtype),
+                    partial_out.contiguous(), partial_lse.contiguous(), sinks, out, lse)
+    return out, lse
 
 
 def sink_attn_bwd(problem, meta_host, meta_dev, dout, q, k, v, out, lse, cu_q, cu_k,

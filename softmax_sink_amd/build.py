@@ -14,7 +14,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsinkattn.so")
 OBJDIR = os.path.join(ROOT, "_build")
-SOURCES = ["schedule.cpp", "api.cpp", "fwd_bf16.hip", "bwd_bf16.hip", "f32_path.hip"]
+SOURCES = ["schedule.cpp", "api.cpp", "fwd_bf16.hip", "bwd_bf16.hip", "f32_path.hip",
+           "merge.hip"]
 ARCH = os.environ.get("SINK_ATTN_ARCH", "gfx950")
 
 

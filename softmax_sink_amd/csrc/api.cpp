@@ -249,6 +249,33 @@ sink_attn_status sink_attn_bwd(const sink_attn_problem* p,
   return e == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_E_HIP;
 }
 
+sink_attn_status sink_attn_merge(int32_t num_parts, int32_t total_q,
+                                 int32_t num_heads_q, int32_t head_dim,
+                                 int32_t part_dtype, int32_t out_dtype,
+                                 const void* partial_out, const float* partial_lse,
+                                 const float* sink_logits, void* out, float* lse,
+                                 hipStream_t stream) {
+  if (num_parts <= 0 || num_parts > kMaxMergeParts || total_q <= 0 || num_heads_q <= 0)
+    return SINK_ATTN_E_INVALID;
+  if (head_dim != 64 && head_dim != 128) return SINK_ATTN_E_UNSUPPORTED;
+  const auto known = [](int32_t d) { return d == SINK_ATTN_FP32 || d == SINK_ATTN_BF16; };
+  if (!known(part_dtype) || !known(out_dtype)) return SINK_ATTN_E_UNSUPPORTED;
+  if (!partial_out || !partial_lse || !out || !lse) return SINK_ATTN_E_INVALID;
+  if (!aligned16(partial_out) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(partial_lse) & 3u) || (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return SINK_ATTN_E_INVALID;
+  // the widest index: parts x rows x head_dim elements
+  if (static_cast<int64_t>(num_parts) * total_q * num_heads_q * head_dim >= (int64_t(1) << 40))
+    return SINK_ATTN_E_UNSUPPORTED;
+  MergeArgs a{};
+  a.part_out = partial_out; a.part_lse = partial_lse; a.sinks = sink_logits;
+  a.out = out; a.lse = lse;
+  a.parts = num_parts; a.total_q = total_q; a.hq = num_heads_q;
+  const TimingHook t = take_timing();
+  const hipError_t e = launch_merge(a, head_dim, part_dtype, out_dtype, stream, t);
+  return e == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_E_HIP;
+}
+
 sink_attn_status sink_attn_arm_timing(hipEvent_t start, hipEvent_t stop) {
   if ((start == nullptr) != (stop == nullptr)) return SINK_ATTN_E_INVALID;
   g_timing.start = start;

@@ -43,6 +43,7 @@ constexpr int kDecBN = 64;     // keys per split-KV tile step
 constexpr int kDecChunk = 2048;// keys per split-KV work item
 constexpr int kDecMaxRows = 64;// (query rows x GQA group) handled per split item
 constexpr int kPreRows = 64;   // tokens per block of the backward preprocess
+constexpr int kMaxMergeParts = 4096;  // partials one context-parallel merge accepts
 
 inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
@@ -137,6 +138,15 @@ struct BwdArgs {
   float scale;
 };
 
+struct MergeArgs {
+  const void* part_out;     // [parts, total_q, hq, D]
+  const float* part_lse;    // [parts, hq, total_q], sink-free
+  const float* sinks;       // null: no sink
+  void* out;
+  float* lse;
+  int parts, total_q, hq;
+};
+
 struct TimingHook {
   hipEvent_t start = nullptr;
   hipEvent_t stop = nullptr;
@@ -150,5 +160,7 @@ hipError_t launch_fwd_f32(const FwdArgs& a, int head_dim, hipStream_t s,
                           const TimingHook& t);
 hipError_t launch_bwd_f32(const BwdArgs& a, int head_dim, hipStream_t s,
                           const TimingHook& t);
+hipError_t launch_merge(const MergeArgs& a, int head_dim, int part_dtype, int out_dtype,
+                        hipStream_t s, const TimingHook& t);
 
 }  // namespace sinkattn

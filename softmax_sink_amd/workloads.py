@@ -207,6 +207,20 @@ def _train_lengths(rng, n=8, total=32768, lo=1024, hi=8192):
             return np.concatenate([head, [last]])
 
 
+def merge_inputs(seed, parts, total_q, num_heads_q, head_dim):
+    """Synthetic sink-free partials for a context-parallel merge: partial
+    outputs N(0, 1) as bf16 bits [parts, Tq, Hq, D], partial lse N(2, 3^2)
+    fp32 [parts, Hq, Tq] (about one part in eight empty: -inf), sinks N(0, 1)
+    fp32 [Hq]."""
+    rng = np.random.default_rng(seed)
+    outs = _normal(rng, parts * total_q * num_heads_q * head_dim, True).reshape(
+        parts, total_q, num_heads_q, head_dim)
+    lses = (rng.standard_normal((parts, num_heads_q, total_q), dtype=np.float32) * 3 + 2)
+    lses[rng.random(lses.shape) < 0.125] = -np.inf
+    sinks = rng.standard_normal(num_heads_q, dtype=np.float32)
+    return outs, lses.astype(np.float32), sinks
+
+
 CONFIG_NAMES = ("softmax1_fp32", "prefill_varlen", "train_varlen",
                 "gqa_window", "decode_softmax_n")
 DECODE_PAGE_ROWS = 16      # block size of the paged decode workload

@@ -302,3 +302,20 @@ def test_paged_fwd_argument_checks():
     # a paged table is refused by the contiguous calls
     assert _fwd(p, meta, workspace=FAKE, workspace_bytes=1 << 40) == B.E_META_MISMATCH
     assert _bwd(p, meta) == B.E_META_MISMATCH
+
+
+def test_merge_argument_checks():
+    def m(parts=2, tq=10, hq=4, d=128, pd=B.BF16, od=B.BF16, po=FAKE, pl=FAKE, out=FAKE, lse=FAKE):
+        return B.sink_attn_merge(parts, tq, hq, d, pd, od, po, pl, None, out, lse, stream=0,
+                                 check=False)
+    assert m(parts=0) == B.E_INVALID
+    assert m(parts=4097) == B.E_INVALID
+    assert m(tq=0) == B.E_INVALID
+    assert m(hq=0) == B.E_INVALID
+    assert m(d=96) == B.E_UNSUPPORTED
+    assert m(pd=7) == B.E_UNSUPPORTED
+    assert m(od=3) == B.E_UNSUPPORTED
+    assert m(po=None) == B.E_INVALID
+    assert m(lse=None) == B.E_INVALID
+    assert m(out=FAKE + 8) == B.E_INVALID
+    assert m(pl=FAKE + 2) == B.E_INVALID

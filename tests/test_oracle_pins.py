@@ -479,3 +479,55 @@ def test_gather_paged_inverts_a_page_scatter():
         rows, cu = O.gather_paged(cache, table, lens, bs)
         assert cu.tolist() == np.concatenate([[0], np.cumsum(lens)]).tolist()
         assert np.array_equal(rows, np.array(want))
+
+
+def test_merge_partials_hand_example_and_empty_parts():
+    """One part holding e^{lse_p} = 3 of mass with out_p = 2, a sink with
+    e^s = 1: the merged mass is 4, so lse = ln 4 and out = 2 * 3/4. Parts
+    with no kept key (lse_p = -inf) add nothing; with nothing at all the row
+    is the fully masked row of issue #108108 (out 0, lse = s)."""
+    out, lse = O.merge_partials(np.array([[[[2.0]]], [[[7.0]]]]),
+                                np.array([[[math.log(3.0)]], [[-np.inf]]]), [0.0])
+    assert np.isclose(lse[0, 0], math.log(4.0), rtol=0, atol=1e-15)
+    assert np.isclose(out[0, 0, 0], 1.5, rtol=0, atol=1e-15)
+    out, lse = O.merge_partials(np.zeros((2, 1, 2, 3)), np.full((2, 2, 1), -np.inf),
+                                [0.25, -np.inf])
+    assert np.all(out == 0) and lse[0, 0] == 0.25 and lse[1, 0] == -np.inf
+
+
+def test_merge_of_key_split_equals_unsplit_attention():
+    """Splitting every sequence's keys into disjoint parts, attending each part
+    without the sink and merging gives the unsplit attention with the sink:
+    three parts of a non-causal problem, and for a decode-shaped causal
+    problem a prefix part (every row keeps all of it: non-causal) plus the
+    causal suffix (its bottom-right alignment is the original one)."""
+    rng = np.random.default_rng(21)
+    hq, hk, d = 4, 2, 16
+    sinks = rng.standard_normal(hq)
+    lq, lk = [3, 5], [40, 23]
+    cu_q = np.r_[0, np.cumsum(lq)].astype(np.int32)
+    cu_k = np.r_[0, np.cumsum(lk)].astype(np.int32)
+    q = rng.standard_normal((cu_q[-1], hq, d))
+    k = rng.standard_normal((cu_k[-1], hk, d))
+    v = rng.standard_normal((cu_k[-1], hk, d))
+    none = np.full(hq, -np.inf)
+
+    def part(bounds, causal):
+        idx = np.concatenate([np.arange(cu_k[b] + a, cu_k[b] + c) for b, (a, c) in enumerate(bounds)])
+        ck = np.r_[0, np.cumsum([c - a for a, c in bounds])].astype(np.int32)
+        o, l, _ = O.sink_attention_forward(q, k[idx], v[idx], cu_q, ck, none, 0.3, causal, -1, -1)
+        return o, l
+
+    ref_o, ref_l, _ = O.sink_attention_forward(q, k, v, cu_q, cu_k, sinks, 0.3, False, -1, -1)
+    parts = [part([(0, 10), (0, 7)], False), part([(10, 31), (7, 8)], False),
+             part([(31, 40), (8, 23)], False)]
+    mo, ml = O.merge_partials([p[0] for p in parts], [p[1] for p in parts], sinks)
+    assert np.allclose(mo, ref_o, rtol=0, atol=1e-12) and np.allclose(ml, ref_l, rtol=0, atol=1e-12)
+
+    ref_o, ref_l, _ = O.sink_attention_forward(q, k, v, cu_q, cu_k, sinks, 0.3, True, -1, -1)
+    # rows sit at key positions >= lk - lq, so keys below that are kept by every row
+    pre = [(0, lk[b] - lq[b]) for b in range(2)]
+    suf = [(lk[b] - lq[b], lk[b]) for b in range(2)]
+    parts = [part(pre, False), part(suf, True)]
+    mo, ml = O.merge_partials([p[0] for p in parts], [p[1] for p in parts], sinks)
+    assert np.allclose(mo, ref_o, rtol=0, atol=1e-12) and np.allclose(ml, ref_l, rtol=0, atol=1e-12)
