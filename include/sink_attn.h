@@ -77,7 +77,10 @@ typedef enum {
   SINK_ATTN_E_HIP = 5               /* a HIP launch failed                  */
 } sink_attn_status;
 
-typedef enum { SINK_ATTN_FP32 = 0, SINK_ATTN_BF16 = 1 } sink_attn_dtype;
+/* Element type of q, k, v, out, dout, dq, dk, dv (lse, sinks, dsink are
+ * always fp32). fp16 is the CANN page's other input type (q, k, v
+ * validation); it runs the same MFMA kernels as bf16. */
+typedef enum { SINK_ATTN_FP32 = 0, SINK_ATTN_BF16 = 1, SINK_ATTN_FP16 = 2 } sink_attn_dtype;
 
 /* The problem, passed by pointer and not retained. Checks: 0 < batch <
  * 65536; total_q, total_k, num_heads_q, num_heads_k > 0; num_heads_q %
@@ -183,7 +186,7 @@ typedef struct {
  * they are checked here and hashed into the header, and the device copy
  * passed to sink_attn_fwd_paged must equal it (not checked there). Only
  * short query groups are supported (max_seqlen_q * num_heads_q /
- * num_heads_k <= 64, the split-KV path) and only bf16: otherwise
+ * num_heads_k <= 64, the split-KV path) and only bf16 or fp16: otherwise
  * E_UNSUPPORTED. The table can only be used with sink_attn_fwd_paged.
  * Errors: E_INVALID, E_UNSUPPORTED, E_BUFFER_TOO_SMALL. */
 sink_attn_status sink_attn_metadata_paged(const sink_attn_problem* p,

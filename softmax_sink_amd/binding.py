@@ -22,7 +22,17 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsinkattn.so")
 
 OK, E_INVALID, E_UNSUPPORTED, E_META_MISMATCH, E_BUFFER_TOO_SMALL, E_HIP = range(6)
-FP32, BF16 = 0, 1
+FP32, BF16, FP16 = 0, 1, 2
+
+
+def dtype_code(dtype):
+    """sink_attn_dtype of a name ("fp32", "bf16", "fp16") or torch dtype."""
+    import torch
+    codes = {"fp32": FP32, "bf16": BF16, "fp16": FP16, torch.float32: FP32,
+             torch.bfloat16: BF16, torch.float16: FP16}
+    if dtype not in codes:
+        raise SinkAttnError(E_UNSUPPORTED, f"dtype {dtype}")
+    return codes[dtype]
 
 
 class SinkAttnError(RuntimeError):
@@ -218,10 +228,9 @@ def merge(partial_out, partial_lse, sinks, out_dtype=None):
     import torch
     P, Tq, Hq, D = partial_out.shape
     out_dtype = out_dtype or partial_out.dtype
-    code = lambda dt: BF16 if dt == torch.bfloat16 else FP32
     out = torch.empty(Tq, Hq, D, dtype=out_dtype, device=partial_out.device)
     lse = torch.empty(Hq, Tq, dtype=torch.float32, device=partial_out.device)
-    sink_attn_merge(P, Tq, Hq, D, code(partial_out.dtype), code(out_dtype),
+    sink_attn_merge(P, Tq, Hq, D, dtype_code(partial_out.dtype), dtype_code(out_dtype),
                     partial_out.contiguous(), partial_lse.contiguous(), sinks, out, lse)
     return out, lse
 
@@ -263,7 +272,7 @@ class Plan:
         import torch
         self.cu_q_host = np.asarray(cu_seqlens_q, dtype=np.int32)
         self.cu_k_host = np.asarray(cu_seqlens_k, dtype=np.int32)
-        self.dtype_code = BF16 if dtype in ("bf16", torch.bfloat16) else FP32
+        self.dtype_code = dtype_code(dtype)
         self.problem = make_problem(self.cu_q_host, self.cu_k_host, num_heads_q,
                                     num_heads_k, head_dim, causal, window[0],
                                     window[1], self.dtype_code)
@@ -285,7 +294,7 @@ class PagedPlan:
 
     def __init__(self, cu_seqlens_q, seqused_kv, block_table, block_size, num_blocks,
                  num_heads_q, num_heads_k, head_dim, causal, window=(-1, -1),
-                 device="cuda"):
+                 device="cuda", dtype="bf16"):
         import torch
         self.cu_q_host = np.asarray(cu_seqlens_q, dtype=np.int32)
         self.seqused_host = np.asarray(seqused_kv, dtype=np.int32)
@@ -293,7 +302,7 @@ class PagedPlan:
         self.kv = PagedKV(int(block_size), int(self.block_table_host.shape[1]), int(num_blocks))
         self.problem = make_problem_paged(self.cu_q_host, self.seqused_host, num_heads_q,
                                           num_heads_k, head_dim, causal, window[0],
-                                          window[1], BF16)
+                                          window[1], dtype_code(dtype))
         self.meta, self.fwd_ws_bytes = sink_attn_metadata_paged(
             self.problem, self.kv, self.cu_q_host, self.seqused_host, self.block_table_host)
         self.meta_dev = torch.from_numpy(self.meta).to(device)

@@ -56,10 +56,13 @@ FwdArgs fwd_args(const sink_attn_problem* p, const void* q, const void* k,
 
 // Split-KV items, per-sequence table and partials workspace of a decode-mode
 // table.
-void decode_args(FwdArgs& a, const sink_attn_problem* p, const int32_t* meta_host,
+bool decode_args(FwdArgs& a, const sink_attn_problem* p, const int32_t* meta_host,
                  const int32_t* meta_dev, void* workspace) {
   const FwdWorkspace w = fwd_workspace_layout(meta_host[kDecRows], p->head_dim,
                                               p->dtype, kModeDecode);
+  // the partials must fit the workspace the header asked the caller for
+  if (w.bytes > header_i64(meta_host, kFwdWsLo, kFwdWsHi) || (w.bytes > 0 && !workspace))
+    return false;
   char* base = static_cast<char*>(workspace);
   a.items = meta_dev + meta_host[kDecOff];
   a.n_items = meta_host[kNDec];
@@ -67,6 +70,7 @@ void decode_args(FwdArgs& a, const sink_attn_problem* p, const int32_t* meta_hos
   a.ws_o = reinterpret_cast<float*>(base + w.o_off);
   a.ws_m = reinterpret_cast<float*>(base + w.m_off);
   a.ws_l = reinterpret_cast<float*>(base + w.l_off);
+  return true;
 }
 
 }  // namespace
@@ -110,7 +114,7 @@ sink_attn_status sink_attn_metadata_paged(const sink_attn_problem* p,
   if (st != SINK_ATTN_OK) return st;
   st = validate_cu_seqlens(*p, cu_seqlens_q_host, cu_k.data());
   if (st != SINK_ATTN_OK) return st;
-  if (p->dtype != SINK_ATTN_BF16 ||
+  if (p->dtype == SINK_ATTN_FP32 ||
       static_cast<int64_t>(p->max_seqlen_q) * (p->num_heads_q / p->num_heads_k) > kDecMaxRows)
     return SINK_ATTN_E_UNSUPPORTED;
   if (meta_host && meta_capacity_words < 0) return SINK_ATTN_E_INVALID;
@@ -147,12 +151,12 @@ sink_attn_status sink_attn_fwd(const sink_attn_problem* p,
   if (p->dtype == SINK_ATTN_FP32) {
     e = launch_fwd_f32(a, p->head_dim, stream, t);
   } else if (mode == kModeDecode) {
-    decode_args(a, p, meta_host, meta_dev, workspace);
-    e = launch_fwd_bf16(a, p->head_dim, mode, stream, t);
+    if (!decode_args(a, p, meta_host, meta_dev, workspace)) return SINK_ATTN_E_META_MISMATCH;
+    e = launch_fwd_16(a, p->head_dim, p->dtype, mode, stream, t);
   } else {
     a.items = meta_dev + meta_host[kFwdOff];
     a.n_items = meta_host[kNFwd];
-    e = launch_fwd_bf16(a, p->head_dim, mode, stream, t);
+    e = launch_fwd_16(a, p->head_dim, p->dtype, mode, stream, t);
   }
   return e == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_E_HIP;
 }
@@ -185,7 +189,7 @@ sink_attn_status sink_attn_fwd_paged(const sink_attn_problem* p,
 
   FwdArgs a = fwd_args(p, q, k_cache, v_cache, cu_seqlens_q, nullptr, sink_logits, scale,
                        out, lse);
-  decode_args(a, p, meta_host, meta_dev, workspace);
+  if (!decode_args(a, p, meta_host, meta_dev, workspace)) return SINK_ATTN_E_META_MISMATCH;
   a.block_table = block_table;
   a.seqused_k = seqused_kv;
   a.page_size = kv->block_size;
@@ -193,7 +197,7 @@ sink_attn_status sink_attn_fwd_paged(const sink_attn_problem* p,
   a.page_magic = static_cast<uint32_t>(((uint64_t(1) << 32) + kv->block_size - 1) /
                                        static_cast<uint64_t>(kv->block_size));
   const TimingHook t = take_timing();
-  const hipError_t e = launch_fwd_bf16(a, p->head_dim, kModeDecode, stream, t);
+  const hipError_t e = launch_fwd_16(a, p->head_dim, p->dtype, kModeDecode, stream, t);
   return e == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_E_HIP;
 }
 
@@ -245,7 +249,7 @@ sink_attn_status sink_attn_bwd(const sink_attn_problem* p,
   const TimingHook t = take_timing();
   hipError_t e = p->dtype == SINK_ATTN_FP32
                      ? launch_bwd_f32(a, p->head_dim, stream, t)
-                     : launch_bwd_bf16(a, p->head_dim, stream, t);
+                     : launch_bwd_16(a, p->head_dim, p->dtype, stream, t);
   return e == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_E_HIP;
 }
 
@@ -258,7 +262,9 @@ sink_attn_status sink_attn_merge(int32_t num_parts, int32_t total_q,
   if (num_parts <= 0 || num_parts > kMaxMergeParts || total_q <= 0 || num_heads_q <= 0)
     return SINK_ATTN_E_INVALID;
   if (head_dim != 64 && head_dim != 128) return SINK_ATTN_E_UNSUPPORTED;
-  const auto known = [](int32_t d) { return d == SINK_ATTN_FP32 || d == SINK_ATTN_BF16; };
+  const auto known = [](int32_t d) {
+    return d == SINK_ATTN_FP32 || d == SINK_ATTN_BF16 || d == SINK_ATTN_FP16;
+  };
   if (!known(part_dtype) || !known(out_dtype)) return SINK_ATTN_E_UNSUPPORTED;
   if (!partial_out || !partial_lse || !out || !lse) return SINK_ATTN_E_INVALID;
   if (!aligned16(partial_out) || !aligned16(out) ||
@@ -287,7 +293,7 @@ const char* sink_attn_status_string(sink_attn_status s) {
   switch (s) {
     case SINK_ATTN_OK: return "ok";
     case SINK_ATTN_E_INVALID: return "invalid argument";
-    case SINK_ATTN_E_UNSUPPORTED: return "unsupported head_dim or dtype";
+    case SINK_ATTN_E_UNSUPPORTED: return "unsupported head_dim, dtype or shape";
     case SINK_ATTN_E_META_MISMATCH: return "metadata does not match the call";
     case SINK_ATTN_E_BUFFER_TOO_SMALL: return "buffer too small";
     case SINK_ATTN_E_HIP: return "HIP launch failed";

@@ -1,4 +1,4 @@
-// Backward kernels, bf16 inputs, fp32 accumulation, for gfx950.
+// Backward kernels, bf16 or fp16 inputs (T), fp32 accumulation, for gfx950.
 //
 // Gradient of the sink softmax ("slime: learnable_softmax_attention.py",
 // class docstring and backward; the chain rule through softmax([S, s])):
@@ -39,10 +39,10 @@ using namespace dev;
 // query tile). Role 1 works one step behind role 0, so three Q tiles are
 // live at once (role 0's, role 1's and the one in flight) and two dO tiles;
 // lse and D rows travel with their Q and dO stages. P of a step is handed
-// from role 0 to role 1 as bf16 MFMA fragments ("dumps", one per parity).
+// from role 0 to role 1 as 16-bit MFMA fragments ("dumps", one per parity).
 template <int D>
 struct KvSmem {
-  static constexpr int kTile = kBwdBM * D * 2;          // one [64][D] bf16 tile
+  static constexpr int kTile = kBwdBM * D * 2;          // one [64][D] 16-bit tile
   static constexpr int off_q = 0;                       // Q of step j: stage j % 3
   static constexpr int off_do = off_q + 3 * kTile;      // dO of step j: stage j % 2
   static constexpr int off_lse = off_do + 2 * kTile;    // 3 x [64] fp32, log2 domain
@@ -73,7 +73,7 @@ struct StepIdx {
 // step i-1 (whose P it still holds), so the exponentials of step i can issue
 // between the dV MFMAs; role 1 computes all of step i-1 with the P that
 // role 0 left in LDS. One barrier per iteration; steps + 1 iterations.
-template <int D>
+template <int D, typename T>
 __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using S = KvSmem<D>;
   constexpr int NT = D / 16;
@@ -97,16 +97,16 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int64_t kstride = (int64_t)a.hk * D;
   const int64_t qstride = (int64_t)a.hq * D;
   // role 0 holds K rows (B operand of S = Q K^T), role 1 V rows (of dP = dO V^T)
-  const bf16* fp = static_cast<const bf16*>(role == 0 ? a.k : a.v) + (int64_t)k0 * kstride + hk * D;
-  bf16x8 frag[2][NT];
+  const T* fp = static_cast<const T*>(role == 0 ? a.k : a.v) + (int64_t)k0 * kstride + hk * D;
+  vec8<T> frag[2][NT];
   int ilo[2], ihi[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int j = jbase + 32 * kb;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
-      frag[kb][t] = j < lk ? __builtin_bit_cast(bf16x8, ld16(fp + (int64_t)j * kstride + 16 * t + 8 * hl))
-                           : bf16x8{};
+      frag[kb][t] = j < lk ? __builtin_bit_cast(vec8<T>, ld16(fp + (int64_t)j * kstride + 16 * t + 8 * hl))
+                           : vec8<T>{};
     key_row_range(j, lq, lk, a.causal, a.win_left, a.win_right, ilo[kb], ihi[kb]);
   }
 
@@ -116,8 +116,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int nq = qt_hi - qt_lo;
   const int steps = nq * G;
   const float c2 = a.scale * kLog2e;
-  const bf16* qg = static_cast<const bf16*>(a.q) + (int64_t)q0 * qstride + (int64_t)hk * G * D;
-  const bf16* dg = static_cast<const bf16*>(a.dout) + (int64_t)q0 * qstride + (int64_t)hk * G * D;
+  const T* qg = static_cast<const T*>(a.q) + (int64_t)q0 * qstride + (int64_t)hk * G * D;
+  const T* dg = static_cast<const T*>(a.dout) + (int64_t)q0 * qstride + (int64_t)hk * G * D;
   const int64_t rbase = ((int64_t)hk * G) * a.total_q + q0;   // lse / D row of (g = 0, row 0)
 
   TileDma<D, kKvThreads> dma;
@@ -187,9 +187,9 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // The two roles run separate loops with the same barrier sequence (one
   // per iteration), so that each is register-allocated on its own.
   if (steps > 0 && role == 0) {
-    bf16x8 pf[2][2][2];                          // P of the previous step [qb][kb][half]
+    vec8<T> pf[2][2][2];                          // P of the previous step [qb][kb][half]
 #pragma unroll
-    for (int f = 0; f < 8; ++f) pf[f >> 2][(f >> 1) & 1][f & 1] = bf16x8{};
+    for (int f = 0; f < 8; ++f) pf[f >> 2][(f >> 1) & 1][f & 1] = vec8<T>{};
     int qs = 0;                                  // it % 3
     for (int it = 0; it <= steps; ++it) {
       const int qs_next = qs == 2 ? 0 : qs + 1;
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         f32x16 x0 = f32x16{}, x1 = f32x16{};
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          const bf16x8 qa = lds_row_chunk<D>(q_l, 32 * qb + c, 2 * t + hl);
+          const vec8<T> qa = lds_row_chunk<D, T>(q_l, 32 * qb + c, 2 * t + hl);
           x0 = mfma32(qa, frag[0][t], x0);
           x1 = mfma32(qa, frag[1][t], x1);
         }
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int db = 0; db < NB; ++db) {
-            const bf16x8 da = lds_col_operand<D>(dop_l, 16 * (2 * qb + h), 32 * db);
+            const vec8<T> da = lds_col_operand<D, T>(dop_l, 16 * (2 * qb + h), 32 * db);
             acc[db][0] = mfma32(da, pf[qb][0][h], acc[db][0]);
             acc[db][1] = mfma32(da, pf[qb][1][h], acc[db][1]);
           }
@@ -243,10 +243,10 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          pf[qb][0][h] = frag_half(x0, h);
-          pf[qb][1][h] = frag_half(x1, h);
-          *reinterpret_cast<bf16x8*>(dump + ((4 * qb + h) * 64 + lane) * 16) = pf[qb][0][h];
-          *reinterpret_cast<bf16x8*>(dump + ((4 * qb + 2 + h) * 64 + lane) * 16) = pf[qb][1][h];
+          pf[qb][0][h] = frag_half<T>(x0, h);
+          pf[qb][1][h] = frag_half<T>(x1, h);
+          *reinterpret_cast<vec8<T>*>(dump + ((4 * qb + h) * 64 + lane) * 16) = pf[qb][0][h];
+          *reinterpret_cast<vec8<T>*>(dump + ((4 * qb + 2 + h) * 64 + lane) * 16) = pf[qb][1][h];
         }
       }
       finish(it, qs_next, ds);
@@ -271,15 +271,15 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
           f32x16 x0 = f32x16{}, x1 = f32x16{};
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
-            const bf16x8 ga = lds_row_chunk<D>(do_l, 32 * qb + c, 2 * t + hl);
+            const vec8<T> ga = lds_row_chunk<D, T>(do_l, 32 * qb + c, 2 * t + hl);
             x0 = mfma32(ga, frag[0][t], x0);
             x1 = mfma32(ga, frag[1][t], x1);
           }
           sched_mfma_pipeline<2 * NT, 2, 1, 3>();
-          bf16x8 pp[4];                          // [kb][half]
+          vec8<T> pp[4];                          // [kb][half]
 #pragma unroll
           for (int f = 0; f < 4; ++f)
-            pp[f] = *reinterpret_cast<const bf16x8*>(dump + ((4 * qb + f) * 64 + lane) * 16);
+            pp[f] = *reinterpret_cast<const vec8<T>*>(dump + ((4 * qb + f) * 64 + lane) * 16);
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
             const f32x4 d4 = *reinterpret_cast<const f32x4*>(dv_l + 32 * qb + 8 * g4 + 4 * hl);
@@ -293,11 +293,11 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
           }
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            const bf16x8 s0 = frag_half(x0, h);
-            const bf16x8 s1 = frag_half(x1, h);
+            const vec8<T> s0 = frag_half<T>(x0, h);
+            const vec8<T> s1 = frag_half<T>(x1, h);
 #pragma unroll
             for (int db = 0; db < NB; ++db) {
-              const bf16x8 qa = lds_col_operand<D>(qq_l, 16 * (2 * qb + h), 32 * db);
+              const vec8<T> qa = lds_col_operand<D, T>(qq_l, 16 * (2 * qb + h), 32 * db);
               acc[db][0] = mfma32(qa, s0, acc[db][0]);
               acc[db][1] = mfma32(qa, s1, acc[db][1]);
             }
@@ -316,14 +316,14 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   for (int kb = 0; kb < 2; ++kb) {
     const int j = jbase + 32 * kb;
     if (j < lk) {
-      bf16* dst = static_cast<bf16*>(role == 0 ? a.dv : a.dk) + (int64_t)(k0 + j) * kstride + hk * D;
+      T* dst = static_cast<T*>(role == 0 ? a.dv : a.dk) + (int64_t)(k0 + j) * kstride + hk * D;
 #pragma unroll
       for (int db = 0; db < NB; ++db)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int d = 32 * db + 8 * g4 + 4 * hl;
           *reinterpret_cast<u32x2*>(dst + d) =
-              pack4_bits(acc[db][kb][4 * g4] * sc, acc[db][kb][4 * g4 + 1] * sc,
+              pack4_bits<T>(acc[db][kb][4 * g4] * sc, acc[db][kb][4 * g4 + 1] * sc,
                          acc[db][kb][4 * g4 + 2] * sc, acc[db][kb][4 * g4 + 3] * sc);
         }
     }
@@ -331,7 +331,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // dQ, query-tile outer. Work items and block numbering are the forward's.
-template <int D>
+template <int D, typename T>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   constexpr int BN = kFwdBN;
   constexpr int NT = D / 16;
@@ -357,20 +357,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 
   const int64_t qstride = (int64_t)a.hq * D;
   const int64_t kstride = (int64_t)a.hk * D;
-  const bf16* kp = static_cast<const bf16*>(a.k) + (int64_t)k0 * kstride + hk * D;
-  const bf16* vp = static_cast<const bf16*>(a.v) + (int64_t)k0 * kstride + hk * D;
+  const T* kp = static_cast<const T*>(a.k) + (int64_t)k0 * kstride + hk * D;
+  const T* vp = static_cast<const T*>(a.v) + (int64_t)k0 * kstride + hk * D;
 
   // Q and dO rows as B operands of S^T = K Q^T and dP^T = V dO^T
-  bf16x8 qf[NT], gf[NT];
+  vec8<T> qf[NT], gf[NT];
   const int64_t roff = (int64_t)(q0 + i) * qstride + h * D;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     if (i < lq) {
-      qf[t] = __builtin_bit_cast(bf16x8, ld16(static_cast<const bf16*>(a.q) + roff + 16 * t + 8 * hl));
-      gf[t] = __builtin_bit_cast(bf16x8, ld16(static_cast<const bf16*>(a.dout) + roff + 16 * t + 8 * hl));
+      qf[t] = __builtin_bit_cast(vec8<T>, ld16(static_cast<const T*>(a.q) + roff + 16 * t + 8 * hl));
+      gf[t] = __builtin_bit_cast(vec8<T>, ld16(static_cast<const T*>(a.dout) + roff + 16 * t + 8 * hl));
     } else {
-      qf[t] = bf16x8{};
-      gf[t] = bf16x8{};
+      qf[t] = vec8<T>{};
+      gf[t] = vec8<T>{};
     }
   }
   float lse2 = __builtin_huge_valf(), dval = 0.f;
@@ -413,8 +413,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        s = mfma32(lds_row_chunk<D>(kt_lds, kb * 32 + c, 2 * t + hl), qf[t], s);
-        dp = mfma32(lds_row_chunk<D>(vt_lds, kb * 32 + c, 2 * t + hl), gf[t], dp);
+        s = mfma32(lds_row_chunk<D, T>(kt_lds, kb * 32 + c, 2 * t + hl), qf[t], s);
+        dp = mfma32(lds_row_chunk<D, T>(vt_lds, kb * 32 + c, 2 * t + hl), gf[t], dp);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -427,10 +427,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const bf16x8 sf = frag_half(dp, hh);
+        const vec8<T> sf = frag_half<T>(dp, hh);
 #pragma unroll
         for (int n = 0; n < NB; ++n)
-          o[n] = mfma32(lds_col_operand<D>(kt_lds, 32 * kb + 16 * hh, 32 * n), sf, o[n]);
+          o[n] = mfma32(lds_col_operand<D, T>(kt_lds, 32 * kb + 16 * hh, 32 * n), sf, o[n]);
       }
     }
     wait_vmem();        // the next tile has landed in LDS
@@ -444,7 +444,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   if (kt < kt_hi) tile_step(std::integral_constant<int, 0>{}, kt);
 
   if (i < lq) {
-    bf16* dqp = static_cast<bf16*>(a.dq) + roff;
+    T* dqp = static_cast<T*>(a.dq) + roff;
     const float sc = a.scale;
 #pragma unroll
     for (int n = 0; n < NB; ++n)
@@ -452,28 +452,28 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       for (int g = 0; g < 4; ++g) {
         const int d = 32 * n + 8 * g + 4 * hl;
         *reinterpret_cast<u32x2*>(dqp + d) =
-            pack4_bits(o[n][4 * g] * sc, o[n][4 * g + 1] * sc, o[n][4 * g + 2] * sc,
+            pack4_bits<T>(o[n][4 * g] * sc, o[n][4 * g + 1] * sc, o[n][4 * g + 2] * sc,
                        o[n][4 * g + 3] * sc);
       }
   }
 }
 
-template <int D>
+template <int D, typename T>
 hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s, const TimingHook& th) {
-  hipError_t e = launch_bwd_pre<D, bf16>(a, s);
+  hipError_t e = launch_bwd_pre<D, T>(a, s);
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D>),
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, T>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, KvSmem<D>::bytes);
   if (e != hipSuccess) return e;
   if (th.start) hipEventRecord(th.start, s);
   if (a.n_items > 0)
-    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(a.n_items * a.hk), dim3(kKvThreads),
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, T>), dim3(a.n_items * a.hk), dim3(kKvThreads),
                        KvSmem<D>::bytes, s, a);
   if (th.stop) hipEventRecord(th.stop, s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.n_items_q > 0)
-    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(a.n_items_q * a.hq), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, T>), dim3(a.n_items_q * a.hq), dim3(256), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_dsink_finalize(a, s);
@@ -481,8 +481,11 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s, const TimingHook& th) {
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(const BwdArgs& a, int head_dim, hipStream_t s, const TimingHook& t) {
-  return head_dim == 128 ? launch_bwd_d<128>(a, s, t) : launch_bwd_d<64>(a, s, t);
+hipError_t launch_bwd_16(const BwdArgs& a, int head_dim, int dtype, hipStream_t s,
+                         const TimingHook& t) {
+  if (dtype == SINK_ATTN_FP16)
+    return head_dim == 128 ? launch_bwd_d<128, f16>(a, s, t) : launch_bwd_d<64, f16>(a, s, t);
+  return head_dim == 128 ? launch_bwd_d<128, bf16>(a, s, t) : launch_bwd_d<64, bf16>(a, s, t);
 }
 
 }  // namespace sinkattn

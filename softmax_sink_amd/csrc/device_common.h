@@ -29,6 +29,16 @@ namespace dev {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// Vectors of the 16-bit input types (bf16 or fp16): 8 elements are one
+// MFMA operand fragment per lane, 4 elements one 8-byte store.
+template <typename T> struct V16;
+template <> struct V16<bf16> { typedef bf16x8 x8; typedef bf16x4 x4; };
+template <> struct V16<f16> { typedef f16x8 x8; typedef f16x4 x4; };
+template <typename T> using vec8 = typename V16<T>::x8;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -41,6 +51,10 @@ constexpr float kNegInf = -__builtin_huge_valf();
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// v_mfma_f32_32x32x16_f16: the same lane layouts with fp16 operands.
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 // 2^x with the hardware v_exp_f32 (exact at -inf -> 0); e^x is obtained by
@@ -64,7 +78,7 @@ __device__ __forceinline__ float half_max(float x) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS tiles of bf16 rows (D elements = D/8 16-byte chunks per row), stored
+// LDS tiles of 16-bit rows (D elements = D/8 16-byte chunks per row), stored
 // without padding; the 16-byte chunk c of row r sits at chunk c ^ f(r).
 // f makes both access patterns conflict-free over the 64 4-byte banks:
 //   (a) 16 lanes reading the same chunk of 16 consecutive rows (ds_read_b128);
@@ -87,10 +101,10 @@ __device__ __forceinline__ int tile_off(int r, int col) {
 }
 
 // 16-byte chunk (8 elements starting at column 8*chunk) of row r.
-template <int D>
-__device__ __forceinline__ bf16x8 lds_row_chunk(const char* tile, int r, int chunk) {
-  return *reinterpret_cast<const bf16x8*>(tile + r * (D * 2) +
-                                          ((chunk ^ swz<D>(r)) << 4));
+template <int D, typename T = bf16>
+__device__ __forceinline__ vec8<T> lds_row_chunk(const char* tile, int r, int chunk) {
+  return *reinterpret_cast<const vec8<T>*>(tile + r * (D * 2) +
+                                           ((chunk ^ swz<D>(r)) << 4));
 }
 
 template <int D>
@@ -106,8 +120,8 @@ __device__ __forceinline__ s16x4 ds_read_tr(const char* p) {
 // MFMA operand whose K slots run down the rows of an LDS tile (rows
 // row0 + 8(i/4) + 4hl + i%4, i = 0..7) and whose M/N index is column
 // col0 + lane%32: two transposed reads.
-template <int D>
-__device__ __forceinline__ bf16x8 lds_col_operand(const char* tile, int row0, int col0) {
+template <int D, typename T = bf16>
+__device__ __forceinline__ vec8<T> lds_col_operand(const char* tile, int row0, int col0) {
   const int lane = threadIdx.x & 63;
   const int grp = lane >> 4;          // 16-lane group
   const int hl = grp >> 1;            // lane half
@@ -118,25 +132,28 @@ __device__ __forceinline__ bf16x8 lds_col_operand(const char* tile, int row0, in
   s16x4 hi = ds_read_tr(tile + tile_off<D>(r + 8, col));
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, v);
+  return __builtin_bit_cast(vec8<T>, v);
 }
 
-// Eight fp32 values -> bf16x8, round to nearest even (v_cvt_pk_bf16_f32).
-__device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3,
-                                        float a4, float a5, float a6, float a7) {
-  bf16x8 r = {(bf16)a0, (bf16)a1, (bf16)a2, (bf16)a3,
-              (bf16)a4, (bf16)a5, (bf16)a6, (bf16)a7};
+// Eight fp32 values -> 8 x T, round to nearest even (v_cvt_pk_bf16_f32 /
+// v_cvt_f16_f32).
+template <typename T = bf16>
+__device__ __forceinline__ vec8<T> pack8(float a0, float a1, float a2, float a3,
+                                         float a4, float a5, float a6, float a7) {
+  vec8<T> r = {(T)a0, (T)a1, (T)a2, (T)a3, (T)a4, (T)a5, (T)a6, (T)a7};
   return r;
 }
 
 // Slots 8h..8h+7 of a 32x32 result fragment as the next MFMA's operand.
-__device__ __forceinline__ bf16x8 frag_half(const f32x16& c, int h) {
-  return pack8(c[8 * h + 0], c[8 * h + 1], c[8 * h + 2], c[8 * h + 3],
-               c[8 * h + 4], c[8 * h + 5], c[8 * h + 6], c[8 * h + 7]);
+template <typename T = bf16>
+__device__ __forceinline__ vec8<T> frag_half(const f32x16& c, int h) {
+  return pack8<T>(c[8 * h + 0], c[8 * h + 1], c[8 * h + 2], c[8 * h + 3],
+                  c[8 * h + 4], c[8 * h + 5], c[8 * h + 6], c[8 * h + 7]);
 }
 
+template <typename T = bf16>
 __device__ __forceinline__ u32x2 pack4_bits(float a, float b, float c, float d) {
-  bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+  typename V16<T>::x4 v = {(T)a, (T)b, (T)c, (T)d};
   return __builtin_bit_cast(u32x2, v);
 }
 

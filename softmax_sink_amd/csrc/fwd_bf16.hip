@@ -1,4 +1,4 @@
-// Forward kernels, bf16 inputs, fp32 softmax state, for gfx950.
+// Forward kernels, bf16 or fp16 inputs (T), fp32 softmax state, for gfx950.
 //
 // Method: "slime: learnable_softmax_attention.py" (module docstring) defines
 // the probabilities as softmax over [scores, sink] with the sink column
@@ -13,7 +13,7 @@
 // Prefill kernel (one work item = 128 query rows of one (sequence, q-head)):
 // 4 waves x 32 rows. Per 64-key tile, K and V are staged HBM -> LDS
 // (double buffered, 16-byte coalesced loads, swizzled rows) and each wave
-// computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so that every lane
+// computes S^T = K Q^T with v_mfma_f32_32x32x16_{bf16,f16}, so that every lane
 // owns one query row: the row max needs one exchange with lane ^ 32, the
 // rescale factor is a per-lane scalar, and the probabilities are already the
 // B operand of O^T += V^T P^T (V^T read with ds_read_b64_tr_b16). Only tiles
@@ -34,7 +34,7 @@ namespace {
 using namespace dev;
 
 
-template <int D>
+template <int D, typename T>
 __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdArgs a) {
   constexpr int BN = kFwdBN;
   constexpr int NT = D / 16;            // K chunks of the QK^T product
@@ -60,16 +60,16 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdArgs a) {
 
   const int64_t qstride = (int64_t)a.hq * D;
   const int64_t kstride = (int64_t)a.hk * D;
-  const bf16* qp = static_cast<const bf16*>(a.q) + (int64_t)q0 * qstride + h * D;
-  const bf16* kp = static_cast<const bf16*>(a.k) + (int64_t)k0 * kstride + hk * D;
-  const bf16* vp = static_cast<const bf16*>(a.v) + (int64_t)k0 * kstride + hk * D;
+  const T* qp = static_cast<const T*>(a.q) + (int64_t)q0 * qstride + h * D;
+  const T* kp = static_cast<const T*>(a.k) + (int64_t)k0 * kstride + hk * D;
+  const T* vp = static_cast<const T*>(a.v) + (int64_t)k0 * kstride + hk * D;
 
   // Q as the B operand of S^T = K Q^T: lane (hl, c) holds Q[i][16t + 8hl .. +7]
-  bf16x8 qf[NT];
+  vec8<T> qf[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    if (i < lq) qf[t] = __builtin_bit_cast(bf16x8, ld16(qp + (int64_t)i * qstride + 16 * t + 8 * hl));
-    else qf[t] = bf16x8{};
+    if (i < lq) qf[t] = __builtin_bit_cast(vec8<T>, ld16(qp + (int64_t)i * qstride + 16 * t + 8 * hl));
+    else qf[t] = vec8<T>{};
   }
 
   const float sink = a.sinks ? a.sinks[h] : kNegInf;
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdArgs a) {
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        s[kb] = mfma32(lds_row_chunk<D>(kt_lds, kb * 32 + c, 2 * t + hl), qf[t], s[kb]);
+        s[kb] = mfma32(lds_row_chunk<D, T>(kt_lds, kb * 32 + c, 2 * t + hl), qf[t], s[kb]);
     }
 
     // mask (partial tiles only): key of slot r is kt*BN + 32kb + 8(r/4) + 4hl + r%4
@@ -132,16 +132,16 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdArgs a) {
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = half_max(mx);
     // The running max follows the exact row max, so the largest P of a row
-    // is exactly 1 in bf16 (few-key rows keep their accuracy); O and l are
+    // is exactly 1 in 16 bits (few-key rows keep their accuracy); O and l are
     // rescaled only when some lane's max moved.
     const float m_new = fmaxf(m, mx * c2);
     const bool move = m_new > m;
     const float m_use = m_new == kNegInf ? 0.f : m_new;
     const float alpha = exp2_hw(m - m_use);
     m = m_new;
-    // P (fp32 row sum, so that lse keeps fp32 accuracy; bf16 as the B
+    // P (fp32 row sum, so that lse keeps fp32 accuracy; 16-bit as the B
     // operand of the PV product)
-    bf16x8 pf[4];
+    vec8<T> pf[4];
     float psum = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdArgs a) {
         e[u] = exp2_hw(__builtin_fmaf(st[o8 + u], c2, -m_use));
         psum += e[u];
       }
-      pf[t] = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+      pf[t] = pack8<T>(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
     }
     if (__any(move)) {
       l *= alpha;
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdArgs a) {
     for (int t = 0; t < 4; ++t) {
 #pragma unroll
       for (int n = 0; n < NB; ++n)
-        o[n] = mfma32(lds_col_operand<D>(vt_lds, 16 * t, 32 * n), pf[t], o[n]);
+        o[n] = mfma32(lds_col_operand<D, T>(vt_lds, 16 * t, 32 * n), pf[t], o[n]);
     }
 
     wait_vmem();        // the next tile has landed in LDS
@@ -184,14 +184,14 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdArgs a) {
   const float lt = l + half_partner(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (i < lq) {
-    bf16* op = static_cast<bf16*>(a.out) + (int64_t)(q0 + i) * qstride + h * D;
+    T* op = static_cast<T*>(a.out) + (int64_t)(q0 + i) * qstride + h * D;
 #pragma unroll
     for (int n = 0; n < NB; ++n)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = 32 * n + 8 * g + 4 * hl;
         *reinterpret_cast<u32x2*>(op + d) =
-            pack4_bits(o[n][4 * g] * inv, o[n][4 * g + 1] * inv,
+            pack4_bits<T>(o[n][4 * g] * inv, o[n][4 * g + 1] * inv,
                        o[n][4 * g + 2] * inv, o[n][4 * g + 3] * inv);
       }
     if (hl == 0)
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdArgs a) {
 constexpr int kMaxItemPages = 132;  // pages a kDecChunk-key item can touch (block size >= 16)
 static_assert(kMaxItemPages >= 1 + (kDecChunk + 14) / 16, "page list too short");
 
-template <int D, bool PAGED>
+template <int D, typename T, bool PAGED>
 __global__ __launch_bounds__(256, 2) void fwd_split_kernel(FwdArgs a) {
   constexpr int BN = kDecBN;
   constexpr int NT = D / 16;
@@ -240,15 +240,15 @@ __global__ __launch_bounds__(256, 2) void fwd_split_kernel(FwdArgs a) {
 
   const int64_t qstride = (int64_t)a.hq * D;
   const int64_t kstride = (int64_t)a.hk * D;
-  const bf16* kp = static_cast<const bf16*>(a.k) + (int64_t)k0 * kstride + hk * D;
-  const bf16* vp = static_cast<const bf16*>(a.v) + (int64_t)k0 * kstride + hk * D;
+  const T* kp = static_cast<const T*>(a.k) + (int64_t)k0 * kstride + hk * D;
+  const T* vp = static_cast<const T*>(a.v) + (int64_t)k0 * kstride + hk * D;
 
-  bf16x8 qf[NT];
+  vec8<T> qf[NT];
   const bool live_row = r < rows;
-  const bf16* qrow = static_cast<const bf16*>(a.q) + (int64_t)(q0 + i) * qstride + h * D;
+  const T* qrow = static_cast<const T*>(a.q) + (int64_t)(q0 + i) * qstride + h * D;
 #pragma unroll
   for (int t = 0; t < NT; ++t)
-    qf[t] = live_row ? __builtin_bit_cast(bf16x8, ld16(qrow + 16 * t + 8 * hl)) : bf16x8{};
+    qf[t] = live_row ? __builtin_bit_cast(vec8<T>, ld16(qrow + 16 * t + 8 * hl)) : vec8<T>{};
 
   int jlo, jhi;
   row_key_range(i, lq, lk, a.causal, a.win_left, a.win_right, jlo, jhi);
@@ -278,9 +278,9 @@ __global__ __launch_bounds__(256, 2) void fwd_split_kernel(FwdArgs a) {
   // K and V rows [row0, row0 + BN) of the item into one LDS buffer
   auto load_kv = [&](int row0, char* dst) __attribute__((always_inline)) {
     if constexpr (PAGED) {
-      pl.load(static_cast<const bf16*>(a.k), (int64_t)hk * D, kstride, pages, off0, k_lo, row0,
+      pl.load(static_cast<const T*>(a.k), (int64_t)hk * D, kstride, pages, off0, k_lo, row0,
               k_hi - 1, a.page_size, a.page_magic, dst);
-      pl.load(static_cast<const bf16*>(a.v), (int64_t)hk * D, kstride, pages, off0, k_lo, row0,
+      pl.load(static_cast<const T*>(a.v), (int64_t)hk * D, kstride, pages, off0, k_lo, row0,
               k_hi - 1, a.page_size, a.page_magic, dst + TILE);
     } else {
       kl.load(kp, kstride, row0, k_hi, dst);
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(256, 2) void fwd_split_kernel(FwdArgs a) {
     f32x16 s = f32x16{};
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      bf16x8 kf = lds_row_chunk<D>(kt_lds, kh * 32 + c, 2 * t + hl);
+      vec8<T> kf = lds_row_chunk<D, T>(kt_lds, kh * 32 + c, 2 * t + hl);
       s = mfma32(kf, qf[t], s);
     }
 #pragma unroll
@@ -331,10 +331,10 @@ __global__ __launch_bounds__(256, 2) void fwd_split_kernel(FwdArgs a) {
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const bf16x8 pf = frag_half(s, t);
+      const vec8<T> pf = frag_half<T>(s, t);
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
-        const bf16x8 vf = lds_col_operand<D>(vt_lds, kh * 32 + 16 * t, 32 * n);
+        const vec8<T> vf = lds_col_operand<D, T>(vt_lds, kh * 32 + 16 * t, 32 * n);
         o[n] = mfma32(vf, pf, o[n]);
       }
     }
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(256, 2) void fwd_split_kernel(FwdArgs a) {
 
 // One wave per (token, q-head) row: merge the chunk partials of its sequence
 // by their maxima, add the sink once, normalise.
-template <int D>
+template <int D, typename T>
 __global__ __launch_bounds__(256) void fwd_combine_kernel(FwdArgs a) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -424,29 +424,29 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(FwdArgs a) {
     for (int e = 0; e < PER; ++e) acc[e] += po[e] * f;
   }
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  bf16* op = static_cast<bf16*>(a.out) + ((int64_t)t * a.hq + h) * D + lane * PER;
+  T* op = static_cast<T*>(a.out) + ((int64_t)t * a.hq + h) * D + lane * PER;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) op[e] = (bf16)(acc[e] * inv);
+  for (int e = 0; e < PER; ++e) op[e] = (T)(acc[e] * inv);
   if (lane == 0)
     a.lse[(int64_t)h * a.total_q + t] = lt > 0.f ? (mt + log2_hw(lt)) * kLn2 : kNegInf;
 }
 
-template <int D>
+template <int D, typename T>
 hipError_t launch_fwd_d(const FwdArgs& a, int mode, hipStream_t s, const TimingHook& th) {
   if (mode == kModeDecode) {
     if (th.start) hipEventRecord(th.start, s);
     if (a.n_items > 0) {
       if (a.block_table)
-        hipLaunchKernelGGL((fwd_split_kernel<D, true>), dim3(a.n_items * a.hk), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((fwd_split_kernel<D, T, true>), dim3(a.n_items * a.hk), dim3(256), 0, s, a);
       else
-        hipLaunchKernelGGL((fwd_split_kernel<D, false>), dim3(a.n_items * a.hk), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((fwd_split_kernel<D, T, false>), dim3(a.n_items * a.hk), dim3(256), 0, s, a);
     }
     if (th.stop) hipEventRecord(th.stop, s);
     const int rows = a.total_q * a.hq;
-    hipLaunchKernelGGL(fwd_combine_kernel<D>, dim3((rows + 3) / 4), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((fwd_combine_kernel<D, T>), dim3((rows + 3) / 4), dim3(256), 0, s, a);
   } else {
     if (th.start) hipEventRecord(th.start, s);
-    hipLaunchKernelGGL(fwd_prefill_kernel<D>, dim3(a.n_items * a.hq), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((fwd_prefill_kernel<D, T>), dim3(a.n_items * a.hq), dim3(256), 0, s, a);
     if (th.stop) hipEventRecord(th.stop, s);
   }
   return hipGetLastError();
@@ -454,10 +454,13 @@ hipError_t launch_fwd_d(const FwdArgs& a, int mode, hipStream_t s, const TimingH
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mode, hipStream_t s,
-                           const TimingHook& t) {
-  return head_dim == 128 ? launch_fwd_d<128>(a, mode, s, t)
-                         : launch_fwd_d<64>(a, mode, s, t);
+hipError_t launch_fwd_16(const FwdArgs& a, int head_dim, int dtype, int mode, hipStream_t s,
+                         const TimingHook& t) {
+  if (dtype == SINK_ATTN_FP16)
+    return head_dim == 128 ? launch_fwd_d<128, f16>(a, mode, s, t)
+                           : launch_fwd_d<64, f16>(a, mode, s, t);
+  return head_dim == 128 ? launch_fwd_d<128, bf16>(a, mode, s, t)
+                         : launch_fwd_d<64, bf16>(a, mode, s, t);
 }
 
 }  // namespace sinkattn

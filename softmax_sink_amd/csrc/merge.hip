@@ -32,9 +32,15 @@ __device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[4 + e] = b[e]; }
 }
-__device__ __forceinline__ void store8(bf16* p, const float (&x)[8]) {
+__device__ __forceinline__ void load8(const f16* p, float (&x)[8]) {
+  const f16x8 v = __builtin_bit_cast(f16x8, ld16(p));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
+}
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const float (&x)[8]) {
   *reinterpret_cast<u32x4*>(p) = __builtin_bit_cast(
-      u32x4, pack8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]));
+      u32x4, pack8<T>(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]));
 }
 __device__ __forceinline__ void store8(float* p, const float (&x)[8]) {
   *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
@@ -103,6 +109,8 @@ hipError_t launch_d(const MergeArgs& a, int out_dtype, hipStream_t s) {
   const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
   if (out_dtype == SINK_ATTN_BF16)
     hipLaunchKernelGGL((merge_kernel<D, TP, bf16>), grid, dim3(256), 0, s, a);
+  else if (out_dtype == SINK_ATTN_FP16)
+    hipLaunchKernelGGL((merge_kernel<D, TP, f16>), grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((merge_kernel<D, TP, float>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
@@ -118,9 +126,9 @@ hipError_t launch_tp(const MergeArgs& a, int head_dim, int out_dtype, hipStream_
 hipError_t launch_merge(const MergeArgs& a, int head_dim, int part_dtype, int out_dtype,
                         hipStream_t s, const TimingHook& t) {
   if (t.start) (void)hipEventRecord(t.start, s);
-  const hipError_t e = part_dtype == SINK_ATTN_BF16
-                           ? launch_tp<dev::bf16>(a, head_dim, out_dtype, s)
-                           : launch_tp<float>(a, head_dim, out_dtype, s);
+  const hipError_t e = part_dtype == SINK_ATTN_BF16   ? launch_tp<dev::bf16>(a, head_dim, out_dtype, s)
+                       : part_dtype == SINK_ATTN_FP16 ? launch_tp<dev::f16>(a, head_dim, out_dtype, s)
+                                                      : launch_tp<float>(a, head_dim, out_dtype, s);
   if (t.stop) (void)hipEventRecord(t.stop, s);
   return e;
 }

@@ -108,7 +108,9 @@ uint32_t fnv1a(const int32_t* a, int64_t n, uint32_t h) {
 FwdWorkspace fwd_workspace_layout(int64_t dec_rows, int head_dim, int dtype,
                                   int mode) {
   FwdWorkspace w{0, 0, 0, 0};
-  if (dtype != SINK_ATTN_BF16 || mode != kModeDecode) return w;
+  // the split-KV partials of the 16-bit (bf16, fp16) decode path; the fp32
+  // path has no split mode
+  if (dtype == SINK_ATTN_FP32 || mode != kModeDecode) return w;
   w.o_off = 0;
   w.m_off = align_up(dec_rows * head_dim * 4, 256);
   w.l_off = w.m_off + align_up(dec_rows * 4, 256);
@@ -137,7 +139,7 @@ sink_attn_status validate_problem(const sink_attn_problem* p) {
   if (p->causal != 0 && p->causal != 1) return SINK_ATTN_E_INVALID;
   if (p->win_left < -1 || p->win_right < -1) return SINK_ATTN_E_INVALID;
   if (p->causal && p->win_right > 0) return SINK_ATTN_E_INVALID;
-  if (p->dtype != SINK_ATTN_FP32 && p->dtype != SINK_ATTN_BF16)
+  if (p->dtype != SINK_ATTN_FP32 && p->dtype != SINK_ATTN_BF16 && p->dtype != SINK_ATTN_FP16)
     return SINK_ATTN_E_UNSUPPORTED;
   if (p->head_dim != 64 && p->head_dim != 128) return SINK_ATTN_E_UNSUPPORTED;
   // element offsets of the largest tensors must fit the kernels' 32-bit

@@ -152,10 +152,11 @@ struct TimingHook {
   hipEvent_t stop = nullptr;
 };
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mode,
-                           hipStream_t s, const TimingHook& t);
-hipError_t launch_bwd_bf16(const BwdArgs& a, int head_dim, hipStream_t s,
-                           const TimingHook& t);
+// 16-bit inputs (dtype SINK_ATTN_BF16 or SINK_ATTN_FP16), MFMA kernels
+hipError_t launch_fwd_16(const FwdArgs& a, int head_dim, int dtype, int mode,
+                         hipStream_t s, const TimingHook& t);
+hipError_t launch_bwd_16(const BwdArgs& a, int head_dim, int dtype, hipStream_t s,
+                         const TimingHook& t);
 hipError_t launch_fwd_f32(const FwdArgs& a, int head_dim, hipStream_t s,
                           const TimingHook& t);
 hipError_t launch_bwd_f32(const BwdArgs& a, int head_dim, hipStream_t s,

@@ -12,7 +12,7 @@ namespace dev {
 // format, no swizzle, no index stride.
 constexpr int kBufferWord3 = 0x00020000;
 
-// Copy a [64 x D] bf16 tile of a THD tensor (row stride `stride` elements)
+// Copy a [64 x D] tile of 16-bit elements of a THD tensor (row stride `stride` elements)
 // straight from global memory into a swizzled LDS tile with gfx950's
 // buffer_load_dwordx4 ... lds: no registers hold the data, so the next tile
 // can be in flight during a whole step of MFMA work. Each such instruction
@@ -59,13 +59,14 @@ struct TileDma {
   };
   // rows [row0, row0 + 64) of the tensor at `base` into `tile`; the caller
   // guarantees row0 < nrows
-  __device__ __forceinline__ Tile prepare(const bf16* base, int64_t stride, int row0, int nrows,
+  template <typename T>
+  __device__ __forceinline__ Tile prepare(const T* base, int64_t stride, int row0, int nrows,
                                           char* tile) const {
     Tile t;
     // raw buffer over the tile's first row; rows are clamped to lim, so the
     // range check (2 GiB) never trims a load
     t.rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16*>(base + (int64_t)row0 * stride), (short)0, 0x7FFFFFFF, kBufferWord3);
+        const_cast<T*>(base + (int64_t)row0 * stride), (short)0, 0x7FFFFFFF, kBufferWord3);
     t.lds = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(tile + wave_off));
     t.lim = nrows - row0 - 1;
@@ -88,7 +89,8 @@ struct TileDma {
           : "memory", "m0");
     }
   }
-  __device__ __forceinline__ void load(const bf16* base, int64_t stride, int row0, int nrows,
+  template <typename T>
+  __device__ __forceinline__ void load(const T* base, int64_t stride, int row0, int nrows,
                                        char* tile) const {
     issue<0, kPer>(prepare(base, stride, row0, nrows, tile));
   }
@@ -115,7 +117,8 @@ struct PagedTileDma {
     lcol = (((threadIdx.x % (D / 8)) ^ swz<D>(lrow)) * 16);
     wave_off = __builtin_amdgcn_readfirstlane((threadIdx.x / 64) * 1024);
   }
-  __device__ __forceinline__ void load(const bf16* cache, int64_t head_off, int64_t row_stride,
+  template <typename T>
+  __device__ __forceinline__ void load(const T* cache, int64_t head_off, int64_t row_stride,
                                        const int* pages, int off0, int k_lo, int row0,
                                        int row_last, int block_size, uint32_t magic,
                                        char* tile) const {

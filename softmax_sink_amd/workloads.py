@@ -7,9 +7,9 @@ produces, so it imports neither of them.
 Recipe (one numpy ``default_rng(seed)`` stream per problem; draw order:
 sequence lengths, q, k, v, dO, sinks):
 
-* values are drawn as fp32 N(0, 1); for bf16 problems they are rounded to
-  bf16 with round-to-nearest-even and kept as raw bf16 bit patterns
-  (``uint16``); ``as_f32`` widens them exactly;
+* values are drawn as fp32 N(0, 1); for bf16 (fp16) problems they are
+  rounded to bf16 (fp16) with round-to-nearest-even and kept as raw 16-bit
+  patterns (``uint16``); ``as_f32`` widens them exactly;
 * the softmax scale is the fp32 value of 1/sqrt(head_dim) unless given;
 * sink logits are fp32: drawn N(0, 1) per q-head ("learnable offset"), or a
   constant ln n for softmax_n problems.
@@ -51,21 +51,24 @@ def bf16_bits_to_f32(bits):
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def _normal(rng, n, bf16):
+def _normal(rng, n, bf16, fp16=False):
     """n draws of N(0,1) in fp32, drawn chunk by chunk (same stream as one
-    call), optionally rounded to bf16 bits."""
-    out = np.empty(n, dtype=np.uint16 if bf16 else np.float32)
+    call), optionally rounded to bf16 or fp16 bits."""
+    out = np.empty(n, dtype=np.uint16 if (bf16 or fp16) else np.float32)
     for a in range(0, n, _CHUNK):
         b = min(n, a + _CHUNK)
         x = rng.standard_normal(b - a, dtype=np.float32)
-        out[a:b] = round_to_bf16_bits(x) if bf16 else x
+        if fp16:
+            out[a:b] = x.astype(np.float16).view(np.uint16)     # IEEE round to nearest even
+        else:
+            out[a:b] = round_to_bf16_bits(x) if bf16 else x
     return out
 
 
 @dataclass
 class Problem:
     name: str
-    dtype: str                     # "bf16" or "fp32"
+    dtype: str                     # "bf16", "fp16" or "fp32"
     cu_q: np.ndarray               # int32 [B+1]
     cu_k: np.ndarray               # int32 [B+1]
     num_heads_q: int
@@ -106,7 +109,11 @@ class Problem:
     def as_f32(self, name):
         """Exact fp32 view of one of q, k, v, dout."""
         x = getattr(self, name)
-        return bf16_bits_to_f32(x) if self.dtype == "bf16" else x
+        if self.dtype == "bf16":
+            return bf16_bits_to_f32(x)
+        if self.dtype == "fp16":
+            return np.asarray(x, dtype=np.uint16).view(np.float16).astype(np.float32)
+        return x
 
     def sub_batch(self, seqs):
         """A new Problem holding only the listed sequences (same heads,
@@ -140,11 +147,12 @@ def make_problem(seed, lens_q, lens_k, num_heads_q, num_heads_k, head_dim,
     cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
     cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
     Tq, Tk = int(cu_q[-1]), int(cu_k[-1])
-    bf16 = dtype == "bf16"
-    q = _normal(rng, Tq * num_heads_q * head_dim, bf16).reshape(Tq, num_heads_q, head_dim)
-    k = _normal(rng, Tk * num_heads_k * head_dim, bf16).reshape(Tk, num_heads_k, head_dim)
-    v = _normal(rng, Tk * num_heads_k * head_dim, bf16).reshape(Tk, num_heads_k, head_dim)
-    dout = _normal(rng, Tq * num_heads_q * head_dim, bf16).reshape(Tq, num_heads_q, head_dim)
+    bf16, fp16 = dtype == "bf16", dtype == "fp16"
+    q = _normal(rng, Tq * num_heads_q * head_dim, bf16, fp16).reshape(Tq, num_heads_q, head_dim)
+    k = _normal(rng, Tk * num_heads_k * head_dim, bf16, fp16).reshape(Tk, num_heads_k, head_dim)
+    v = _normal(rng, Tk * num_heads_k * head_dim, bf16, fp16).reshape(Tk, num_heads_k, head_dim)
+    dout = _normal(rng, Tq * num_heads_q * head_dim, bf16, fp16).reshape(Tq, num_heads_q,
+                                                                        head_dim)
     if isinstance(sinks, str) and sinks == "normal":
         s = rng.standard_normal(num_heads_q, dtype=np.float32)
     elif np.isscalar(sinks):

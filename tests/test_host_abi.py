@@ -319,3 +319,24 @@ def test_merge_argument_checks():
     assert m(lse=None) == B.E_INVALID
     assert m(out=FAKE + 8) == B.E_INVALID
     assert m(pl=FAKE + 2) == B.E_INVALID
+
+
+def test_decode_workspace_sized_for_every_16bit_dtype():
+    # the split-KV partials (fp32 O, m, l per (row, q-head, chunk)) must be
+    # asked for whatever the 16-bit input type; the fp32 path has no split mode
+    cq = np.array([0, 3, 5], np.int32)
+    ck = np.array([0, 900, 3000], np.int32)
+    sizes = {}
+    for dt in (B.BF16, B.FP16, B.FP32):
+        p = B.make_problem(cq, ck, 8, 2, 128, True, dtype=dt)
+        meta, fws, _ = B.sink_attn_metadata(p, cq, ck)
+        sizes[dt] = fws
+        if dt != B.FP32:
+            rows = meta[W_DECROWS]
+            assert meta[W_MODE] == 1 and rows > 0 and fws >= rows * (128 + 2) * 4
+    assert sizes[B.BF16] == sizes[B.FP16] and sizes[B.FP32] == 0
+    # a paged fp16 table asks for the same
+    p = B.make_problem_paged(cq, np.diff(ck), 8, 2, 128, True, dtype=B.FP16)
+    table = np.arange(2 * 188, dtype=np.int32).reshape(2, 188)
+    _, fws = B.sink_attn_metadata_paged(p, B.PagedKV(16, 188, 2 * 188), cq, np.diff(ck), table)
+    assert fws == sizes[B.BF16]
