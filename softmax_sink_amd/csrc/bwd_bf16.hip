@@ -416,6 +416,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         s = mfma32(lds_row_chunk<D, T>(kt_lds, kb * 32 + c, 2 * t + hl), qf[t], s);
         dp = mfma32(lds_row_chunk<D, T>(vt_lds, kb * 32 + c, 2 * t + hl), gf[t], dp);
       }
+      sched_mfma_pipeline<2 * NT, 1, 1, 3>();
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = exp2_hw(__builtin_fmaf(s[r], c2, -lse2));
@@ -432,6 +433,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         for (int n = 0; n < NB; ++n)
           o[n] = mfma32(lds_col_operand<D, T>(kt_lds, 32 * kb + 16 * hh, 32 * n), sf, o[n]);
       }
+      sched_mfma_pipeline<2 * NB, 1, 2, 2>();
     }
     wait_vmem();        // the next tile has landed in LDS
     __syncthreads();

@@ -113,6 +113,7 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdArgs a) {
       for (int kb = 0; kb < 2; ++kb)
         s[kb] = mfma32(lds_row_chunk<D, T>(kt_lds, kb * 32 + c, 2 * t + hl), qf[t], s[kb]);
     }
+    sched_mfma_pipeline<2 * NT, 1, 1, 3>();
 
     // mask (partial tiles only): key of slot r is kt*BN + 32kb + 8(r/4) + 4hl + r%4
     if (kt < kf_lo || kt >= kf_hi) {
@@ -169,6 +170,7 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdArgs a) {
       for (int n = 0; n < NB; ++n)
         o[n] = mfma32(lds_col_operand<D, T>(vt_lds, 16 * t, 32 * n), pf[t], o[n]);
     }
+    sched_mfma_pipeline<4 * NB, 1, 2, 2>();
 
     wait_vmem();        // the next tile has landed in LDS
     __syncthreads();
