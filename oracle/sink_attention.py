@@ -79,6 +79,21 @@ def keep_mask(len_q, len_k, causal, win_left=-1, win_right=-1):
     return keep
 
 
+def keep_row(i, len_q, len_k, causal, win_left=-1, win_right=-1):
+    """Row i of keep_mask (the same rule, issue #108108 Proposal), without
+    building the [len_q, len_k] matrix -- for single rows of long sequences."""
+    j = np.arange(len_k)
+    pos = i + (len_k - len_q)
+    keep = np.ones(len_k, dtype=bool)
+    if causal:
+        keep &= j <= pos
+    if win_right >= 0:
+        keep &= j <= pos + win_right
+    if win_left >= 0:
+        keep &= j >= pos - win_left
+    return keep
+
+
 def keep_mask_top_left(len_q, len_k):
     """The older top-left causal alignment (issue #108108, Current Behavior).
     Only used by tests to show the two alignments differ when len_q != len_k."""
@@ -285,7 +300,7 @@ def sink_attention_rows(q, k, v, cu_q, cu_k, sinks, scale, causal,
         b = int(np.searchsorted(cu_q, t, side="right") - 1)
         q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
         i = t - q0
-        keep = keep_mask(q1 - q0, k1 - k0, causal, win_left, win_right)[i:i + 1]
+        keep = keep_row(i, q1 - q0, k1 - k0, causal, win_left, win_right)[None, :]
         hk = h // G
         Q = _f64(q[t:t + 1, h])
         K = _f64(k[k0:k1, hk])

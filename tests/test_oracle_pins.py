@@ -531,3 +531,15 @@ def test_merge_of_key_split_equals_unsplit_attention():
     parts = [part(pre, False), part(suf, True)]
     mo, ml = O.merge_partials([p[0] for p in parts], [p[1] for p in parts], sinks)
     assert np.allclose(mo, ref_o, rtol=0, atol=1e-12) and np.allclose(ml, ref_l, rtol=0, atol=1e-12)
+
+
+def test_keep_row_is_a_row_of_keep_mask():
+    """The single-row mask used for sampled rows of long sequences is the
+    same rule as the full mask, row for row, over causal / window cases
+    with Lq < Lk, Lq = Lk and Lq > Lk."""
+    for lq, lk in ((5, 9), (7, 7), (9, 4), (1, 13)):
+        for causal, wl, wr in ((True, -1, -1), (False, -1, -1), (True, 2, -1), (False, 3, 1),
+                               (False, 0, 0)):
+            full = O.keep_mask(lq, lk, causal, wl, wr)
+            for i in range(lq):
+                assert np.array_equal(O.keep_row(i, lq, lk, causal, wl, wr), full[i])
