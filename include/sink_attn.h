@@ -33,7 +33,8 @@
  *   dv_j = sum_i P_ij dO_i  (dk, dv summed over the q-heads of a group),
  *   dsink_h = -sum_i e^{s_h - lse_i} D_i.
  *
- * Layouts (all contiguous, row-major, base pointers 16-byte aligned):
+ * Layouts (all contiguous, row-major, base pointers 16-byte aligned). The
+ * packed TND layout of the sink_attn_fwd / _bwd / _fwd_paged calls:
  *   q, out, dout, dq : [total_q, num_heads_q, head_dim]  (dtype)
  *   k, v, dk, dv     : [total_k, num_heads_k, head_dim]  (dtype)
  *   lse              : [num_heads_q, total_q] fp32
@@ -41,6 +42,18 @@
  *   cu_seqlens_q/k   : [batch + 1] int32, first 0, non-decreasing,
  *                      last = total ("slime" wrapper docstring; CANN page,
  *                      SeqLengths parameter group)
+ * and the batch-padded layouts of the *_padded calls (CANN page, q, k, v
+ * validation and the layout matching table), with S_q = seq_q, S_k = seq_k:
+ *   BSND: q, dq [batch, S_q, num_heads_q, head_dim]; k, v, dk, dv
+ *         [batch, S_k, num_heads_k, head_dim]
+ *   BNSD: q, dq [batch, num_heads_q, S_q, head_dim]; k, v, dk, dv
+ *         [batch, num_heads_k, S_k, head_dim]
+ *   out, dout: layout_out (BSND or BNSD) of q's shape
+ *   lse  : [batch, num_heads_q, S_q] fp32
+ *   seqused_q / seqused_kv: [batch] int32, rows of sequence b in use
+ *         (0 <= used <= S; NULL: all S). Rows past them are padding: they
+ *         are never read, and out, lse, dq, dk, dv keep whatever they held
+ *         there.
  *
  * Ownership and threading. The library allocates nothing and keeps no state
  * between calls (except the one-shot timing events of sink_attn_arm_timing,
@@ -66,7 +79,7 @@
 extern "C" {
 #endif
 
-#define SINK_ATTN_ABI_VERSION 2
+#define SINK_ATTN_ABI_VERSION 3
 
 typedef enum {
   SINK_ATTN_OK = 0,
@@ -82,17 +95,28 @@ typedef enum {
  * validation); it runs the same MFMA kernels as bf16. */
 typedef enum { SINK_ATTN_FP32 = 0, SINK_ATTN_BF16 = 1, SINK_ATTN_FP16 = 2 } sink_attn_dtype;
 
+/* Tensor layouts (CANN page, layout matching table): k and v always share
+ * q's layout; out may differ from q only as BNSD q with BSND out. */
+typedef enum { SINK_ATTN_TND = 0, SINK_ATTN_BSND = 1, SINK_ATTN_BNSD = 2 } sink_attn_layout;
+
 /* The problem, passed by pointer and not retained. Checks: 0 < batch <
  * 65536; total_q, total_k, num_heads_q, num_heads_k > 0; num_heads_q %
  * num_heads_k == 0 (CANN page, axis validation); head_dim in {64, 128};
- * max_seqlen_q/k equal to the true maxima of the host cu_seqlens (the CANN
- * page leaves a mismatch undefined; here it is E_INVALID); causal in {0,1};
- * win_left, win_right >= -1; dtype a sink_attn_dtype. */
+ * max_seqlen_q/k equal to the true maxima of the host sequence lengths
+ * (cu_seqlens differences, or seqused / S in a padded layout; the CANN page
+ * leaves a mismatch undefined; here it is E_INVALID); causal in {0,1};
+ * win_left, win_right >= -1; dtype a sink_attn_dtype. Layout: layout_q a
+ * sink_attn_layout and layout_out equal to it, or BSND with BNSD q. TND
+ * has seq_q = seq_k = 0; a padded layout has seq_q, seq_k > 0, total_q =
+ * batch * seq_q and total_k = batch * seq_k (all rows, padding included).
+ * A zero-initialised tail (layout TND, seq 0) is the packed problem. */
 typedef struct {
   int32_t batch, num_heads_q, num_heads_k, head_dim;
   int32_t total_q, total_k, max_seqlen_q, max_seqlen_k;
   int32_t causal, win_left, win_right;
   int32_t dtype;
+  int32_t layout_q, layout_out;
+  int32_t seq_q, seq_k;
 } sink_attn_problem;
 
 /* Tile schedule ("CANN ops-transformer: flash_attn", Function section: a
@@ -110,9 +134,9 @@ typedef struct {
  * same per (sequence, key tile) for the backward; and split-KV items for
  * short query groups. Masked-out tiles are never visited. Copy the table
  * unchanged to device memory (meta_dev) for fwd/bwd.
- * Errors: E_INVALID (problem or cu_seqlens checks above, NULL pointers),
- * E_UNSUPPORTED, E_BUFFER_TOO_SMALL (meta_capacity_words < *meta_words; the
- * sizes are still written). */
+ * Errors: E_INVALID (problem or cu_seqlens checks above, NULL pointers, a
+ * padded layout), E_UNSUPPORTED, E_BUFFER_TOO_SMALL (meta_capacity_words <
+ * *meta_words; the sizes are still written). */
 sink_attn_status sink_attn_metadata(const sink_attn_problem* p,
                                     const int32_t* cu_seqlens_q_host,
                                     const int32_t* cu_seqlens_k_host,
@@ -217,6 +241,63 @@ sink_attn_status sink_attn_fwd_paged(const sink_attn_problem* p,
                                      void* out, float* lse, void* workspace,
                                      int64_t workspace_bytes,
                                      hipStream_t stream);
+
+/* Batch-padded layouts (BSND, BNSD; CANN page, q, k, v validation, the
+ * layout matching table and the SeqLengths parameter group): every
+ * sequence owns seq_q query rows and seq_k key rows of the tensors, of which
+ * the first seqused_q[b] / seqused_kv[b] are in use (all of them when the
+ * pointer is NULL). The method, the masks (bottom-right alignment over the
+ * used lengths) and the results on the used rows are those of the packed
+ * calls on the same sequences. cu_seqlens play no part.
+ *
+ * Metadata: as sink_attn_metadata, from the HOST copies of seqused_q /
+ * seqused_kv ([batch] int32 each, NULL = S for every sequence). Whether each
+ * pointer was NULL is recorded in the header; the device pointers passed to
+ * the calls below must match (E_META_MISMATCH). A table made here is for
+ * sink_attn_fwd_padded / sink_attn_bwd_padded only.
+ * Errors: E_INVALID (problem checks, a TND layout, used lengths outside
+ * [0, S]), E_UNSUPPORTED, E_BUFFER_TOO_SMALL. */
+sink_attn_status sink_attn_metadata_padded(const sink_attn_problem* p,
+                                           const int32_t* seqused_q_host,
+                                           const int32_t* seqused_kv_host,
+                                           int32_t* meta_host,
+                                           int64_t meta_capacity_words,
+                                           int64_t* meta_words,
+                                           int64_t* fwd_workspace_bytes,
+                                           int64_t* bwd_workspace_bytes);
+
+/* Forward over a padded layout. As sink_attn_fwd, with the device copies of
+ * seqused_q / seqused_kv (or NULL, as for the metadata) in place of
+ * cu_seqlens_q/k; tensors in the layouts above. Writes out and lse on the
+ * used rows only.
+ * Errors: as sink_attn_fwd. */
+sink_attn_status sink_attn_fwd_padded(const sink_attn_problem* p,
+                                      const int32_t* meta_host,
+                                      const int32_t* meta_dev,
+                                      const void* q, const void* k, const void* v,
+                                      const int32_t* seqused_q,
+                                      const int32_t* seqused_kv,
+                                      const float* sink_logits, float scale,
+                                      void* out, float* lse,
+                                      void* workspace, int64_t workspace_bytes,
+                                      hipStream_t stream);
+
+/* Backward over a padded layout. As sink_attn_bwd, with seqused_q /
+ * seqused_kv as for sink_attn_fwd_padded; dout has out's layout
+ * (layout_out), dq q's, dk and dv k's. Writes dq, dk, dv on the used rows
+ * only, and dsink. Deterministic.
+ * Errors: as sink_attn_bwd. */
+sink_attn_status sink_attn_bwd_padded(const sink_attn_problem* p,
+                                      const int32_t* meta_host,
+                                      const int32_t* meta_dev,
+                                      const void* dout, const void* q, const void* k,
+                                      const void* v, const void* out, const float* lse,
+                                      const int32_t* seqused_q,
+                                      const int32_t* seqused_kv,
+                                      const float* sink_logits, float scale,
+                                      void* dq, void* dk, void* dv, float* dsink,
+                                      void* workspace, int64_t workspace_bytes,
+                                      hipStream_t stream);
 
 /* Context-parallel merge. "CANN ops-transformer: flash_attn", Note on
  * softmax_lse: ring attention combines partial results through their lse.

@@ -3,11 +3,14 @@
 Argument marshalling only: every step of the computation runs in the
 library's HIP kernels; torch provides device memory and the stream. The
 functions ``sink_attn_metadata``, ``sink_attn_fwd``, ``sink_attn_bwd``,
-``sink_attn_metadata_paged``, ``sink_attn_fwd_paged``, ``sink_attn_merge``
-and ``sink_attn_arm_timing`` mirror the C entry points one to one. ``Plan``,
-``PagedPlan``, ``forward``, ``forward_paged``, ``backward``,
-``SinkAttnFunction`` and ``learnable_sink_attn_varlen`` are conveniences that
-allocate outputs and workspace with torch and call them.
+``sink_attn_metadata_paged``, ``sink_attn_fwd_paged``,
+``sink_attn_metadata_padded``, ``sink_attn_fwd_padded``,
+``sink_attn_bwd_padded``, ``sink_attn_merge`` and ``sink_attn_arm_timing``
+mirror the C entry points one to one. ``Plan``, ``PagedPlan``,
+``PaddedPlan``, ``forward``, ``forward_paged``, ``forward_padded``,
+``backward``, ``backward_padded``, ``SinkAttnFunction`` and
+``learnable_sink_attn_varlen`` are conveniences that allocate outputs and
+workspace with torch and call them.
 
 If the library has not been built the first call raises: there is no other
 path.
@@ -23,6 +26,8 @@ LIB_PATH = os.path.join(_HERE, "libsinkattn.so")
 
 OK, E_INVALID, E_UNSUPPORTED, E_META_MISMATCH, E_BUFFER_TOO_SMALL, E_HIP = range(6)
 FP32, BF16, FP16 = 0, 1, 2
+TND, BSND, BNSD = 0, 1, 2
+LAYOUTS = {"TND": TND, "BSND": BSND, "BNSD": BNSD}
 
 
 def dtype_code(dtype):
@@ -45,7 +50,8 @@ class Problem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "num_heads_q", "num_heads_k", "head_dim",
         "total_q", "total_k", "max_seqlen_q", "max_seqlen_k",
-        "causal", "win_left", "win_right", "dtype")]
+        "causal", "win_left", "win_right", "dtype",
+        "layout_q", "layout_out", "seq_q", "seq_k")]
 
 
 class PagedKV(ctypes.Structure):
@@ -84,6 +90,13 @@ def lib():
                                           vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp,
                                           vp, vp, ctypes.c_int64, vp]
         L.sink_attn_fwd_paged.restype = ctypes.c_int
+        L.sink_attn_metadata_padded.argtypes = [ctypes.POINTER(Problem), i32p, i32p, i32p,
+                                                ctypes.c_int64, i64p, i64p, i64p]
+        L.sink_attn_metadata_padded.restype = ctypes.c_int
+        L.sink_attn_fwd_padded.argtypes = L.sink_attn_fwd.argtypes
+        L.sink_attn_fwd_padded.restype = ctypes.c_int
+        L.sink_attn_bwd_padded.argtypes = L.sink_attn_bwd.argtypes
+        L.sink_attn_bwd_padded.restype = ctypes.c_int
         L.sink_attn_merge.argtypes = [ctypes.c_int32] * 6 + [vp, vp, vp, vp, vp, vp]
         L.sink_attn_merge.restype = ctypes.c_int
         L.sink_attn_arm_timing.argtypes = [vp, vp]
@@ -148,6 +161,42 @@ def sink_attn_metadata(problem, cu_seqlens_q_host, cu_seqlens_k_host):
     return meta, fws.value, bws.value
 
 
+def make_problem_padded(batch, seq_q, seq_k, seqused_q, seqused_kv, num_heads_q,
+                        num_heads_k, head_dim, causal, win_left=-1, win_right=-1,
+                        dtype=BF16, layout="BSND", layout_out=None):
+    """Problem struct for a batch-padded layout ("BSND" or "BNSD"; out
+    defaults to q's layout). seqused_q / seqused_kv: host int32 [batch] or
+    None (all rows in use)."""
+    lq = np.full(batch, seq_q) if seqused_q is None else np.asarray(seqused_q)
+    lk = np.full(batch, seq_k) if seqused_kv is None else np.asarray(seqused_kv)
+    lay = LAYOUTS[layout]
+    lay_out = lay if layout_out is None else LAYOUTS[layout_out]
+    return Problem(int(batch), num_heads_q, num_heads_k, head_dim,
+                   int(batch) * int(seq_q), int(batch) * int(seq_k),
+                   int(lq.max()) if len(lq) else 0, int(lk.max()) if len(lk) else 0,
+                   int(bool(causal)), int(win_left), int(win_right), int(dtype),
+                   lay, lay_out, int(seq_q), int(seq_k))
+
+
+def sink_attn_metadata_padded(problem, seqused_q_host, seqused_kv_host):
+    """-> (meta int32 array, fwd_workspace_bytes, bwd_workspace_bytes)."""
+    L = lib()
+    uq = None if seqused_q_host is None else np.ascontiguousarray(seqused_q_host, np.int32)
+    uk = None if seqused_kv_host is None else np.ascontiguousarray(seqused_kv_host, np.int32)
+    words, fws, bws = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    st = L.sink_attn_metadata_padded(ctypes.byref(problem), _i32p(uq), _i32p(uk), None, 0,
+                                     ctypes.byref(words), ctypes.byref(fws), ctypes.byref(bws))
+    if st != OK:
+        raise SinkAttnError(st, "sink_attn_metadata_padded")
+    meta = np.zeros(words.value, dtype=np.int32)
+    st = L.sink_attn_metadata_padded(ctypes.byref(problem), _i32p(uq), _i32p(uk), _i32p(meta),
+                                     words.value, ctypes.byref(words), ctypes.byref(fws),
+                                     ctypes.byref(bws))
+    if st != OK:
+        raise SinkAttnError(st, "sink_attn_metadata_padded")
+    return meta, fws.value, bws.value
+
+
 def make_problem_paged(cu_q, seqused_kv, num_heads_q, num_heads_k, head_dim, causal,
                        win_left=-1, win_right=-1, dtype=BF16):
     """Problem struct for a paged forward: key lengths from seqused_kv."""
@@ -207,6 +256,33 @@ def sink_attn_fwd_paged(problem, kv, meta_host, meta_dev, q, k_cache, v_cache, b
                                    _ptr(workspace), int(workspace_bytes), _stream(stream))
     if check and st != OK:
         raise SinkAttnError(st, "sink_attn_fwd_paged")
+    return st
+
+
+def sink_attn_fwd_padded(problem, meta_host, meta_dev, q, k, v, seqused_q, seqused_kv,
+                         sinks, scale, out, lse, workspace=None, workspace_bytes=0,
+                         stream=None, check=True):
+    st = lib().sink_attn_fwd_padded(ctypes.byref(problem), _i32p(meta_host), _ptr(meta_dev),
+                                    _ptr(q), _ptr(k), _ptr(v), _ptr(seqused_q),
+                                    _ptr(seqused_kv), _ptr(sinks), float(scale), _ptr(out),
+                                    _ptr(lse), _ptr(workspace), int(workspace_bytes),
+                                    _stream(stream))
+    if check and st != OK:
+        raise SinkAttnError(st, "sink_attn_fwd_padded")
+    return st
+
+
+def sink_attn_bwd_padded(problem, meta_host, meta_dev, dout, q, k, v, out, lse, seqused_q,
+                         seqused_kv, sinks, scale, dq, dk, dv, dsink, workspace=None,
+                         workspace_bytes=0, stream=None, check=True):
+    st = lib().sink_attn_bwd_padded(ctypes.byref(problem), _i32p(meta_host), _ptr(meta_dev),
+                                    _ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                    _ptr(lse), _ptr(seqused_q), _ptr(seqused_kv),
+                                    _ptr(sinks), float(scale), _ptr(dq), _ptr(dk), _ptr(dv),
+                                    _ptr(dsink), _ptr(workspace), int(workspace_bytes),
+                                    _stream(stream))
+    if check and st != OK:
+        raise SinkAttnError(st, "sink_attn_bwd_padded")
     return st
 
 
@@ -311,6 +387,38 @@ class PagedPlan:
         self.block_table = torch.from_numpy(self.block_table_host).to(device)
 
 
+class PaddedPlan:
+    """Metadata for one batch in a padded layout ("BSND" or "BNSD"):
+    seq_q / seq_k rows per sequence, of which seqused_q / seqused_kv (host
+    int32 [batch], or None for all) are in use."""
+
+    def __init__(self, batch, seq_q, seq_k, seqused_q, seqused_kv, num_heads_q,
+                 num_heads_k, head_dim, causal, window=(-1, -1), dtype="bf16",
+                 layout="BSND", layout_out=None, device="cuda"):
+        import torch
+        self.layout = layout
+        self.layout_out = layout_out or layout
+        self.used_q_host = None if seqused_q is None else np.asarray(seqused_q, np.int32)
+        self.used_k_host = None if seqused_kv is None else np.asarray(seqused_kv, np.int32)
+        self.problem = make_problem_padded(batch, seq_q, seq_k, self.used_q_host,
+                                           self.used_k_host, num_heads_q, num_heads_k,
+                                           head_dim, causal, window[0], window[1],
+                                           dtype_code(dtype), layout, layout_out)
+        self.meta, self.fwd_ws_bytes, self.bwd_ws_bytes = sink_attn_metadata_padded(
+            self.problem, self.used_q_host, self.used_k_host)
+        self.meta_dev = torch.from_numpy(self.meta).to(device)
+        self.used_q = (None if self.used_q_host is None
+                       else torch.from_numpy(self.used_q_host).to(device))
+        self.used_k = (None if self.used_k_host is None
+                       else torch.from_numpy(self.used_k_host).to(device))
+
+    def out_shape(self):
+        p = self.problem
+        if self.layout_out == "BNSD":
+            return (p.batch, p.num_heads_q, p.seq_q, p.head_dim)
+        return (p.batch, p.seq_q, p.num_heads_q, p.head_dim)
+
+
 def _workspace(nbytes, device):
     import torch
     if nbytes == 0:
@@ -342,6 +450,39 @@ def forward_paged(plan, q, k_cache, v_cache, sinks, scale):
                         plan.block_table, plan.cu_q, plan.seqused, sinks, scale, out, lse,
                         ws, plan.fwd_ws_bytes)
     return out, lse
+
+
+def forward_padded(plan, q, k, v, sinks, scale, out=None, lse=None):
+    """Padded-layout forward -> out (plan.layout_out), lse [B, Hq, S_q] fp32.
+    Rows past the used lengths keep what `out` / `lse` held (fresh, they are
+    uninitialised)."""
+    import torch
+    p = plan.problem
+    if out is None:
+        out = torch.empty(plan.out_shape(), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty(p.batch, p.num_heads_q, p.seq_q, dtype=torch.float32,
+                          device=q.device)
+    ws = _workspace(plan.fwd_ws_bytes, q.device)
+    sink_attn_fwd_padded(p, plan.meta, plan.meta_dev, q, k, v, plan.used_q, plan.used_k,
+                         sinks, scale, out, lse, ws, plan.fwd_ws_bytes)
+    return out, lse
+
+
+def backward_padded(plan, dout, q, k, v, out, lse, sinks, scale, dq=None, dk=None, dv=None):
+    """Padded-layout backward -> dq, dk, dv, dsink (rows past the used
+    lengths keep what dq / dk / dv held)."""
+    import torch
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    dsink = (torch.empty(plan.problem.num_heads_q, dtype=torch.float32, device=q.device)
+             if sinks is not None else None)
+    ws = _workspace(plan.bwd_ws_bytes, q.device)
+    sink_attn_bwd_padded(plan.problem, plan.meta, plan.meta_dev, dout, q, k, v, out, lse,
+                         plan.used_q, plan.used_k, sinks, scale, dq, dk, dv, dsink, ws,
+                         plan.bwd_ws_bytes)
+    return dq, dk, dv, dsink
 
 
 def backward(plan, dout, q, k, v, out, lse, sinks, scale):

@@ -40,10 +40,12 @@ sink_attn_status common_checks(const sink_attn_problem* p,
 
 FwdArgs fwd_args(const sink_attn_problem* p, const void* q, const void* k,
                  const void* v, const int32_t* cu_q, const int32_t* cu_k,
+                 const int32_t* used_q, const int32_t* used_k,
                  const float* sinks, float scale, void* out, float* lse) {
   FwdArgs a{};
   a.q = q; a.k = k; a.v = v;
   a.cu_q = cu_q; a.cu_k = cu_k;
+  a.g = make_geometry(*p, used_q, used_k);
   a.sinks = sinks;
   a.out = out; a.lse = lse;
   a.batch = p->batch; a.hq = p->num_heads_q; a.hk = p->num_heads_k;
@@ -73,6 +75,95 @@ bool decode_args(FwdArgs& a, const sink_attn_problem* p, const int32_t* meta_hos
   return true;
 }
 
+// The packed calls take TND problems with cu_seqlens; the padded calls take
+// BSND / BNSD problems whose seqused pointers are null exactly where they
+// were for the metadata. Called after common_checks.
+sink_attn_status check_family(const sink_attn_problem* p, const int32_t* meta_host,
+                              bool padded, const int32_t* used_q, const int32_t* used_k) {
+  if ((p->layout_q != SINK_ATTN_TND) != padded) return SINK_ATTN_E_INVALID;
+  const int mask = (used_q ? 1 : 0) | (used_k ? 2 : 0);
+  if (meta_host[kUsedMask] != mask) return SINK_ATTN_E_META_MISMATCH;
+  return SINK_ATTN_OK;
+}
+
+sink_attn_status fwd_impl(const sink_attn_problem* p, const int32_t* meta_host,
+                          const int32_t* meta_dev, const void* q, const void* k,
+                          const void* v, const int32_t* cu_q, const int32_t* cu_k,
+                          const int32_t* used_q, const int32_t* used_k,
+                          const float* sink_logits, float scale, void* out, float* lse,
+                          void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !out || !lse) return SINK_ATTN_E_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      !aligned16(lse))
+    return SINK_ATTN_E_INVALID;
+  const int64_t need = header_i64(meta_host, kFwdWsLo, kFwdWsHi);
+  if (workspace_bytes < need) return SINK_ATTN_E_BUFFER_TOO_SMALL;
+  if (need > 0 && (!workspace || !aligned16(workspace))) return SINK_ATTN_E_INVALID;
+
+  const int mode = meta_host[kMode];
+  FwdArgs a = fwd_args(p, q, k, v, cu_q, cu_k, used_q, used_k, sink_logits, scale, out, lse);
+  const TimingHook t = take_timing();
+  hipError_t e;
+  if (p->dtype == SINK_ATTN_FP32) {
+    e = launch_fwd_f32(a, p->head_dim, stream, t);
+  } else if (mode == kModeDecode) {
+    if (!decode_args(a, p, meta_host, meta_dev, workspace)) return SINK_ATTN_E_META_MISMATCH;
+    e = launch_fwd_16(a, p->head_dim, p->dtype, mode, stream, t);
+  } else {
+    a.items = meta_dev + meta_host[kFwdOff];
+    a.n_items = meta_host[kNFwd];
+    e = launch_fwd_16(a, p->head_dim, p->dtype, mode, stream, t);
+  }
+  return e == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_E_HIP;
+}
+
+sink_attn_status bwd_impl(const sink_attn_problem* p, const int32_t* meta_host,
+                          const int32_t* meta_dev, const void* dout, const void* q,
+                          const void* k, const void* v, const void* out, const float* lse,
+                          const int32_t* cu_q, const int32_t* cu_k,
+                          const int32_t* used_q, const int32_t* used_k,
+                          const float* sink_logits, float scale, void* dq, void* dk,
+                          void* dv, float* dsink, void* workspace,
+                          int64_t workspace_bytes, hipStream_t stream) {
+  if (!dout || !q || !k || !v || !out || !lse || !dq || !dk || !dv)
+    return SINK_ATTN_E_INVALID;
+  if ((sink_logits == nullptr) != (dsink == nullptr)) return SINK_ATTN_E_INVALID;
+  if (!aligned16(dout) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
+      !aligned16(out) || !aligned16(lse) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv))
+    return SINK_ATTN_E_INVALID;
+  const int64_t need = header_i64(meta_host, kBwdWsLo, kBwdWsHi);
+  if (workspace_bytes < need) return SINK_ATTN_E_BUFFER_TOO_SMALL;
+  if (need > 0 && (!workspace || !aligned16(workspace))) return SINK_ATTN_E_INVALID;
+
+  const int64_t pre_blocks = meta_host[kBwdPreBlocks];
+  const BwdWorkspace w = bwd_workspace_layout(p->total_q, p->num_heads_q,
+                                              p->head_dim, p->dtype, pre_blocks);
+  char* base = static_cast<char*>(workspace);
+  BwdArgs a{};
+  a.dout = dout; a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
+  a.cu_q = cu_q; a.cu_k = cu_k; a.sinks = sink_logits;
+  a.g = make_geometry(*p, used_q, used_k);
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dsink = dsink;
+  a.items = meta_dev + meta_host[kBwdOff];
+  a.n_items = meta_host[kNBwd];
+  a.items_q = meta_dev + meta_host[kFwdOff];
+  a.n_items_q = meta_host[kNFwd];
+  a.pre_blocks = static_cast<int>(pre_blocks);
+  a.dval = reinterpret_cast<float*>(base + w.dval_off);
+  a.part = reinterpret_cast<float*>(base + w.part_off);
+  a.batch = p->batch; a.hq = p->num_heads_q; a.hk = p->num_heads_k;
+  a.group = p->num_heads_q / p->num_heads_k;
+  a.causal = p->causal; a.win_left = p->win_left; a.win_right = p->win_right;
+  a.total_q = p->total_q; a.total_k = p->total_k;
+  a.scale = scale;
+  const TimingHook t = take_timing();
+  hipError_t e = p->dtype == SINK_ATTN_FP32
+                     ? launch_bwd_f32(a, p->head_dim, stream, t)
+                     : launch_bwd_16(a, p->head_dim, p->dtype, stream, t);
+  return e == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_E_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -89,10 +180,35 @@ sink_attn_status sink_attn_metadata(const sink_attn_problem* p,
   if (st != SINK_ATTN_OK) return st;
   if (!meta_words || !fwd_workspace_bytes || !bwd_workspace_bytes)
     return SINK_ATTN_E_INVALID;
+  if (p->layout_q != SINK_ATTN_TND) return SINK_ATTN_E_INVALID;
   st = validate_cu_seqlens(*p, cu_seqlens_q_host, cu_seqlens_k_host);
   if (st != SINK_ATTN_OK) return st;
   if (meta_host && meta_capacity_words < 0) return SINK_ATTN_E_INVALID;
-  return build_metadata(*p, cu_seqlens_q_host, cu_seqlens_k_host, nullptr, meta_host,
+  return build_metadata(*p, cu_seqlens_q_host, cu_seqlens_k_host, nullptr, 0, meta_host,
+                        meta_capacity_words, meta_words, fwd_workspace_bytes,
+                        bwd_workspace_bytes);
+}
+
+sink_attn_status sink_attn_metadata_padded(const sink_attn_problem* p,
+                                           const int32_t* seqused_q_host,
+                                           const int32_t* seqused_kv_host,
+                                           int32_t* meta_host,
+                                           int64_t meta_capacity_words,
+                                           int64_t* meta_words,
+                                           int64_t* fwd_workspace_bytes,
+                                           int64_t* bwd_workspace_bytes) {
+  sink_attn_status st = validate_problem(p);
+  if (st != SINK_ATTN_OK) return st;
+  if (!meta_words || !fwd_workspace_bytes || !bwd_workspace_bytes)
+    return SINK_ATTN_E_INVALID;
+  if (p->layout_q == SINK_ATTN_TND) return SINK_ATTN_E_INVALID;
+  std::vector<int32_t> cu_q(static_cast<size_t>(p->batch) + 1);
+  std::vector<int32_t> cu_k(static_cast<size_t>(p->batch) + 1);
+  st = validate_seqused(*p, seqused_q_host, seqused_kv_host, cu_q.data(), cu_k.data());
+  if (st != SINK_ATTN_OK) return st;
+  if (meta_host && meta_capacity_words < 0) return SINK_ATTN_E_INVALID;
+  const int mask = (seqused_q_host ? 1 : 0) | (seqused_kv_host ? 2 : 0);
+  return build_metadata(*p, cu_q.data(), cu_k.data(), nullptr, mask, meta_host,
                         meta_capacity_words, meta_words, fwd_workspace_bytes,
                         bwd_workspace_bytes);
 }
@@ -109,6 +225,7 @@ sink_attn_status sink_attn_metadata_paged(const sink_attn_problem* p,
   sink_attn_status st = validate_problem(p);
   if (st != SINK_ATTN_OK) return st;
   if (!meta_words || !fwd_workspace_bytes) return SINK_ATTN_E_INVALID;
+  if (p->layout_q != SINK_ATTN_TND) return SINK_ATTN_E_INVALID;
   std::vector<int32_t> cu_k(static_cast<size_t>(p->batch) + 1);
   st = validate_paged(*p, kv, seqused_kv_host, block_table_host, cu_k.data());
   if (st != SINK_ATTN_OK) return st;
@@ -120,7 +237,7 @@ sink_attn_status sink_attn_metadata_paged(const sink_attn_problem* p,
   if (meta_host && meta_capacity_words < 0) return SINK_ATTN_E_INVALID;
   const PagedInfo info{*kv, block_table_host};
   int64_t bwd_bytes = 0;
-  return build_metadata(*p, cu_seqlens_q_host, cu_k.data(), &info, meta_host,
+  return build_metadata(*p, cu_seqlens_q_host, cu_k.data(), &info, 0, meta_host,
                         meta_capacity_words, meta_words, fwd_workspace_bytes, &bwd_bytes);
 }
 
@@ -135,30 +252,28 @@ sink_attn_status sink_attn_fwd(const sink_attn_problem* p,
                                int64_t workspace_bytes, hipStream_t stream) {
   sink_attn_status st = common_checks(p, meta_host, meta_dev, scale);
   if (st != SINK_ATTN_OK) return st;
-  if (!q || !k || !v || !out || !lse || !cu_seqlens_q || !cu_seqlens_k)
-    return SINK_ATTN_E_INVALID;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
-      !aligned16(lse))
-    return SINK_ATTN_E_INVALID;
-  const int64_t need = header_i64(meta_host, kFwdWsLo, kFwdWsHi);
-  if (workspace_bytes < need) return SINK_ATTN_E_BUFFER_TOO_SMALL;
-  if (need > 0 && (!workspace || !aligned16(workspace))) return SINK_ATTN_E_INVALID;
+  st = check_family(p, meta_host, false, nullptr, nullptr);
+  if (st != SINK_ATTN_OK) return st;
+  if (!cu_seqlens_q || !cu_seqlens_k) return SINK_ATTN_E_INVALID;
+  return fwd_impl(p, meta_host, meta_dev, q, k, v, cu_seqlens_q, cu_seqlens_k, nullptr,
+                  nullptr, sink_logits, scale, out, lse, workspace, workspace_bytes, stream);
+}
 
-  const int mode = meta_host[kMode];
-  FwdArgs a = fwd_args(p, q, k, v, cu_seqlens_q, cu_seqlens_k, sink_logits, scale, out, lse);
-  const TimingHook t = take_timing();
-  hipError_t e;
-  if (p->dtype == SINK_ATTN_FP32) {
-    e = launch_fwd_f32(a, p->head_dim, stream, t);
-  } else if (mode == kModeDecode) {
-    if (!decode_args(a, p, meta_host, meta_dev, workspace)) return SINK_ATTN_E_META_MISMATCH;
-    e = launch_fwd_16(a, p->head_dim, p->dtype, mode, stream, t);
-  } else {
-    a.items = meta_dev + meta_host[kFwdOff];
-    a.n_items = meta_host[kNFwd];
-    e = launch_fwd_16(a, p->head_dim, p->dtype, mode, stream, t);
-  }
-  return e == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_E_HIP;
+sink_attn_status sink_attn_fwd_padded(const sink_attn_problem* p,
+                                      const int32_t* meta_host,
+                                      const int32_t* meta_dev, const void* q,
+                                      const void* k, const void* v,
+                                      const int32_t* seqused_q,
+                                      const int32_t* seqused_kv,
+                                      const float* sink_logits, float scale,
+                                      void* out, float* lse, void* workspace,
+                                      int64_t workspace_bytes, hipStream_t stream) {
+  sink_attn_status st = common_checks(p, meta_host, meta_dev, scale);
+  if (st != SINK_ATTN_OK) return st;
+  st = check_family(p, meta_host, true, seqused_q, seqused_kv);
+  if (st != SINK_ATTN_OK) return st;
+  return fwd_impl(p, meta_host, meta_dev, q, k, v, nullptr, nullptr, seqused_q, seqused_kv,
+                  sink_logits, scale, out, lse, workspace, workspace_bytes, stream);
 }
 
 sink_attn_status sink_attn_fwd_paged(const sink_attn_problem* p,
@@ -176,6 +291,8 @@ sink_attn_status sink_attn_fwd_paged(const sink_attn_problem* p,
   if (!kv) return SINK_ATTN_E_INVALID;
   sink_attn_status st = common_checks(p, meta_host, meta_dev, scale, kv);
   if (st != SINK_ATTN_OK) return st;
+  st = check_family(p, meta_host, false, nullptr, nullptr);
+  if (st != SINK_ATTN_OK) return st;
   if (!q || !k_cache || !v_cache || !block_table || !out || !lse || !cu_seqlens_q ||
       !seqused_kv)
     return SINK_ATTN_E_INVALID;
@@ -187,8 +304,8 @@ sink_attn_status sink_attn_fwd_paged(const sink_attn_problem* p,
   if (need > 0 && (!workspace || !aligned16(workspace))) return SINK_ATTN_E_INVALID;
   if (meta_host[kMode] != kModeDecode) return SINK_ATTN_E_UNSUPPORTED;
 
-  FwdArgs a = fwd_args(p, q, k_cache, v_cache, cu_seqlens_q, nullptr, sink_logits, scale,
-                       out, lse);
+  FwdArgs a = fwd_args(p, q, k_cache, v_cache, cu_seqlens_q, nullptr, nullptr, nullptr,
+                       sink_logits, scale, out, lse);
   if (!decode_args(a, p, meta_host, meta_dev, workspace)) return SINK_ATTN_E_META_MISMATCH;
   a.block_table = block_table;
   a.seqused_k = seqused_kv;
@@ -214,43 +331,32 @@ sink_attn_status sink_attn_bwd(const sink_attn_problem* p,
                                hipStream_t stream) {
   sink_attn_status st = common_checks(p, meta_host, meta_dev, scale);
   if (st != SINK_ATTN_OK) return st;
-  if (!dout || !q || !k || !v || !out || !lse || !cu_seqlens_q ||
-      !cu_seqlens_k || !dq || !dk || !dv)
-    return SINK_ATTN_E_INVALID;
-  if ((sink_logits == nullptr) != (dsink == nullptr)) return SINK_ATTN_E_INVALID;
-  if (!aligned16(dout) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
-      !aligned16(out) || !aligned16(lse) || !aligned16(dq) || !aligned16(dk) ||
-      !aligned16(dv))
-    return SINK_ATTN_E_INVALID;
-  const int64_t need = header_i64(meta_host, kBwdWsLo, kBwdWsHi);
-  if (workspace_bytes < need) return SINK_ATTN_E_BUFFER_TOO_SMALL;
-  if (need > 0 && (!workspace || !aligned16(workspace))) return SINK_ATTN_E_INVALID;
+  st = check_family(p, meta_host, false, nullptr, nullptr);
+  if (st != SINK_ATTN_OK) return st;
+  if (!cu_seqlens_q || !cu_seqlens_k) return SINK_ATTN_E_INVALID;
+  return bwd_impl(p, meta_host, meta_dev, dout, q, k, v, out, lse, cu_seqlens_q,
+                  cu_seqlens_k, nullptr, nullptr, sink_logits, scale, dq, dk, dv, dsink,
+                  workspace, workspace_bytes, stream);
+}
 
-  const int64_t pre_blocks = meta_host[kBwdPreBlocks];
-  const BwdWorkspace w = bwd_workspace_layout(p->total_q, p->num_heads_q,
-                                              p->head_dim, p->dtype, pre_blocks);
-  char* base = static_cast<char*>(workspace);
-  BwdArgs a{};
-  a.dout = dout; a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
-  a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k; a.sinks = sink_logits;
-  a.dq = dq; a.dk = dk; a.dv = dv; a.dsink = dsink;
-  a.items = meta_dev + meta_host[kBwdOff];
-  a.n_items = meta_host[kNBwd];
-  a.items_q = meta_dev + meta_host[kFwdOff];
-  a.n_items_q = meta_host[kNFwd];
-  a.pre_blocks = static_cast<int>(pre_blocks);
-  a.dval = reinterpret_cast<float*>(base + w.dval_off);
-  a.part = reinterpret_cast<float*>(base + w.part_off);
-  a.batch = p->batch; a.hq = p->num_heads_q; a.hk = p->num_heads_k;
-  a.group = p->num_heads_q / p->num_heads_k;
-  a.causal = p->causal; a.win_left = p->win_left; a.win_right = p->win_right;
-  a.total_q = p->total_q; a.total_k = p->total_k;
-  a.scale = scale;
-  const TimingHook t = take_timing();
-  hipError_t e = p->dtype == SINK_ATTN_FP32
-                     ? launch_bwd_f32(a, p->head_dim, stream, t)
-                     : launch_bwd_16(a, p->head_dim, p->dtype, stream, t);
-  return e == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_E_HIP;
+sink_attn_status sink_attn_bwd_padded(const sink_attn_problem* p,
+                                      const int32_t* meta_host,
+                                      const int32_t* meta_dev, const void* dout,
+                                      const void* q, const void* k, const void* v,
+                                      const void* out, const float* lse,
+                                      const int32_t* seqused_q,
+                                      const int32_t* seqused_kv,
+                                      const float* sink_logits, float scale, void* dq,
+                                      void* dk, void* dv, float* dsink,
+                                      void* workspace, int64_t workspace_bytes,
+                                      hipStream_t stream) {
+  sink_attn_status st = common_checks(p, meta_host, meta_dev, scale);
+  if (st != SINK_ATTN_OK) return st;
+  st = check_family(p, meta_host, true, seqused_q, seqused_kv);
+  if (st != SINK_ATTN_OK) return st;
+  return bwd_impl(p, meta_host, meta_dev, dout, q, k, v, out, lse, nullptr, nullptr,
+                  seqused_q, seqused_kv, sink_logits, scale, dq, dk, dv, dsink, workspace,
+                  workspace_bytes, stream);
 }
 
 sink_attn_status sink_attn_merge(int32_t num_parts, int32_t total_q,

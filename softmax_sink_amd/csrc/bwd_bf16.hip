@@ -85,8 +85,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int* itw = a.items + item * kItemWords;
   const int b = itw[0], kt = itw[1], qt_lo = itw[2], qt_hi = itw[3];
   const int qf_lo = itw[4], qf_hi = itw[5];
-  const int q0 = a.cu_q[b], lq = a.cu_q[b + 1] - q0;
-  const int k0 = a.cu_k[b], lk = a.cu_k[b + 1] - k0;
+  const int q0 = q_start(a, b), lq = q_len(a, b);
+  const int k0 = k_start(a, b), lk = k_len(a, b);
   const int G = a.group;
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -94,10 +94,11 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int hl = lane >> 5, c = lane & 31;
   const int jbase = kt * kBwdBN + 64 * kh + c;   // this lane's key in block kb: jbase + 32 kb
 
-  const int64_t kstride = (int64_t)a.hk * D;
-  const int64_t qstride = (int64_t)a.hq * D;
+  const int64_t kstride = a.g.k_row;
+  const int64_t qstride = a.g.q_row;
+  const int64_t koff = (int64_t)k0 * a.g.k_seq + hk * a.g.k_head;   // key row 0 of k / v / dk / dv
   // role 0 holds K rows (B operand of S = Q K^T), role 1 V rows (of dP = dO V^T)
-  const T* fp = static_cast<const T*>(role == 0 ? a.k : a.v) + (int64_t)k0 * kstride + hk * D;
+  const T* fp = static_cast<const T*>(role == 0 ? a.k : a.v) + koff;
   vec8<T> frag[2][NT];
   int ilo[2], ihi[2];
 #pragma unroll
@@ -116,9 +117,14 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int nq = qt_hi - qt_lo;
   const int steps = nq * G;
   const float c2 = a.scale * kLog2e;
-  const T* qg = static_cast<const T*>(a.q) + (int64_t)q0 * qstride + (int64_t)hk * G * D;
-  const T* dg = static_cast<const T*>(a.dout) + (int64_t)q0 * qstride + (int64_t)hk * G * D;
-  const int64_t rbase = ((int64_t)hk * G) * a.total_q + q0;   // lse / D row of (g = 0, row 0)
+  const int64_t qoff = (int64_t)q0 * a.g.q_seq + (int64_t)hk * G * a.g.q_head;
+  const T* qg = static_cast<const T*>(a.q) + qoff;     // row 0 of q-head hk*G
+  const T* dg = static_cast<const T*>(a.dout) + (int64_t)q0 * a.g.o_seq +
+                (int64_t)hk * G * a.g.o_head;   // row 0 of dO of q-head hk*G
+  // lse of (q-head hk*G + g, row r): lbase + g*l_head + r*l_row; D (the
+  // workspace, [Hq, rows]): rbase + g*total_q + r
+  const int64_t lbase = (int64_t)q0 * a.g.l_seq + (int64_t)hk * G * a.g.l_head;
+  const int64_t rbase = ((int64_t)hk * G) * a.total_q + q0;
 
   TileDma<D, kKvThreads> dma;
   dma.init();
@@ -131,7 +137,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     dma.load(qg, qstride, qt_lo * kBwdBM, lq, smem + S::off_q);
     if (threadIdx.x < kBwdBM) {
       const int row = qt_lo * kBwdBM + threadIdx.x;
-      const float l = a.lse[rbase + min(row, lq - 1)];
+      const float l = a.lse[lbase + (int64_t)min(row, lq - 1) * a.g.l_row];
       reinterpret_cast<float*>(smem + S::off_lse)[threadIdx.x] =
           (row >= lq || l == kNegInf) ? __builtin_huge_valf() : l * kLog2e;
     }
@@ -150,16 +156,18 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   auto prefetch = [&](int it, int qs_next, int ds) __attribute__((always_inline)) {
     if (it + 1 < steps) {
       const int qt = qt_lo + sq.t;
-      dma.load(qg + sq.g * D, qstride, qt * kBwdBM, lq, smem + S::off_q + qs_next * S::kTile);
+      dma.load(qg + sq.g * a.g.q_head, qstride, qt * kBwdBM, lq,
+               smem + S::off_q + qs_next * S::kTile);
       if (threadIdx.x < kBwdBM) {
         const int row = qt * kBwdBM + threadIdx.x;
         lse_live = row < lq;
-        lse_raw = a.lse[rbase + (int64_t)sq.g * a.total_q + min(row, lq - 1)];
+        lse_raw = a.lse[lbase + (int64_t)sq.g * a.g.l_head + (int64_t)min(row, lq - 1) * a.g.l_row];
       }
     }
     if (it < steps) {
       const int qt = qt_lo + sd.t;
-      dma.load(dg + sd.g * D, qstride, qt * kBwdBM, lq, smem + S::off_do + ds * S::kTile);
+      dma.load(dg + sd.g * a.g.o_head, a.g.o_row, qt * kBwdBM, lq,
+               smem + S::off_do + ds * S::kTile);
       if (threadIdx.x < kBwdBM) {
         const int row = qt * kBwdBM + threadIdx.x;
         dval_live = row < lq;
@@ -316,7 +324,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   for (int kb = 0; kb < 2; ++kb) {
     const int j = jbase + 32 * kb;
     if (j < lk) {
-      T* dst = static_cast<T*>(role == 0 ? a.dv : a.dk) + (int64_t)(k0 + j) * kstride + hk * D;
+      T* dst = static_cast<T*>(role == 0 ? a.dv : a.dk) + koff + (int64_t)j * kstride;
 #pragma unroll
       for (int db = 0; db < NB; ++db)
 #pragma unroll
@@ -347,27 +355,27 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int* it = a.items_q + item * kItemWords;
   const int b = it[0], qt = it[1], kt_lo = it[2], kt_hi = it[3];
   const int kf_lo = it[4], kf_hi = it[5];
-  const int q0 = a.cu_q[b], lq = a.cu_q[b + 1] - q0;
-  const int k0 = a.cu_k[b], lk = a.cu_k[b + 1] - k0;
+  const int q0 = q_start(a, b), lq = q_len(a, b);
+  const int k0 = k_start(a, b), lk = k_len(a, b);
   const int hk = h / a.group;
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int hl = lane >> 5, c = lane & 31;
   const int i = qt * kFwdBM + w * 32 + c;     // this lane's query row
 
-  const int64_t qstride = (int64_t)a.hq * D;
-  const int64_t kstride = (int64_t)a.hk * D;
-  const T* kp = static_cast<const T*>(a.k) + (int64_t)k0 * kstride + hk * D;
-  const T* vp = static_cast<const T*>(a.v) + (int64_t)k0 * kstride + hk * D;
+  const int64_t kstride = a.g.k_row;
+  const T* kp = static_cast<const T*>(a.k) + (int64_t)k0 * a.g.k_seq + hk * a.g.k_head;
+  const T* vp = static_cast<const T*>(a.v) + (int64_t)k0 * a.g.k_seq + hk * a.g.k_head;
 
   // Q and dO rows as B operands of S^T = K Q^T and dP^T = V dO^T
   vec8<T> qf[NT], gf[NT];
-  const int64_t roff = (int64_t)(q0 + i) * qstride + h * D;
+  const int64_t roff = (int64_t)q0 * a.g.q_seq + (int64_t)i * a.g.q_row + h * a.g.q_head;
+  const int64_t ooff = (int64_t)q0 * a.g.o_seq + (int64_t)i * a.g.o_row + h * a.g.o_head;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     if (i < lq) {
       qf[t] = __builtin_bit_cast(vec8<T>, ld16(static_cast<const T*>(a.q) + roff + 16 * t + 8 * hl));
-      gf[t] = __builtin_bit_cast(vec8<T>, ld16(static_cast<const T*>(a.dout) + roff + 16 * t + 8 * hl));
+      gf[t] = __builtin_bit_cast(vec8<T>, ld16(static_cast<const T*>(a.dout) + ooff + 16 * t + 8 * hl));
     } else {
       qf[t] = vec8<T>{};
       gf[t] = vec8<T>{};
@@ -375,7 +383,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   }
   float lse2 = __builtin_huge_valf(), dval = 0.f;
   if (i < lq) {
-    const float l = a.lse[(int64_t)h * a.total_q + q0 + i];
+    const float l = a.lse[(int64_t)q0 * a.g.l_seq + (int64_t)i * a.g.l_row + h * a.g.l_head];
     lse2 = l == kNegInf ? __builtin_huge_valf() : l * kLog2e;
     dval = a.dval[(int64_t)h * a.total_q + q0 + i];
   }

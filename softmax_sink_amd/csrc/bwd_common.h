@@ -11,6 +11,7 @@
 
 #include "device_common.h"
 #include "sink_attn_internal.h"
+#include "tile_common.h"
 
 namespace sinkattn {
 namespace {
@@ -30,9 +31,19 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   for (int pass = 0; pass < kPreRows / RPP; ++pass) {
     const int rr = pass * RPP + threadIdx.x / TPR;
     const int t = t0 + rr;
+    // row t of the tensors is row i of its sequence; in a padded layout
+    // the rows past the sequence's length take no part
+    int i = 0;
+    bool live = t < a.total_q;
+    if (a.g.seq_q && live) {
+      int b;
+      q_row_of(a, t, b, i);
+      live = i < q_len(a, b);
+    }
+    const int64_t row0 = (int64_t)(t - i);
     float dot = 0.f;
-    if (t < a.total_q) {
-      const int64_t off = ((int64_t)t * a.hq + h) * D + cidx * 8;
+    if (live) {
+      const int64_t off = row0 * a.g.o_seq + (int64_t)i * a.g.o_row + h * a.g.o_head + cidx * 8;
       const T* dop = static_cast<const T*>(a.dout) + off;
       const T* op = static_cast<const T*>(a.out) + off;
 #pragma unroll
@@ -42,9 +53,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
     for (int o = TPR / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
     if (cidx == 0) {
       float cterm = 0.f;
-      if (t < a.total_q) {
-        a.dval[(int64_t)h * a.total_q + t] = dot;
-        const float lse = a.lse[(int64_t)h * a.total_q + t];
+      if (t < a.total_q) a.dval[(int64_t)h * a.total_q + t] = dot;
+      if (live) {
+        const float lse = a.lse[row0 * a.g.l_seq + (int64_t)i * a.g.l_row + h * a.g.l_head];
         const float ps = sink > kNegInf ? exp2_hw((sink - lse) * kLog2e) : 0.f;
         cterm = -ps * dot;
       }

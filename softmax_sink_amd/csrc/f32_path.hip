@@ -16,26 +16,20 @@ namespace {
 
 using namespace dev;
 
-__device__ __forceinline__ int seq_of(const int32_t* cu, int batch, int t) {
-  int lo = 0, hi = batch;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (cu[mid] <= t) lo = mid; else hi = mid;
-  }
-  return lo;
-}
-
 template <int D>
 __global__ __launch_bounds__(128) void fwd_f32_kernel(FwdArgs a) {
   const int row = blockIdx.x * 128 + threadIdx.x;
   if (row >= a.total_q * a.hq) return;
   const int t = row / a.hq, h = row % a.hq, hk = h / a.group;
-  const int b = seq_of(a.cu_q, a.batch, t);
-  const int q0 = a.cu_q[b], lq = a.cu_q[b + 1] - q0, i = t - q0;
-  const int k0 = a.cu_k[b], lk = a.cu_k[b + 1] - k0;
+  int b, i;
+  q_row_of(a, t, b, i);
+  const int lq = q_len(a, b);
+  if (i >= lq) return;   // padding row of a padded layout
+  const int k0 = k_start(a, b), lk = k_len(a, b);
   int jlo, jhi;
   row_key_range(i, lq, lk, a.causal, a.win_left, a.win_right, jlo, jhi);
-  const float* qp = static_cast<const float*>(a.q) + ((int64_t)t * a.hq + h) * D;
+  const int64_t off = (int64_t)(t - i) * a.g.q_seq + (int64_t)i * a.g.q_row + h * a.g.q_head;
+  const float* qp = static_cast<const float*>(a.q) + off;
   float q[D], o[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) { q[d] = qp[d] * a.scale * kLog2e; o[d] = 0.f; }
@@ -43,8 +37,9 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(FwdArgs a) {
   float m = sink * kLog2e;
   float l = sink > kNegInf ? 1.f : 0.f;
   for (int jj = jlo; jj <= jhi; ++jj) {
-    const float* kp = static_cast<const float*>(a.k) + ((int64_t)(k0 + jj) * a.hk + hk) * D;
-    const float* vp = static_cast<const float*>(a.v) + ((int64_t)(k0 + jj) * a.hk + hk) * D;
+    const int64_t ko = (int64_t)k0 * a.g.k_seq + (int64_t)jj * a.g.k_row + hk * a.g.k_head;
+    const float* kp = static_cast<const float*>(a.k) + ko;
+    const float* vp = static_cast<const float*>(a.v) + ko;
     float s = 0.f;
 #pragma unroll
     for (int d = 0; d < D; ++d) s = __builtin_fmaf(q[d], kp[d], s);
@@ -57,10 +52,12 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(FwdArgs a) {
     m = mn;
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  float* op = static_cast<float*>(a.out) + ((int64_t)t * a.hq + h) * D;
+  float* op = static_cast<float*>(a.out) + (int64_t)(t - i) * a.g.o_seq + (int64_t)i * a.g.o_row +
+              h * a.g.o_head;
 #pragma unroll
   for (int d = 0; d < D; ++d) op[d] = o[d] * inv;
-  a.lse[(int64_t)h * a.total_q + t] = l > 0.f ? (m + log2_hw(l)) * kLn2 : kNegInf;
+  a.lse[(int64_t)(t - i) * a.g.l_seq + (int64_t)i * a.g.l_row + h * a.g.l_head] =
+      l > 0.f ? (m + log2_hw(l)) * kLn2 : kNegInf;
 }
 
 template <int D>
@@ -68,23 +65,28 @@ __global__ __launch_bounds__(128) void bwd_dq_f32_kernel(BwdArgs a) {
   const int row = blockIdx.x * 128 + threadIdx.x;
   if (row >= a.total_q * a.hq) return;
   const int t = row / a.hq, h = row % a.hq, hk = h / a.group;
-  const int b = seq_of(a.cu_q, a.batch, t);
-  const int q0 = a.cu_q[b], lq = a.cu_q[b + 1] - q0, i = t - q0;
-  const int k0 = a.cu_k[b], lk = a.cu_k[b + 1] - k0;
+  int b, i;
+  q_row_of(a, t, b, i);
+  const int lq = q_len(a, b);
+  if (i >= lq) return;
+  const int k0 = k_start(a, b), lk = k_len(a, b);
   int jlo, jhi;
   row_key_range(i, lq, lk, a.causal, a.win_left, a.win_right, jlo, jhi);
-  const int64_t off = ((int64_t)t * a.hq + h) * D;
+  const int64_t off = (int64_t)(t - i) * a.g.q_seq + (int64_t)i * a.g.q_row + h * a.g.q_head;
   const float* qp = static_cast<const float*>(a.q) + off;
-  const float* dop = static_cast<const float*>(a.dout) + off;
+  const float* dop = static_cast<const float*>(a.dout) + (int64_t)(t - i) * a.g.o_seq +
+                     (int64_t)i * a.g.o_row + h * a.g.o_head;
   float q[D], g[D], dq[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) { q[d] = qp[d]; g[d] = dop[d]; dq[d] = 0.f; }
-  const float lse2 = a.lse[(int64_t)h * a.total_q + t] * kLog2e;
+  const float lse2 =
+      a.lse[(int64_t)(t - i) * a.g.l_seq + (int64_t)i * a.g.l_row + h * a.g.l_head] * kLog2e;
   const float Dt = a.dval[(int64_t)h * a.total_q + t];
   const float c2 = a.scale * kLog2e;
   for (int jj = jlo; jj <= jhi; ++jj) {
-    const float* kp = static_cast<const float*>(a.k) + ((int64_t)(k0 + jj) * a.hk + hk) * D;
-    const float* vp = static_cast<const float*>(a.v) + ((int64_t)(k0 + jj) * a.hk + hk) * D;
+    const int64_t ko = (int64_t)k0 * a.g.k_seq + (int64_t)jj * a.g.k_row + hk * a.g.k_head;
+    const float* kp = static_cast<const float*>(a.k) + ko;
+    const float* vp = static_cast<const float*>(a.v) + ko;
     float s = 0.f, dp = 0.f;
 #pragma unroll
     for (int d = 0; d < D; ++d) { s = __builtin_fmaf(q[d], kp[d], s); dp = __builtin_fmaf(g[d], vp[d], dp); }
@@ -103,12 +105,14 @@ __global__ __launch_bounds__(128) void bwd_dkdv_f32_kernel(BwdArgs a) {
   const int row = blockIdx.x * 128 + threadIdx.x;
   if (row >= a.total_k * a.hk) return;
   const int t = row / a.hk, hk = row % a.hk;
-  const int b = seq_of(a.cu_k, a.batch, t);
-  const int k0 = a.cu_k[b], lk = a.cu_k[b + 1] - k0, j = t - k0;
-  const int q0 = a.cu_q[b], lq = a.cu_q[b + 1] - q0;
+  int b, j;
+  k_row_of(a, t, b, j);
+  const int lk = k_len(a, b);
+  if (j >= lk) return;   // padding key of a padded layout
+  const int q0 = q_start(a, b), lq = q_len(a, b);
   int ilo, ihi;
   key_row_range(j, lq, lk, a.causal, a.win_left, a.win_right, ilo, ihi);
-  const int64_t off = ((int64_t)t * a.hk + hk) * D;
+  const int64_t off = (int64_t)(t - j) * a.g.k_seq + (int64_t)j * a.g.k_row + hk * a.g.k_head;
   const float* kp = static_cast<const float*>(a.k) + off;
   const float* vp = static_cast<const float*>(a.v) + off;
   float kk[D], vv[D], dk[D], dv[D];
@@ -118,13 +122,15 @@ __global__ __launch_bounds__(128) void bwd_dkdv_f32_kernel(BwdArgs a) {
   for (int g = 0; g < a.group; ++g) {
     const int h = hk * a.group + g;
     for (int i = ilo; i <= ihi; ++i) {
-      const int64_t qo = ((int64_t)(q0 + i) * a.hq + h) * D;
+      const int64_t qo = (int64_t)q0 * a.g.q_seq + (int64_t)i * a.g.q_row + h * a.g.q_head;
       const float* qp = static_cast<const float*>(a.q) + qo;
-      const float* dop = static_cast<const float*>(a.dout) + qo;
+      const float* dop = static_cast<const float*>(a.dout) + (int64_t)q0 * a.g.o_seq +
+                         (int64_t)i * a.g.o_row + h * a.g.o_head;
       float s = 0.f, dp = 0.f;
 #pragma unroll
       for (int d = 0; d < D; ++d) { s = __builtin_fmaf(qp[d], kk[d], s); dp = __builtin_fmaf(dop[d], vv[d], dp); }
-      const float lse2 = a.lse[(int64_t)h * a.total_q + q0 + i] * kLog2e;
+      const float lse2 =
+          a.lse[(int64_t)q0 * a.g.l_seq + (int64_t)i * a.g.l_row + h * a.g.l_head] * kLog2e;
       const float p = exp2_hw(__builtin_fmaf(s, c2, -lse2));
       const float ds = a.scale * p * (dp - a.dval[(int64_t)h * a.total_q + q0 + i]);
 #pragma unroll

@@ -50,19 +50,20 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdArgs a) {
   const int* it = a.items + item * kItemWords;
   const int b = it[0], qt = it[1], kt_lo = it[2], kt_hi = it[3];
   const int kf_lo = it[4], kf_hi = it[5];
-  const int q0 = a.cu_q[b], lq = a.cu_q[b + 1] - q0;
-  const int k0 = a.cu_k[b], lk = a.cu_k[b + 1] - k0;
+  const int q0 = q_start(a, b), lq = q_len(a, b);
+  const int k0 = k_start(a, b), lk = k_len(a, b);
   const int hk = h / a.group;
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int hl = lane >> 5, c = lane & 31;
   const int i = qt * kFwdBM + w * 32 + c;     // this lane's query row
 
-  const int64_t qstride = (int64_t)a.hq * D;
-  const int64_t kstride = (int64_t)a.hk * D;
-  const T* qp = static_cast<const T*>(a.q) + (int64_t)q0 * qstride + h * D;
-  const T* kp = static_cast<const T*>(a.k) + (int64_t)k0 * kstride + hk * D;
-  const T* vp = static_cast<const T*>(a.v) + (int64_t)k0 * kstride + hk * D;
+  const int64_t qstride = a.g.q_row;
+  const int64_t kstride = a.g.k_row;
+  const int64_t qoff = (int64_t)q0 * a.g.q_seq + h * a.g.q_head;   // row 0 of q
+  const T* qp = static_cast<const T*>(a.q) + qoff;
+  const T* kp = static_cast<const T*>(a.k) + (int64_t)k0 * a.g.k_seq + hk * a.g.k_head;
+  const T* vp = static_cast<const T*>(a.v) + (int64_t)k0 * a.g.k_seq + hk * a.g.k_head;
 
   // Q as the B operand of S^T = K Q^T: lane (hl, c) holds Q[i][16t + 8hl .. +7]
   vec8<T> qf[NT];
@@ -186,7 +187,8 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdArgs a) {
   const float lt = l + half_partner(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (i < lq) {
-    T* op = static_cast<T*>(a.out) + (int64_t)(q0 + i) * qstride + h * D;
+    T* op = static_cast<T*>(a.out) + (int64_t)q0 * a.g.o_seq + (int64_t)i * a.g.o_row +
+            h * a.g.o_head;
 #pragma unroll
     for (int n = 0; n < NB; ++n)
 #pragma unroll
@@ -197,7 +199,8 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdArgs a) {
                        o[n][4 * g + 2] * inv, o[n][4 * g + 3] * inv);
       }
     if (hl == 0)
-      a.lse[(int64_t)h * a.total_q + q0 + i] = lt > 0.f ? (m + log2_hw(lt)) * kLn2 : kNegInf;
+      a.lse[(int64_t)q0 * a.g.l_seq + (int64_t)i * a.g.l_row + h * a.g.l_head] =
+          lt > 0.f ? (m + log2_hw(lt)) * kLn2 : kNegInf;
   }
 }
 
@@ -226,10 +229,10 @@ __global__ __launch_bounds__(256, 2) void fwd_split_kernel(FwdArgs a) {
   const int hk = blockIdx.x % a.hk;
   const int* it = a.items + item * kItemWords;
   const int b = it[0], k_lo = it[2], k_hi = it[3], row_base = it[4];
-  const int q0 = a.cu_q[b], lq = a.cu_q[b + 1] - q0;
+  const int q0 = q_start(a, b), lq = q_len(a, b);
   int k0 = 0, lk;
   if constexpr (PAGED) lk = a.seqused_k[b];
-  else { k0 = a.cu_k[b]; lk = a.cu_k[b + 1] - k0; }
+  else { k0 = k_start(a, b); lk = k_len(a, b); }
   const int G = a.group;
   const int rows = lq * G;
 
@@ -240,14 +243,14 @@ __global__ __launch_bounds__(256, 2) void fwd_split_kernel(FwdArgs a) {
   const int g = lq > 0 ? r / lq : 0, i = lq > 0 ? r % lq : 0;
   const int h = hk * G + g;
 
-  const int64_t qstride = (int64_t)a.hq * D;
-  const int64_t kstride = (int64_t)a.hk * D;
-  const T* kp = static_cast<const T*>(a.k) + (int64_t)k0 * kstride + hk * D;
-  const T* vp = static_cast<const T*>(a.v) + (int64_t)k0 * kstride + hk * D;
+  const int64_t kstride = a.g.k_row;
+  const T* kp = static_cast<const T*>(a.k) + (int64_t)k0 * a.g.k_seq + hk * a.g.k_head;
+  const T* vp = static_cast<const T*>(a.v) + (int64_t)k0 * a.g.k_seq + hk * a.g.k_head;
 
   vec8<T> qf[NT];
   const bool live_row = r < rows;
-  const T* qrow = static_cast<const T*>(a.q) + (int64_t)(q0 + i) * qstride + h * D;
+  const T* qrow = static_cast<const T*>(a.q) + (int64_t)q0 * a.g.q_seq + (int64_t)i * a.g.q_row +
+                  h * a.g.q_head;
 #pragma unroll
   for (int t = 0; t < NT; ++t)
     qf[t] = live_row ? __builtin_bit_cast(vec8<T>, ld16(qrow + 16 * t + 8 * hl)) : vec8<T>{};
@@ -280,9 +283,10 @@ __global__ __launch_bounds__(256, 2) void fwd_split_kernel(FwdArgs a) {
   // K and V rows [row0, row0 + BN) of the item into one LDS buffer
   auto load_kv = [&](int row0, char* dst) __attribute__((always_inline)) {
     if constexpr (PAGED) {
-      pl.load(static_cast<const T*>(a.k), (int64_t)hk * D, kstride, pages, off0, k_lo, row0,
+      // the cache layout is [num_blocks, block_size, Hk, D] whatever the q layout
+      pl.load(static_cast<const T*>(a.k), (int64_t)hk * D, (int64_t)a.hk * D, pages, off0, k_lo, row0,
               k_hi - 1, a.page_size, a.page_magic, dst);
-      pl.load(static_cast<const T*>(a.v), (int64_t)hk * D, kstride, pages, off0, k_lo, row0,
+      pl.load(static_cast<const T*>(a.v), (int64_t)hk * D, (int64_t)a.hk * D, pages, off0, k_lo, row0,
               k_hi - 1, a.page_size, a.page_magic, dst + TILE);
     } else {
       kl.load(kp, kstride, row0, k_hi, dst);
@@ -397,13 +401,10 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(FwdArgs a) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= a.total_q * a.hq) return;
   const int t = row / a.hq, h = row % a.hq;
-  int lo = 0, hi = a.batch;                     // sequence of token t
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.cu_q[mid] <= t) lo = mid; else hi = mid;
-  }
-  const int b = lo;
-  const int q0 = a.cu_q[b], lq = a.cu_q[b + 1] - q0, i = t - q0;
+  int b, i;                                     // sequence and row of token t
+  q_row_of(a, t, b, i);
+  const int q0 = q_start(a, b), lq = q_len(a, b);
+  if (i >= lq) return;                          // padding of a padded layout
   const int first = a.dec_seq[2 * b], n = a.dec_seq[2 * b + 1];
   const float sink = a.sinks ? a.sinks[h] : kNegInf;
   float mt = sink * kLog2e;
@@ -426,11 +427,13 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(FwdArgs a) {
     for (int e = 0; e < PER; ++e) acc[e] += po[e] * f;
   }
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  T* op = static_cast<T*>(a.out) + ((int64_t)t * a.hq + h) * D + lane * PER;
+  T* op = static_cast<T*>(a.out) + (int64_t)q0 * a.g.o_seq + (int64_t)i * a.g.o_row +
+          h * a.g.o_head + lane * PER;
 #pragma unroll
   for (int e = 0; e < PER; ++e) op[e] = (T)(acc[e] * inv);
   if (lane == 0)
-    a.lse[(int64_t)h * a.total_q + t] = lt > 0.f ? (mt + log2_hw(lt)) * kLn2 : kNegInf;
+    a.lse[(int64_t)q0 * a.g.l_seq + (int64_t)i * a.g.l_row + h * a.g.l_head] =
+        lt > 0.f ? (mt + log2_hw(lt)) * kLn2 : kNegInf;
 }
 
 template <int D, typename T>

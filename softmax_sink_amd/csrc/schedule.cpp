@@ -129,6 +129,39 @@ BwdWorkspace bwd_workspace_layout(int64_t total_q, int hq, int head_dim,
   return w;
 }
 
+Geometry make_geometry(const sink_attn_problem& p, const int32_t* used_q,
+                       const int32_t* used_k) {
+  Geometry g{};
+  const int64_t hq = p.num_heads_q, hk = p.num_heads_k, d = p.head_dim;
+  g.used_q = used_q;
+  g.used_k = used_k;
+  // Row i of head h of the sequence starting at row r: r*x_seq + i*x_row +
+  // h*x_head. TND and BSND ([.., S, N, D]) interleave the heads in a row;
+  // BNSD ([B, N, S, D]) keeps each head's S rows together.
+  auto set = [&](int layout, int64_t n, int64_t seq, int64_t& xs, int64_t& xr, int64_t& xh) {
+    xs = n * d;
+    if (layout == SINK_ATTN_BNSD) { xr = d; xh = seq * d; }
+    else { xr = n * d; xh = d; }
+  };
+  set(p.layout_q, hq, p.seq_q, g.q_seq, g.q_row, g.q_head);
+  set(p.layout_out, hq, p.seq_q, g.o_seq, g.o_row, g.o_head);
+  set(p.layout_q, hk, p.seq_k, g.k_seq, g.k_row, g.k_head);
+  if (p.layout_q == SINK_ATTN_TND) {
+    // lse [Hq, Tq]
+    g.l_seq = 1;
+    g.l_row = 1;
+    g.l_head = p.total_q;
+  } else {
+    // lse [B, Hq, S]: sequence b starts at row b*S, b*Hq*S elements in
+    g.seq_q = p.seq_q;
+    g.seq_k = p.seq_k;
+    g.l_seq = hq;
+    g.l_row = 1;
+    g.l_head = p.seq_q;
+  }
+  return g;
+}
+
 sink_attn_status validate_problem(const sink_attn_problem* p) {
   if (!p) return SINK_ATTN_E_INVALID;
   if (p->batch <= 0 || p->batch >= 65536) return SINK_ATTN_E_INVALID;
@@ -142,6 +175,21 @@ sink_attn_status validate_problem(const sink_attn_problem* p) {
   if (p->dtype != SINK_ATTN_FP32 && p->dtype != SINK_ATTN_BF16 && p->dtype != SINK_ATTN_FP16)
     return SINK_ATTN_E_UNSUPPORTED;
   if (p->head_dim != 64 && p->head_dim != 128) return SINK_ATTN_E_UNSUPPORTED;
+  // layouts: out follows q, except BNSD q with BSND out
+  if (p->layout_q != SINK_ATTN_TND && p->layout_q != SINK_ATTN_BSND &&
+      p->layout_q != SINK_ATTN_BNSD)
+    return SINK_ATTN_E_INVALID;
+  if (p->layout_out != p->layout_q &&
+      !(p->layout_q == SINK_ATTN_BNSD && p->layout_out == SINK_ATTN_BSND))
+    return SINK_ATTN_E_INVALID;
+  if (p->layout_q == SINK_ATTN_TND) {
+    if (p->seq_q != 0 || p->seq_k != 0) return SINK_ATTN_E_INVALID;
+  } else {
+    if (p->seq_q <= 0 || p->seq_k <= 0) return SINK_ATTN_E_INVALID;
+    if (static_cast<int64_t>(p->batch) * p->seq_q != p->total_q ||
+        static_cast<int64_t>(p->batch) * p->seq_k != p->total_k)
+      return SINK_ATTN_E_INVALID;
+  }
   // element offsets of the largest tensors must fit the kernels' 32-bit
   // row arithmetic
   int64_t rows_q = static_cast<int64_t>(p->total_q) * p->num_heads_q;
@@ -165,6 +213,26 @@ sink_attn_status validate_cu_seqlens(const sink_attn_problem& p,
   }
   if (cu_q[p.batch] != p.total_q || cu_k[p.batch] != p.total_k)
     return SINK_ATTN_E_INVALID;
+  if (mq != p.max_seqlen_q || mk != p.max_seqlen_k) return SINK_ATTN_E_INVALID;
+  return SINK_ATTN_OK;
+}
+
+sink_attn_status validate_seqused(const sink_attn_problem& p, const int32_t* used_q,
+                                  const int32_t* used_k, int32_t* cu_q_out,
+                                  int32_t* cu_k_out) {
+  if (!cu_q_out || !cu_k_out) return SINK_ATTN_E_INVALID;
+  cu_q_out[0] = cu_k_out[0] = 0;
+  int32_t mq = 0, mk = 0;
+  for (int b = 0; b < p.batch; ++b) {
+    const int32_t lq = used_q ? used_q[b] : p.seq_q;
+    const int32_t lk = used_k ? used_k[b] : p.seq_k;
+    if (lq < 0 || lq > p.seq_q || lk < 0 || lk > p.seq_k) return SINK_ATTN_E_INVALID;
+    mq = std::max(mq, lq);
+    mk = std::max(mk, lk);
+    // at most batch * seq rows in all, which the problem check keeps in int32
+    cu_q_out[b + 1] = cu_q_out[b] + lq;
+    cu_k_out[b + 1] = cu_k_out[b] + lk;
+  }
   if (mq != p.max_seqlen_q || mk != p.max_seqlen_k) return SINK_ATTN_E_INVALID;
   return SINK_ATTN_OK;
 }
@@ -194,8 +262,8 @@ sink_attn_status validate_paged(const sink_attn_problem& p,
 
 sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
                                 const int32_t* cu_k, const PagedInfo* paged,
-                                int32_t* out, int64_t capacity, int64_t* words,
-                                int64_t* fwd_ws, int64_t* bwd_ws) {
+                                int used_mask, int32_t* out, int64_t capacity,
+                                int64_t* words, int64_t* fwd_ws, int64_t* bwd_ws) {
   const int B = p.batch;
   const int G = p.num_heads_q / p.num_heads_k;
   std::vector<Item> fwd, bwd, dec;
@@ -326,6 +394,11 @@ sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
       fnv1a(cu_k, B + 1, fnv1a(cu_q, B + 1, 2166136261u)));
   h[kMetaWords] = static_cast<int32_t>(total);
   h[kBwdPreBlocks] = static_cast<int32_t>(pre_blocks);
+  h[kLayoutQ] = p.layout_q;
+  h[kLayoutOut] = p.layout_out;
+  h[kSeqQ] = p.seq_q;
+  h[kSeqK] = p.seq_k;
+  h[kUsedMask] = used_mask;
   if (paged) {
     const int64_t bs = paged->kv.block_size;
     uint32_t hash = 2166136261u;
@@ -358,7 +431,9 @@ sink_attn_status check_header(const sink_attn_problem& p, const int32_t* h,
       h[kTq] != p.total_q || h[kTk] != p.total_k ||
       h[kMaxQ] != p.max_seqlen_q || h[kMaxK] != p.max_seqlen_k ||
       h[kCausal] != p.causal || h[kWinL] != p.win_left ||
-      h[kWinR] != p.win_right || h[kDtype] != p.dtype)
+      h[kWinR] != p.win_right || h[kDtype] != p.dtype ||
+      h[kLayoutQ] != p.layout_q || h[kLayoutOut] != p.layout_out ||
+      h[kSeqQ] != p.seq_q || h[kSeqK] != p.seq_k)
     return SINK_ATTN_E_META_MISMATCH;
   if (h[kWordFwdBM] != kFwdBM || h[kWordFwdBN] != kFwdBN || h[kWordBwdBM] != kBwdBM ||
       h[kWordBwdBN] != kBwdBN || h[kWordDecBN] != kDecBN || h[kWordDecChunk] != kDecChunk)

@@ -20,6 +20,7 @@ enum MetaWord : int {
   kFwdWsLo, kFwdWsHi, kBwdWsLo, kBwdWsHi, kCuHash, kMetaWords,
   kBwdPreBlocks,
   kPaged, kPageSize, kPageMaxBlocks, kPageNumBlocks, kPageHash,
+  kLayoutQ, kLayoutOut, kSeqQ, kSeqK, kUsedMask,
   kHeaderWords = 48
 };
 
@@ -70,6 +71,11 @@ struct PagedInfo {
 sink_attn_status validate_problem(const sink_attn_problem* p);
 sink_attn_status validate_cu_seqlens(const sink_attn_problem& p,
                                      const int32_t* cu_q, const int32_t* cu_k);
+// Padded layouts: checks the host used lengths (null: all S) and writes
+// their prefix sums (batch + 1 words each), which is all the schedule needs.
+sink_attn_status validate_seqused(const sink_attn_problem& p, const int32_t* used_q,
+                                  const int32_t* used_k, int32_t* cu_q_out,
+                                  int32_t* cu_k_out);
 // Checks a paged layout against the problem and the host tables, and
 // writes the key-length prefix sums (batch + 1 words) into cu_k_out.
 sink_attn_status validate_paged(const sink_attn_problem& p,
@@ -77,11 +83,12 @@ sink_attn_status validate_paged(const sink_attn_problem& p,
                                 const int32_t* seqused_kv,
                                 const int32_t* block_table, int32_t* cu_k_out);
 // Builds the table; writes it when `out` is non-null and capacity allows.
-// `paged` is null for contiguous keys and values.
+// `paged` is null for contiguous keys and values; `used_mask` records which
+// seqused arrays a padded-layout call passes (1: q, 2: kv).
 sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
                                 const int32_t* cu_k, const PagedInfo* paged,
-                                int32_t* out, int64_t capacity, int64_t* words,
-                                int64_t* fwd_ws, int64_t* bwd_ws);
+                                int used_mask, int32_t* out, int64_t capacity,
+                                int64_t* words, int64_t* fwd_ws, int64_t* bwd_ws);
 // Header against the call; `kv` is null for the contiguous calls.
 sink_attn_status check_header(const sink_attn_problem& p, const int32_t* meta,
                               const sink_attn_paged_kv* kv);
@@ -89,12 +96,33 @@ sink_attn_status check_header(const sink_attn_problem& p, const int32_t* meta,
 // ---------------------------------------------------------------------------
 // Kernel arguments and launchers (kernels_*.hip).
 // ---------------------------------------------------------------------------
+// Where the rows of every sequence live. Sequence b holds rows
+// [0, len(b)) starting at row start(b) of its tensors: TND takes both from
+// cu_seqlens; the padded layouts (BSND, BNSD) have start(b) = b * seq and
+// len(b) = used[b] (or seq). Row i of head h of sequence b sits at element
+//   start(b) * x_seq + i * x_row + h * x_head
+// of q/dq (x = q), out/dout (x = o), k/v/dk/dv (x = k) and lse (x = l).
+struct Geometry {
+  const int32_t* used_q;    // padded layouts: rows in use (null: all seq_q)
+  const int32_t* used_k;
+  int seq_q, seq_k;         // padded layouts: rows per batch entry; TND: 0
+  int64_t q_seq, q_row, q_head;
+  int64_t o_seq, o_row, o_head;
+  int64_t k_seq, k_row, k_head;
+  int64_t l_seq, l_row, l_head;
+};
+// The geometry of a problem's layout (TND: the contiguous THD tensors and
+// the [Hq, Tq] lse).
+Geometry make_geometry(const sink_attn_problem& p, const int32_t* used_q,
+                       const int32_t* used_k);
+
 struct FwdArgs {
   const void* q;
   const void* k;
   const void* v;
   const int32_t* cu_q;
   const int32_t* cu_k;
+  Geometry g;
   const float* sinks;       // null: no sink
   void* out;
   float* lse;
@@ -123,6 +151,7 @@ struct BwdArgs {
   const float* lse;
   const int32_t* cu_q;
   const int32_t* cu_k;
+  Geometry g;
   const float* sinks;
   void* dq;
   void* dk;

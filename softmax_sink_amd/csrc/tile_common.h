@@ -144,6 +144,59 @@ struct PagedTileDma {
   }
 };
 
+// Rows of sequence b (see Geometry): first row and row count, for the query
+// side and the key side.
+template <class A>
+__device__ __forceinline__ int q_start(const A& a, int b) {
+  return a.g.seq_q ? b * a.g.seq_q : a.cu_q[b];
+}
+template <class A>
+__device__ __forceinline__ int q_len(const A& a, int b) {
+  return a.g.seq_q ? (a.g.used_q ? a.g.used_q[b] : a.g.seq_q) : a.cu_q[b + 1] - a.cu_q[b];
+}
+template <class A>
+__device__ __forceinline__ int k_start(const A& a, int b) {
+  return a.g.seq_k ? b * a.g.seq_k : a.cu_k[b];
+}
+template <class A>
+__device__ __forceinline__ int k_len(const A& a, int b) {
+  return a.g.seq_k ? (a.g.used_k ? a.g.used_k[b] : a.g.seq_k) : a.cu_k[b + 1] - a.cu_k[b];
+}
+// Sequence and in-sequence row of query row t of the tensors (rows past a
+// sequence's length in a padded layout give i >= q_len).
+template <class A>
+__device__ __forceinline__ void q_row_of(const A& a, int t, int& b, int& i) {
+  if (a.g.seq_q) {
+    b = t / a.g.seq_q;
+    i = t - b * a.g.seq_q;
+    return;
+  }
+  int lo = 0, hi = a.batch;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.cu_q[mid] <= t) lo = mid; else hi = mid;
+  }
+  b = lo;
+  i = t - a.cu_q[b];
+}
+
+// The same for key row t.
+template <class A>
+__device__ __forceinline__ void k_row_of(const A& a, int t, int& b, int& j) {
+  if (a.g.seq_k) {
+    b = t / a.g.seq_k;
+    j = t - b * a.g.seq_k;
+    return;
+  }
+  int lo = 0, hi = a.batch;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.cu_k[mid] <= t) lo = mid; else hi = mid;
+  }
+  b = lo;
+  j = t - a.cu_k[b];
+}
+
 // Head index for the j-th slot of the head-fastest block numbering. Blocks
 // are spread over the 8 XCDs round robin (block id mod 8); with this map the
 // q-heads of one kv group -- which read the same K/V -- share an XCD and

@@ -205,6 +205,29 @@ def scatter_to_pages(x, cu_k, layout):
     return cache
 
 
+# Raw NaN patterns by element type: padding rows of the batch-padded layouts
+# are filled with NaN so that any read of them shows in the results.
+NAN_BITS = {"bf16": np.uint16(0x7FC0), "fp16": np.uint16(0x7E00), "fp32": np.float32(np.nan)}
+
+
+def pad_rows(x, cu, seq, layout, fill):
+    """Packed rows x [T, N, D] of sequences cu -> a batch-padded tensor with
+    seq rows per sequence: "BSND" [B, seq, N, D] or "BNSD" [B, N, seq, D].
+    Row i of sequence b lands at [b, i] (BSND) or [b, :, i] (BNSD); rows past
+    a sequence's length hold `fill`."""
+    nb = len(cu) - 1
+    n, d = x.shape[1], x.shape[2]
+    out = np.full((nb, seq, n, d), fill, dtype=x.dtype)
+    for b in range(nb):
+        rows = x[int(cu[b]):int(cu[b + 1])]
+        out[b, :len(rows)] = rows
+    if layout == "BNSD":
+        out = np.ascontiguousarray(out.transpose(0, 2, 1, 3))
+    elif layout != "BSND":
+        raise ValueError(layout)
+    return out
+
+
 def _train_lengths(rng, n=8, total=32768, lo=1024, hi=8192):
     """n lengths uniform in [lo, hi] summing to total: draw n-1, set the last
     to the remainder, redraw all until the last is in range."""

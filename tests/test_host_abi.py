@@ -29,11 +29,12 @@ def test_exports_every_declared_symbol(L):
     names = set(re.findall(r"\b(sink_attn_[a-z_]+)\s*\(", text))
     assert {"sink_attn_metadata", "sink_attn_fwd", "sink_attn_bwd",
             "sink_attn_metadata_paged", "sink_attn_fwd_paged",
+            "sink_attn_metadata_padded", "sink_attn_fwd_padded", "sink_attn_bwd_padded",
             "sink_attn_status_string", "sink_attn_abi_version",
             "sink_attn_arm_timing"} <= names
     for n in names:
         assert hasattr(L, n), n
-    assert B.abi_version() == 2
+    assert B.abi_version() == 3
     for s in range(6):
         assert isinstance(B.status_string(s), str)
 
@@ -113,7 +114,7 @@ def test_metadata_two_call_protocol_and_sizes(L):
                               ctypes.byref(words), ctypes.byref(fws), ctypes.byref(bws))
     assert st == B.E_BUFFER_TOO_SMALL
     meta, f, b = B.sink_attn_metadata(p, cu, cu)
-    assert meta[0] == 0x4B4E4953 and meta[1] == 2 and len(meta) == words.value
+    assert meta[0] == 0x4B4E4953 and meta[1] == 3 and len(meta) == words.value
     # bwd workspace: D [Hq,Tq] fp32 + per-block dsink partials (no dQ accumulator)
     assert 300 * 8 * 4 <= b < 300 * 8 * 4 + 4096
     assert f == 0       # prefill mode needs no forward scratch
@@ -340,3 +341,111 @@ def test_decode_workspace_sized_for_every_16bit_dtype():
     table = np.arange(2 * 188, dtype=np.int32).reshape(2, 188)
     _, fws = B.sink_attn_metadata_paged(p, B.PagedKV(16, 188, 2 * 188), cq, np.diff(ck), table)
     assert fws == sizes[B.BF16]
+
+
+# ---------------------------------------------------------------------------
+# batch-padded layouts (BSND / BNSD, seqused)
+# ---------------------------------------------------------------------------
+W_LAYOUT = 41   # header words: layout_q, layout_out, seq_q, seq_k, seqused mask
+
+
+def _padded(batch=3, sq=70, sk=130, uq=(70, 0, 33), uk=(130, 5, 64), layout="BSND",
+            layout_out=None, causal=True, wl=-1, wr=-1, hq=8, hk=2):
+    uq = None if uq is None else np.array(uq, np.int32)
+    uk = None if uk is None else np.array(uk, np.int32)
+    p = B.make_problem_padded(batch, sq, sk, uq, uk, hq, hk, 128, causal, wl, wr, B.BF16,
+                              layout, layout_out)
+    return p, uq, uk
+
+
+@pytest.mark.parametrize("layout,lout", [("BSND", None), ("BNSD", None), ("BNSD", "BSND")])
+def test_padded_schedule_equals_packed_schedule(layout, lout):
+    """The work items depend on the sequence lengths only: a padded problem
+    schedules exactly what the packed problem of its used lengths does."""
+    for causal, wl, wr in ((True, -1, -1), (False, 17, 3), (False, -1, -1)):
+        p, uq, uk = _padded(layout=layout, layout_out=lout, causal=causal, wl=wl, wr=wr)
+        meta, fws, bws = B.sink_attn_metadata_padded(p, uq, uk)
+        cu_q = np.r_[0, np.cumsum(uq)].astype(np.int32)
+        cu_k = np.r_[0, np.cumsum(uk)].astype(np.int32)
+        _, (pm, _, _) = _meta(cu_q, cu_k, 8, 2, 128, causal, wl, wr)
+        for nw, ow, width in ((W_NFWD, W_FWDOFF, 6), (W_NBWD, W_BWDOFF, 6),
+                              (W_NDEC, W_DECOFF, 5)):
+            assert _items(meta, nw, ow, width) == _items(pm, nw, ow, width)
+        assert meta[W_MODE] == pm[W_MODE]
+        lay = B.LAYOUTS
+        assert list(meta[W_LAYOUT:W_LAYOUT + 5]) == [lay[layout], lay[lout or layout], 70, 130, 3]
+        # D [Hq, B*S_q] covers the padding rows too
+        assert bws >= 8 * 3 * 70 * 4
+
+
+def test_padded_without_seqused():
+    p, _, _ = _padded(uq=None, uk=None)
+    assert p.max_seqlen_q == 70 and p.max_seqlen_k == 130
+    meta, _, _ = B.sink_attn_metadata_padded(p, None, None)
+    assert meta[W_LAYOUT + 4] == 0
+    cu_q = np.arange(4, dtype=np.int32) * 70
+    cu_k = np.arange(4, dtype=np.int32) * 130
+    _, (pm, _, _) = _meta(cu_q, cu_k, 8, 2, 128, True)
+    assert _items(meta, W_NFWD, W_FWDOFF) == _items(pm, W_NFWD, W_FWDOFF)
+
+
+def test_padded_metadata_rejects():
+    p, uq, uk = _padded()
+
+    def status(prob, a=uq, b=uk):
+        with pytest.raises(B.SinkAttnError) as e:
+            B.sink_attn_metadata_padded(prob, a, b)
+        return e.value.status
+
+    assert status(p, np.array([71, 0, 33], np.int32)) == B.E_INVALID    # used > S_q
+    assert status(p, uq, np.array([130, -1, 64], np.int32)) == B.E_INVALID
+    for field, value in (("total_q", 209), ("seq_k", 0), ("layout_out", 2), ("layout_q", 3),
+                         ("max_seqlen_q", 69), ("max_seqlen_k", 131)):
+        q, _, _ = _padded()
+        setattr(q, field, value)
+        assert status(q) == B.E_INVALID, field
+    q, _, _ = _padded(layout="BNSD", layout_out="BSND")
+    assert B.sink_attn_metadata_padded(q, uq, uk)[0][W_LAYOUT + 1] == B.BSND
+    # a padded problem through the packed metadata call, and the reverse
+    cu = np.array([0, 70, 140, 210], np.int32)
+    with pytest.raises(B.SinkAttnError) as e:
+        B.sink_attn_metadata(p, cu, cu)
+    assert e.value.status == B.E_INVALID
+    t = B.make_problem(cu, cu, 8, 2, 128, True)
+    assert status(t, None, None) == B.E_INVALID
+    t.seq_q = 70                     # TND with a padded row count
+    with pytest.raises(B.SinkAttnError) as e:
+        B.sink_attn_metadata(t, cu, cu)
+    assert e.value.status == B.E_INVALID
+
+
+def test_padded_fwd_bwd_argument_checks():
+    p, uq, uk = _padded()
+    meta, fws, bws = B.sink_attn_metadata_padded(p, uq, uk)
+
+    def fwd(prob, m, used_q=FAKE, used_k=FAKE, **kw):
+        a = dict(q=FAKE, out=FAKE)
+        a.update(kw)
+        return B.sink_attn_fwd_padded(prob, m, FAKE, a["q"], FAKE, FAKE, used_q, used_k, FAKE,
+                                      0.1, a["out"], FAKE, FAKE, 1 << 40, stream=0,
+                                      check=False)
+
+    def bwd(prob, m, used_q=FAKE, used_k=FAKE, dsink=FAKE):
+        return B.sink_attn_bwd_padded(prob, m, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      used_q, used_k, FAKE, 0.1, FAKE, FAKE, FAKE, dsink,
+                                      FAKE, 1 << 40, stream=0, check=False)
+
+    assert fwd(p, meta, q=None) == B.E_INVALID
+    assert fwd(p, meta, out=FAKE + 2) == B.E_INVALID
+    assert fwd(p, meta, used_q=None) == B.E_META_MISMATCH     # the table had seqused_q
+    assert bwd(p, meta, used_k=None) == B.E_META_MISMATCH
+    assert bwd(p, meta, dsink=None) == B.E_INVALID
+    other, _, _ = _padded(layout="BNSD")
+    assert fwd(other, meta) == B.E_META_MISMATCH               # layout differs
+    # the packed calls refuse padded problems and tables, and the reverse
+    assert _fwd(p, meta) == B.E_INVALID
+    assert _bwd(p, meta) == B.E_INVALID
+    cu = np.array([0, 40, 100], np.int32)
+    t, (tmeta, _, _) = _meta(cu, cu, 8, 2, 128, True)
+    assert fwd(t, tmeta, None, None) == B.E_INVALID
+    assert bwd(t, tmeta, None, None) == B.E_INVALID

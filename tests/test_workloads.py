@@ -3,6 +3,7 @@ recipes (lengths, ranges, shapes)."""
 import math
 
 import numpy as np
+import pytest
 import torch
 
 from softmax_sink_amd import workloads as W
@@ -58,3 +59,26 @@ def test_length_recipes():
     lq, lk = rng.integers(1, 17, 64), rng.integers(512, 32769, 64)
     assert lq.min() >= 1 and lq.max() <= 16 and lk.min() >= 512 and lk.max() <= 32768
     assert (lq <= lk).all()
+
+
+def test_pad_rows_places_every_row():
+    """Row i of sequence b (packed index cu[b] + i) lands at [b, i] in BSND
+    and [b, :, i] in BNSD (the page's (B, S, N, D) / (B, N, S, D) shapes);
+    every other row holds the fill value."""
+    cu = np.array([0, 3, 3, 8], np.int32)
+    T, N, D, S = 8, 2, 4, 6
+    x = (np.arange(T * N * D, dtype=np.float32) + 1).reshape(T, N, D)
+    bsnd = W.pad_rows(x, cu, S, "BSND", -1.0)
+    bnsd = W.pad_rows(x, cu, S, "BNSD", -1.0)
+    assert bsnd.shape == (3, S, N, D) and bnsd.shape == (3, N, S, D)
+    seen = 0
+    for b in range(3):
+        for i in range(S):
+            for n in range(N):
+                live = i < cu[b + 1] - cu[b]
+                want = x[cu[b] + i, n] if live else np.full(D, -1.0, np.float32)
+                assert (bsnd[b, i, n] == want).all() and (bnsd[b, n, i] == want).all()
+                seen += live
+    assert seen == T * N
+    with pytest.raises(ValueError):
+        W.pad_rows(x, cu, S, "TND", 0.0)
