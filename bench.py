@@ -4,10 +4,11 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                 [--no-cpu-baseline]
 
 One step = the whole hot path over one batch: the host tile schedule
-(sink_attn_metadata, or sink_attn_metadata_paged) and its copy to the
-device, the forward (sink_attn_fwd, or sink_attn_fwd_paged reading a paged
-K/V cache) and, for training workloads, the backward (sink_attn_bwd), all
-through the C ABI on torch's current stream. Inputs are resident in HBM
+(sink_attn_metadata, sink_attn_metadata_paged or sink_attn_metadata_padded)
+and its copy to the device, the forward (sink_attn_fwd, sink_attn_fwd_paged
+reading a paged K/V cache, or sink_attn_fwd_padded for a batch-padded
+layout) and, for training workloads, the backward (sink_attn_bwd or
+sink_attn_bwd_padded), all through the C ABI on torch's current stream. Inputs are resident in HBM
 before timing starts. Prints one JSON line.
 
 FLOPs count only kept (query row, key, q-head) pairs: 4*D per pair forward,
@@ -15,6 +16,7 @@ FLOPs count only kept (query row, key, q-head) pairs: 4*D per pair forward,
 once plus q, out, lse.
 """
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -30,7 +32,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 METRIC = "sink-attention fwd+bwd TFLOP/s and % of bf16 MFMA peak, varlen THD causal"
-TRAIN = {"train_varlen", "gqa_window"}
+TRAIN = {"train_varlen", "gqa_window", "gqa_window_bnsd", "train_varlen_d256"}
 
 
 def kept_pairs(cu_q, cu_k, causal, wl, wr):
@@ -221,8 +223,21 @@ def main():
     train = args.workload in TRAIN
     paged = args.workload == "decode_paged"
     decode = args.workload in ("decode_softmax_n", "decode_paged")
+    padded = p.meta.get("layout")          # "BNSD": a batch-padded layout
     D, Hq, Hk = p.head_dim, p.num_heads_q, p.num_heads_k
-    q = to_dev(p, "q")
+    if padded:
+        lens_q, lens_k = np.diff(p.cu_q), np.diff(p.cu_k)
+        seq_q, seq_k = int(lens_q.max()), int(lens_k.max())
+        assert (lens_q == seq_q).all() and (lens_k == seq_k).all()
+        # device copies in the padded layout; p itself stays packed (the
+        # oracle's sample reads it)
+        src = dataclasses.replace(p, **{
+            name: W.pad_rows(getattr(p, name), cu, seq, padded, 0)
+            for name, cu, seq in (("q", p.cu_q, seq_q), ("k", p.cu_k, seq_k),
+                                  ("v", p.cu_k, seq_k), ("dout", p.cu_q, seq_q))})
+    else:
+        src = p
+    q = to_dev(src, "q")
     if paged:
         layout = p.meta["paged"]
         kv_desc = B.PagedKV(layout.block_size, layout.block_table.shape[1], layout.num_blocks)
@@ -235,8 +250,8 @@ def main():
         bt_dev = torch.from_numpy(bt_host).cuda()
         used_dev = torch.from_numpy(used_host).cuda()
     else:
-        k, v = to_dev(p, "k"), to_dev(p, "v")
-    dout = to_dev(p, "dout") if train else None
+        k, v = to_dev(src, "k"), to_dev(src, "v")
+    dout = to_dev(src, "dout") if train else None
     sinks = torch.from_numpy(p.sinks).cuda()
     scale = float(p.scale)
     dtype_code = B.BF16 if p.dtype == "bf16" else B.FP32
@@ -249,6 +264,11 @@ def main():
                                        p.win_right, dtype_code)
         meta0, fws = B.sink_attn_metadata_paged(problem, kv_desc, p.cu_q, used_host, bt_host)
         bws = 0
+    elif padded:
+        problem = B.make_problem_padded(p.batch, seq_q, seq_k, None, None, Hq, Hk, D,
+                                        p.causal, p.win_left, p.win_right, dtype_code,
+                                        padded)
+        meta0, fws, bws = B.sink_attn_metadata_padded(problem, None, None)
     else:
         meta0, fws, bws = B.sink_attn_metadata(problem, p.cu_q, p.cu_k)
     # two pinned host / device metadata buffers, alternated across steps
@@ -256,7 +276,8 @@ def main():
     meta_dev = [torch.empty(len(meta0), dtype=torch.int32, device="cuda") for _ in range(2)]
     copied = [None, None]
     out = torch.empty_like(q)
-    lse = torch.empty(Hq, p.total_q, dtype=torch.float32, device="cuda")
+    lse = (torch.empty(p.batch, Hq, seq_q, dtype=torch.float32, device="cuda") if padded
+           else torch.empty(Hq, p.total_q, dtype=torch.float32, device="cuda"))
     fwd_ws = torch.empty(max(fws, 1), dtype=torch.uint8, device="cuda")
     if train:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -273,6 +294,8 @@ def main():
         mh = meta_host[slot].numpy()
         if paged:
             m, _ = B.sink_attn_metadata_paged(problem, kv_desc, cq, used_host, bt_host)
+        elif padded:
+            m, _, _ = B.sink_attn_metadata_padded(problem, None, None)
         else:
             m, _, _ = B.sink_attn_metadata(problem, cq, ck)
         mh[:] = m
@@ -286,6 +309,9 @@ def main():
         if paged:
             B.sink_attn_fwd_paged(problem, kv_desc, mh, meta_dev[slot], q, k, v, bt_dev,
                                   cu_q_dev, used_dev, sinks, scale, out, lse, fwd_ws, fws)
+        elif padded:
+            B.sink_attn_fwd_padded(problem, mh, meta_dev[slot], q, k, v, None, None, sinks,
+                                   scale, out, lse, fwd_ws, fws)
         else:
             B.sink_attn_fwd(problem, mh, meta_dev[slot], q, k, v, cu_q_dev, cu_k_dev, sinks,
                             scale, out, lse, fwd_ws, fws)
@@ -296,8 +322,14 @@ def main():
                 b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 B.sink_attn_arm_timing(b0, b1)
                 main_events.append(("fwd", s0, s1))
-            B.sink_attn_bwd(problem, mh, meta_dev[slot], dout, q, k, v, out, lse, cu_q_dev,
-                            cu_k_dev, sinks, scale, dq, dk, dv, dsink, bwd_ws, bws)
+            if padded:
+                B.sink_attn_bwd_padded(problem, mh, meta_dev[slot], dout, q, k, v, out, lse,
+                                       None, None, sinks, scale, dq, dk, dv, dsink, bwd_ws,
+                                       bws)
+            else:
+                B.sink_attn_bwd(problem, mh, meta_dev[slot], dout, q, k, v, out, lse,
+                                cu_q_dev, cu_k_dev, sinks, scale, dq, dk, dv, dsink, bwd_ws,
+                                bws)
             if timed:
                 main_events.append(("bwd", b0, b1))
 
@@ -358,6 +390,7 @@ def main():
                    "total_k": p.total_k, "heads_q": Hq, "heads_kv": Hk, "head_dim": D,
                    "causal": p.causal, "window": [p.win_left, p.win_right],
                    "seed": p.seed, "kept_pairs": pairs,
+                   **({"layout": padded} if padded else {}),
                    "passes": "metadata+fwd+bwd" if train else "metadata+fwd",
                    **({"kv_pages": {"block_size": layout.block_size,
                                     "num_blocks": layout.num_blocks}} if paged else {})},

@@ -101,7 +101,8 @@ typedef enum { SINK_ATTN_TND = 0, SINK_ATTN_BSND = 1, SINK_ATTN_BNSD = 2 } sink_
 
 /* The problem, passed by pointer and not retained. Checks: 0 < batch <
  * 65536; total_q, total_k, num_heads_q, num_heads_k > 0; num_heads_q %
- * num_heads_k == 0 (CANN page, axis validation); head_dim in {64, 128};
+ * num_heads_k == 0 (CANN page, axis validation); head_dim in {64, 128,
+ * 256} (the page's set; 256 with bf16 or fp16 only);
  * max_seqlen_q/k equal to the true maxima of the host sequence lengths
  * (cu_seqlens differences, or seqused / S in a padded layout; the CANN page
  * leaves a mismatch undefined; here it is E_INVALID); causal in {0,1};
@@ -316,7 +317,7 @@ sink_attn_status sink_attn_bwd_padded(const sink_attn_problem* p,
  * part_dtype adds that rounding of each partial to the result. Enqueues on
  * `stream`; allocates nothing. Errors: E_INVALID (num_parts outside
  * [1, 4096], total_q or num_heads_q <= 0, NULL or misaligned pointers),
- * E_UNSUPPORTED (head_dim not 64 or 128, unknown dtype, more than 2^40
+ * E_UNSUPPORTED (head_dim not 64, 128 or 256, unknown dtype, more than 2^40
  * elements), E_HIP. */
 sink_attn_status sink_attn_merge(int32_t num_parts, int32_t total_q,
                                  int32_t num_heads_q, int32_t head_dim,

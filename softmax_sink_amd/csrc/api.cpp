@@ -367,7 +367,7 @@ sink_attn_status sink_attn_merge(int32_t num_parts, int32_t total_q,
                                  hipStream_t stream) {
   if (num_parts <= 0 || num_parts > kMaxMergeParts || total_q <= 0 || num_heads_q <= 0)
     return SINK_ATTN_E_INVALID;
-  if (head_dim != 64 && head_dim != 128) return SINK_ATTN_E_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return SINK_ATTN_E_UNSUPPORTED;
   const auto known = [](int32_t d) {
     return d == SINK_ATTN_FP32 || d == SINK_ATTN_BF16 || d == SINK_ATTN_FP16;
   };

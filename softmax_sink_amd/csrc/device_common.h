@@ -86,30 +86,48 @@ __device__ __forceinline__ float half_max(float x) {
 // D = 128 (256-byte rows): f = 4(r%4) + (r/4)%4, a permutation of 0..15 on
 //   any 16 consecutive rows whose upper two bits differ on 4 consecutive rows.
 // D = 64 (128-byte rows, two rows per bank sweep): f = 4((r/2)%2) + (r/4)%4.
+// D = 256: the 64-row tile is kept as two [64 x 128] slices (columns 0..127,
+//   then 128..255), each laid out as a D = 128 tile, so that every access
+//   pattern and tile transfer of D = 128 carries over slice by slice.
 // ---------------------------------------------------------------------------
 template <int D>
 __device__ __forceinline__ int swz(int r) {
+  static_assert(D == 64 || D == 128, "row swizzle of one slice");
   if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
   else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+template <int D>
+constexpr int kSliceCols = D > 128 ? 128 : D;                 // columns per slice
+template <int D>
+constexpr int kSliceBytes = 64 * kSliceCols<D> * 2;          // bytes per 64-row slice
+
+// Byte offset of the 16-byte chunk `chunk` (columns 8*chunk..+7) of row r.
+template <int D>
+__device__ __forceinline__ int chunk_off(int r, int chunk) {
+  constexpr int DS = kSliceCols<D>;
+  constexpr int CPS = DS / 8;                                 // chunks per slice row
+  if constexpr (D > DS)
+    return (chunk / CPS) * kSliceBytes<D> + r * (DS * 2) + (((chunk % CPS) ^ swz<DS>(r)) << 4);
+  else
+    return r * (D * 2) + ((chunk ^ swz<D>(r)) << 4);
 }
 
 // Byte offset of element (r, col) (col a multiple of 4 elements).
 template <int D>
 __device__ __forceinline__ int tile_off(int r, int col) {
-  const int chunk = col >> 3;
-  return r * (D * 2) + ((chunk ^ swz<D>(r)) << 4) + ((col & 7) << 1);
+  return chunk_off<D>(r, col >> 3) + ((col & 7) << 1);
 }
 
 // 16-byte chunk (8 elements starting at column 8*chunk) of row r.
 template <int D, typename T = bf16>
 __device__ __forceinline__ vec8<T> lds_row_chunk(const char* tile, int r, int chunk) {
-  return *reinterpret_cast<const vec8<T>*>(tile + r * (D * 2) +
-                                           ((chunk ^ swz<D>(r)) << 4));
+  return *reinterpret_cast<const vec8<T>*>(tile + chunk_off<D>(r, chunk));
 }
 
 template <int D>
 __device__ __forceinline__ void lds_store_chunk(char* tile, int r, int chunk, u32x4 v) {
-  *reinterpret_cast<u32x4*>(tile + r * (D * 2) + ((chunk ^ swz<D>(r)) << 4)) = v;
+  *reinterpret_cast<u32x4*>(tile + chunk_off<D>(r, chunk)) = v;
 }
 
 __device__ __forceinline__ s16x4 ds_read_tr(const char* p) {

@@ -35,7 +35,7 @@ using namespace dev;
 
 
 template <int D, typename T>
-__global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, D > 128 ? 1 : 2) void fwd_prefill_kernel(FwdArgs a) {
   constexpr int BN = kFwdBN;
   constexpr int NT = D / 16;            // K chunks of the QK^T product
   constexpr int NB = D / 32;            // 32-column blocks of O^T
@@ -215,7 +215,7 @@ constexpr int kMaxItemPages = 132;  // pages a kDecChunk-key item can touch (blo
 static_assert(kMaxItemPages >= 1 + (kDecChunk + 14) / 16, "page list too short");
 
 template <int D, typename T, bool PAGED>
-__global__ __launch_bounds__(256, 2) void fwd_split_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, D > 128 ? 1 : 2) void fwd_split_kernel(FwdArgs a) {
   constexpr int BN = kDecBN;
   constexpr int NT = D / 16;
   constexpr int NB = D / 32;
@@ -356,9 +356,11 @@ __global__ __launch_bounds__(256, 2) void fwd_split_kernel(FwdArgs a) {
 
   // merge the two key halves: waves 2,3 hand (m, l, O) to waves 0,1
   l = l + half_partner(l);
-  float* xo = reinterpret_cast<float*>(lds0);        // [2 waves][NB*16][64 lanes]
-  float* xm = xo + 2 * NB * 16 * 64;                   // [2 waves][64 lanes]
+  // (both buffers are idle: the last step waited for its loads and synced)
+  float* xo = reinterpret_cast<float*>(lds0);        // [2 waves][NB*16][64 lanes]: all of lds0
+  float* xm = reinterpret_cast<float*>(lds1);        // [2 waves][64 lanes]
   float* xl = xm + 2 * 64;
+  static_assert(2 * NB * 16 * 64 * 4 <= 2 * TILE, "O exchange fits one buffer");
   if (kh == 1) {
 #pragma unroll
     for (int n = 0; n < NB; ++n)
@@ -457,15 +459,22 @@ hipError_t launch_fwd_d(const FwdArgs& a, int mode, hipStream_t s, const TimingH
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t launch_fwd_t(const FwdArgs& a, int head_dim, int mode, hipStream_t s,
+                        const TimingHook& t) {
+  switch (head_dim) {
+    case 64: return launch_fwd_d<64, T>(a, mode, s, t);
+    case 128: return launch_fwd_d<128, T>(a, mode, s, t);
+    default: return launch_fwd_d<256, T>(a, mode, s, t);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_fwd_16(const FwdArgs& a, int head_dim, int dtype, int mode, hipStream_t s,
                          const TimingHook& t) {
-  if (dtype == SINK_ATTN_FP16)
-    return head_dim == 128 ? launch_fwd_d<128, f16>(a, mode, s, t)
-                           : launch_fwd_d<64, f16>(a, mode, s, t);
-  return head_dim == 128 ? launch_fwd_d<128, bf16>(a, mode, s, t)
-                         : launch_fwd_d<64, bf16>(a, mode, s, t);
+  return dtype == SINK_ATTN_FP16 ? launch_fwd_t<f16>(a, head_dim, mode, s, t)
+                                 : launch_fwd_t<bf16>(a, head_dim, mode, s, t);
 }
 
 }  // namespace sinkattn

@@ -118,7 +118,11 @@ hipError_t launch_d(const MergeArgs& a, int out_dtype, hipStream_t s) {
 
 template <typename TP>
 hipError_t launch_tp(const MergeArgs& a, int head_dim, int out_dtype, hipStream_t s) {
-  return head_dim == 128 ? launch_d<128, TP>(a, out_dtype, s) : launch_d<64, TP>(a, out_dtype, s);
+  switch (head_dim) {
+    case 64: return launch_d<64, TP>(a, out_dtype, s);
+    case 128: return launch_d<128, TP>(a, out_dtype, s);
+    default: return launch_d<256, TP>(a, out_dtype, s);
+  }
 }
 
 }  // namespace

@@ -174,7 +174,10 @@ sink_attn_status validate_problem(const sink_attn_problem* p) {
   if (p->causal && p->win_right > 0) return SINK_ATTN_E_INVALID;
   if (p->dtype != SINK_ATTN_FP32 && p->dtype != SINK_ATTN_BF16 && p->dtype != SINK_ATTN_FP16)
     return SINK_ATTN_E_UNSUPPORTED;
-  if (p->head_dim != 64 && p->head_dim != 128) return SINK_ATTN_E_UNSUPPORTED;
+  // D = 256 runs on the 16-bit MFMA kernels only
+  if (p->head_dim != 64 && p->head_dim != 128 &&
+      !(p->head_dim == 256 && p->dtype != SINK_ATTN_FP32))
+    return SINK_ATTN_E_UNSUPPORTED;
   // layouts: out follows q, except BNSD q with BSND out
   if (p->layout_q != SINK_ATTN_TND && p->layout_q != SINK_ATTN_BSND &&
       p->layout_q != SINK_ATTN_BNSD)

@@ -35,17 +35,20 @@ constexpr int kBufferWord3 = 0x00020000;
 // passes. Rows at or past the end of the sequence fetch its last row (finite,
 // in bounds; every consumer gives them zero weight). Completion is waited
 // for with wait_vmem() before the barrier that publishes the tile.
+// A D = 256 tile moves as its two 128-column slices, one after the other.
 template <int D, int THREADS = 256>
 struct TileDma {
-  static constexpr int kPer = 64 * D / 8 / THREADS;      // passes per tile
-  static constexpr int kRowsPerPass = THREADS / (D / 8);
+  static constexpr int DS = kSliceCols<D>;
+  static constexpr int kSlices = D / DS;
+  static constexpr int kPer = 64 * DS / 8 / THREADS;     // passes per slice
+  static constexpr int kRowsPerPass = THREADS / (DS / 8);
   static_assert(kRowsPerPass % 16 == 0, "a pass must keep the row swizzle");
   int lrow;             // this lane's row in pass 0
   int lcol;             // byte offset of the logical chunk this lane fetches
   int wave_off;         // byte offset of this wave's 1 KB run within a pass
   __device__ __forceinline__ void init() {
-    lrow = threadIdx.x / (D / 8);
-    lcol = (((threadIdx.x % (D / 8)) ^ swz<D>(lrow)) * 16);
+    lrow = threadIdx.x / (DS / 8);
+    lcol = (((threadIdx.x % (DS / 8)) ^ swz<DS>(lrow)) * 16);
     wave_off = __builtin_amdgcn_readfirstlane((threadIdx.x / 64) * 1024);
   }
   // One tile transfer, prepared (uniform values only) and then issued in
@@ -57,8 +60,8 @@ struct TileDma {
     int lim;            // last valid row, relative to the tile's first row
     int stride2;        // row stride in bytes
   };
-  // rows [row0, row0 + 64) of the tensor at `base` into `tile`; the caller
-  // guarantees row0 < nrows
+  // rows [row0, row0 + 64) of one slice (columns from `base` on) of the
+  // tensor at `base` into `tile`; the caller guarantees row0 < nrows
   template <typename T>
   __device__ __forceinline__ Tile prepare(const T* base, int64_t stride, int row0, int nrows,
                                           char* tile) const {
@@ -92,7 +95,9 @@ struct TileDma {
   template <typename T>
   __device__ __forceinline__ void load(const T* base, int64_t stride, int row0, int nrows,
                                        char* tile) const {
-    issue<0, kPer>(prepare(base, stride, row0, nrows, tile));
+#pragma unroll
+    for (int sl = 0; sl < kSlices; ++sl)
+      issue<0, kPer>(prepare(base + sl * DS, stride, row0, nrows, tile + sl * kSliceBytes<D>));
   }
 };
 
@@ -108,13 +113,15 @@ struct TileDma {
 // here because the numerator stays below 2^12.
 template <int D, int THREADS = 256>
 struct PagedTileDma {
-  static constexpr int kPer = 64 * D / 8 / THREADS;
-  static constexpr int kRowsPerPass = THREADS / (D / 8);
+  static constexpr int DS = kSliceCols<D>;
+  static constexpr int kSlices = D / DS;
+  static constexpr int kPer = 64 * DS / 8 / THREADS;
+  static constexpr int kRowsPerPass = THREADS / (DS / 8);
   static_assert(kRowsPerPass % 16 == 0, "a pass must keep the row swizzle");
   int lrow, lcol, wave_off;
   __device__ __forceinline__ void init() {
-    lrow = threadIdx.x / (D / 8);
-    lcol = (((threadIdx.x % (D / 8)) ^ swz<D>(lrow)) * 16);
+    lrow = threadIdx.x / (DS / 8);
+    lcol = (((threadIdx.x % (DS / 8)) ^ swz<DS>(lrow)) * 16);
     wave_off = __builtin_amdgcn_readfirstlane((threadIdx.x / 64) * 1024);
   }
   template <typename T>
@@ -133,13 +140,15 @@ struct PagedTileDma {
       const int64_t phys = pages[pi];
       const char* src = reinterpret_cast<const char*>(
                             cache + (phys * block_size + slot) * row_stride + head_off) + lcol;
-      asm volatile(
-          "s_mov_b32 m0, %1\n\t"
-          "s_nop 0\n\t"
-          "global_load_lds_dwordx4 %0, off"
-          :
-          : "v"(src), "s"(lds0 + s * THREADS * 16)
-          : "memory", "m0");
+#pragma unroll
+      for (int sl = 0; sl < kSlices; ++sl)
+        asm volatile(
+            "s_mov_b32 m0, %1\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %0, off"
+            :
+            : "v"(src + sl * DS * 2), "s"(lds0 + sl * kSliceBytes<D> + s * THREADS * 16)
+            : "memory", "m0");
     }
   }
 };

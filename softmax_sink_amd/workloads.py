@@ -24,7 +24,10 @@ with window (1024, 0), forward + backward) and ``decode_softmax_n`` (64
 sequences, q length uniform in [1, 16], kv length uniform in [512, 32768],
 32/8 heads, D 128, bottom-right causal, n = 0.5), plus ``decode_paged``:
 the same draw with its keys and values scattered into 16-row pages of a
-paged cache in random page order (``paged_layout``, ``scatter_to_pages``).
+paged cache in random page order (``paged_layout``, ``scatter_to_pages``),
+``gqa_window_bnsd``: the ``gqa_window`` draw laid out as BNSD
+(``pad_rows``), and ``train_varlen_d256``: the ``train_varlen`` lengths with
+16/16 heads of head_dim 256.
 """
 
 import math
@@ -274,10 +277,24 @@ def config(name):
         lens = _train_lengths(rng)
         return make_problem(3, lens, lens, 32, 32, 128, causal=True,
                             name=name, rng=rng)
+    if name == "train_varlen_d256":
+        # the training lengths at head_dim 256 with half the heads (the same
+        # FLOPs per kept pair and head-row bytes as train_varlen)
+        rng = np.random.default_rng(3)
+        lens = _train_lengths(rng)
+        return make_problem(3, lens, lens, 16, 16, 256, causal=True,
+                            name=name, rng=rng)
     if name == "gqa_window":
         lens = np.full(4, 8192)
         return make_problem(4, lens, lens, 64, 8, 128, causal=True,
                             win_left=1024, win_right=0, name=name)
+    if name == "gqa_window_bnsd":
+        # the same draw, handed over in the batch-padded BNSD layout (every
+        # sequence is 8192 rows, so no row is padding)
+        p = config("gqa_window")
+        p.name = name
+        p.meta["layout"] = "BNSD"
+        return p
     if name in ("decode_softmax_n", "decode_paged"):
         rng = np.random.default_rng(5)
         lq = rng.integers(1, 17, 64)

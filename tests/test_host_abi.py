@@ -449,3 +449,16 @@ def test_padded_fwd_bwd_argument_checks():
     t, (tmeta, _, _) = _meta(cu, cu, 8, 2, 128, True)
     assert fwd(t, tmeta, None, None) == B.E_INVALID
     assert bwd(t, tmeta, None, None) == B.E_INVALID
+
+
+def test_head_dim_256_for_16_bit_types_only():
+    cu = np.array([0, 100, 300], np.int32)
+    for dt in (B.BF16, B.FP16):
+        p = B.make_problem(cu, cu, 8, 2, 256, True, dtype=dt)
+        meta, fws, bws = B.sink_attn_metadata(p, cu, cu)
+        assert meta[5] == 256
+    for d, dt in ((256, B.FP32), (512, B.BF16), (192, B.BF16)):
+        p = B.make_problem(cu, cu, 8, 2, d, True, dtype=dt)
+        with pytest.raises(B.SinkAttnError) as e:
+            B.sink_attn_metadata(p, cu, cu)
+        assert e.value.status == B.E_UNSUPPORTED
