@@ -47,6 +47,7 @@ class GpuRun:
         dq, dk, dv, ds = B.backward(self.plan, self.dout, self.q, self.k, self.v, self.out,
                                     self.lse, self.sinks, self.scale)
         torch.cuda.synchronize()
+        self.dq, self.dk, self.dv, self.dsink = dq, dk, dv, ds
         f = lambda t: t.float().cpu().numpy().astype(np.float64)
         return f(dq), f(dk), f(dv), (ds.cpu().numpy().astype(np.float64) if ds is not None else None)
 

@@ -40,7 +40,8 @@ def test_prefill_varlen_full_size():
 # therefore compared as a relative L2 error over a set of heads.
 @pytest.mark.parametrize("name,heads,dsink_heads", [
     ("train_varlen", [5], list(range(0, 32, 4))),
-    ("gqa_window", list(range(24, 32)), list(range(24, 32)))])
+    ("gqa_window", list(range(24, 32)), list(range(24, 32))),
+    ("train_varlen_d256", [3], list(range(0, 16, 2)))])
 def test_training_workloads_full_size(name, heads, dsink_heads):
     p = W.config(name)
     log(f"{name}: Tq={p.total_q} lens={np.diff(p.cu_q).tolist()} H={p.num_heads_q}/{p.num_heads_k}")
@@ -83,3 +84,32 @@ def test_decode_softmax_n_full_size():
     log(f"  sequences {seqs}: max|d out|={e_out:.3e} max|d lse|={e_lse:.3e}")
     tol = TOL["bf16"]
     assert e_out <= tol["out"] and e_lse <= tol["lse"]
+
+
+def test_gqa_window_bnsd_equals_packed_bitwise():
+    """The gqa_window workload handed over in the BNSD layout (as the
+    gqa_window_bnsd bench line does) runs the same arithmetic as the packed
+    call: every output equals the packed one bit for bit."""
+    from softmax_sink_amd import binding as B
+    p = W.config("gqa_window_bnsd")
+    S = int(np.diff(p.cu_q)[0])
+    log(f"gqa_window_bnsd: B={p.batch} S={S} H={p.num_heads_q}/{p.num_heads_k}")
+    g = GpuRun(p)
+    g.fwd()
+    g.bwd()
+    plan = B.PaddedPlan(p.batch, S, S, None, None, p.num_heads_q, p.num_heads_k, p.head_dim,
+                        p.causal, (p.win_left, p.win_right), p.dtype, "BNSD")
+    # BNSD views of the packed device tensors: [T, N, D] -> [B, N, S, D]
+    bnsd = lambda t: t.view(p.batch, S, t.shape[1], t.shape[2]).transpose(1, 2).contiguous()
+    packed = lambda t: t.transpose(1, 2).reshape(p.batch * S, t.shape[1], t.shape[3])
+    q, k, v, do = bnsd(g.q), bnsd(g.k), bnsd(g.v), bnsd(g.dout)
+    out, lse = B.forward_padded(plan, q, k, v, g.sinks, g.scale)
+    dq, dk, dv, ds = B.backward_padded(plan, do, q, k, v, out, lse, g.sinks, g.scale)
+    torch.cuda.synchronize()
+    same = lambda a, b: torch.equal(a.contiguous().view(torch.int16), b.contiguous().view(torch.int16))
+    assert same(packed(out), g.out)
+    # lse [B, Hq, S] against the packed [Hq, Tq]
+    assert torch.equal(lse.transpose(0, 1).reshape(p.num_heads_q, -1), g.lse)
+    assert same(packed(dq), g.dq) and same(packed(dk), g.dk) and same(packed(dv), g.dv)
+    assert torch.equal(ds, g.dsink)
+    log("  BNSD forward and backward equal the packed results bit for bit")
