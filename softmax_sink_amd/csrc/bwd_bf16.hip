@@ -39,7 +39,8 @@ using namespace dev;
 // query tile). Role 1 works one step behind role 0, so three Q tiles are
 // live at once (role 0's, role 1's and the one in flight) and two dO tiles;
 // lse and D rows travel with their Q and dO stages. P of a step is handed
-// from role 0 to role 1 as 16-bit MFMA fragments ("dumps", one per parity).
+// from role 0 to role 1 as 16-bit MFMA fragments ("dumps", one per parity):
+// 2 query blocks x 2 halves x 4 key blocks of 32 fragments of 64 lanes x 16 B.
 template <int D>
 struct KvSmem {
   static constexpr int kTile = kBwdBM * D * 2;          // one [64][D] 16-bit tile
@@ -47,12 +48,20 @@ struct KvSmem {
   static constexpr int off_do = off_q + 3 * kTile;      // dO of step j: stage j % 2
   static constexpr int off_lse = off_do + 2 * kTile;    // 3 x [64] fp32, log2 domain
   static constexpr int off_dval = off_lse + 3 * 256;    // 2 x [64] fp32
-  static constexpr int kHalfDump = 8 * 64 * 16;         // 8 fragments x 64 lanes x 16 B
+  static constexpr int kDump = 16 * 64 * 16;            // one step's P: 16 fragments
   static constexpr int off_p = off_dval + 2 * 256;      // P of step j: dump j % 2
-  static constexpr int bytes = off_p + 2 * 2 * kHalfDump;
+  static constexpr int bytes = off_p + 2 * kDump;
 };
 
-constexpr int kKvThreads = 256;                   // 4 waves: 2 roles x 2 key halves
+// 32-key MFMA blocks per wave of the dK/dV kernel. With 2 (4 waves, one per
+// SIMD, up to 512 registers each) every LDS operand feeds two MFMAs; with 1
+// (8 waves, two per SIMD) each wave needs half the registers and the two
+// waves of a SIMD fill each other's waits. 1 is the faster by a fifth on the
+// training workloads (4.25 -> 3.38 ms and 3.36 -> 2.57 ms for dK/dV, same
+// results bit for bit).
+constexpr int kKvKB = 1;
+constexpr int kKvWavesPerRole = kBwdBN / (32 * kKvKB);
+constexpr int kKvThreads = 64 * 2 * kKvWavesPerRole;
 
 // (q-head offset g, query tile t) of consecutive steps: t runs fastest.
 struct StepIdx {
@@ -62,13 +71,13 @@ struct StepIdx {
   }
 };
 
-// dK/dV, key-tile outer, one wave per SIMD. Wave w owns the 64 keys
-// 64(w&1)..64(w&1)+63 of the item in role w>>1:
+// dK/dV, key-tile outer. Wave w owns the 32 KB keys starting at
+// 32 KB (w % W) of the item (W waves per role) in role w / W:
 //   role 0: S = Q K^T, P = 2^(S scale log2e - lse log2e), dV^T += dO^T P
 //   role 1: dP = dO V^T, dS = P (dP - D),                  dK^T += Q^T dS
-// A wave covers two 32-key MFMA blocks, so every operand read from LDS feeds
-// two MFMAs (one per key block): 1 LDS read per MFMA in total, against ~4.7
-// cycles of LDS issue per wave-instruction and 8 cycles of MFMA per CU.
+// With KB = 2 (one wave per SIMD) every operand read from LDS feeds two MFMAs
+// (one per key block); with KB = 1 (the build's choice) a SIMD runs two
+// waves, which hide each other's waits, at one MFMA per LDS read.
 // In iteration i, role 0 computes S and P of step i and the dV update of
 // step i-1 (whose P it still holds), so the exponentials of step i can issue
 // between the dV MFMAs; role 1 computes all of step i-1 with the P that
@@ -78,6 +87,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using S = KvSmem<D>;
   constexpr int NT = D / 16;
   constexpr int NB = D / 32;
+  constexpr int KB = kKvKB;
+  constexpr int W = kKvWavesPerRole;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int item = blockIdx.x / a.hk;
@@ -90,19 +101,19 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int G = a.group;
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int role = w >> 1, kh = w & 1;
+  const int role = w / W, kq = w % W;
   const int hl = lane >> 5, c = lane & 31;
-  const int jbase = kt * kBwdBN + 64 * kh + c;   // this lane's key in block kb: jbase + 32 kb
+  const int jbase = kt * kBwdBN + 32 * KB * kq + c;  // this lane's key in block kb: jbase + 32 kb
 
   const int64_t kstride = a.g.k_row;
   const int64_t qstride = a.g.q_row;
   const int64_t koff = (int64_t)k0 * a.g.k_seq + hk * a.g.k_head;   // key row 0 of k / v / dk / dv
   // role 0 holds K rows (B operand of S = Q K^T), role 1 V rows (of dP = dO V^T)
   const T* fp = static_cast<const T*>(role == 0 ? a.k : a.v) + koff;
-  vec8<T> frag[2][NT];
-  int ilo[2], ihi[2];
+  vec8<T> frag[KB][NT];
+  int ilo[KB], ihi[KB];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < KB; ++kb) {
     const int j = jbase + 32 * kb;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -111,9 +122,11 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     key_row_range(j, lq, lk, a.causal, a.win_left, a.win_right, ilo[kb], ihi[kb]);
   }
 
-  f32x16 acc[NB][2];                             // role 0: dV^T, role 1: dK^T
+  f32x16 acc[NB][KB];                            // role 0: dV^T, role 1: dK^T
 #pragma unroll
-  for (int n = 0; n < NB; ++n) acc[n][0] = acc[n][1] = f32x16{};
+  for (int n = 0; n < NB; ++n)
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) acc[n][kb] = f32x16{};
   const int nq = qt_hi - qt_lo;
   const int steps = nq * G;
   const float c2 = a.scale * kLog2e;
@@ -125,6 +138,11 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // workspace, [Hq, rows]): rbase + g*total_q + r
   const int64_t lbase = (int64_t)q0 * a.g.l_seq + (int64_t)hk * G * a.g.l_head;
   const int64_t rbase = ((int64_t)hk * G) * a.total_q + q0;
+  // P fragment (query block qb, key block kb, half h) of this wave's keys
+  const int frag0 = kq * KB;                     // first 32-key block of this wave
+  auto dump_at = [&](char* dump, int qb, int kb, int h) __attribute__((always_inline)) {
+    return dump + ((((qb * 4 + frag0 + kb) * 2 + h) * 64) + lane) * 16;
+  };
 
   TileDma<D, kKvThreads> dma;
   dma.init();
@@ -195,9 +213,11 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // The two roles run separate loops with the same barrier sequence (one
   // per iteration), so that each is register-allocated on its own.
   if (steps > 0 && role == 0) {
-    vec8<T> pf[2][2][2];                          // P of the previous step [qb][kb][half]
+    vec8<T> pf[2][KB][2];                         // P of the previous step [qb][kb][half]
 #pragma unroll
-    for (int f = 0; f < 8; ++f) pf[f >> 2][(f >> 1) & 1][f & 1] = vec8<T>{};
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) pf[qb][kb][0] = pf[qb][kb][1] = vec8<T>{};
     int qs = 0;                                  // it % 3
     for (int it = 0; it <= steps; ++it) {
       const int qs_next = qs == 2 ? 0 : qs + 1;
@@ -206,7 +226,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       const char* q_l = smem + S::off_q + qs * S::kTile;
       const float* lse_l = reinterpret_cast<const float*>(smem + S::off_lse + qs * 256);
       const char* dop_l = smem + S::off_do + (ds ^ 1) * S::kTile;
-      char* dump = smem + S::off_p + (2 * ds + kh) * S::kHalfDump;
+      char* dump = smem + S::off_p + ds * S::kDump;
       const int qt = qt_lo + sd.t;
       const bool partial = it < steps && (qt < qf_lo || qt >= qf_hi);
       // One 32-row query block at a time: S and P of step it, and the half
@@ -216,20 +236,23 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       // stage holds stale (or never written) data; that P is never read.
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        f32x16 x0 = f32x16{}, x1 = f32x16{};
+        f32x16 x[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) x[kb] = f32x16{};
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           const vec8<T> qa = lds_row_chunk<D, T>(q_l, 32 * qb + c, 2 * t + hl);
-          x0 = mfma32(qa, frag[0][t], x0);
-          x1 = mfma32(qa, frag[1][t], x1);
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) x[kb] = mfma32(qa, frag[kb][t], x[kb]);
         }
-        sched_mfma_pipeline<2 * NT, 2, 1, 3>();
+        sched_mfma_pipeline<KB * NT, KB, 1, 3>();
         if (partial) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int i = qt * kBwdBM + 32 * qb + 8 * (r >> 2) + 4 * hl + (r & 3);
-            if (i < ilo[0] || i > ihi[0]) x0[r] = kNegInf;
-            if (i < ilo[1] || i > ihi[1]) x1[r] = kNegInf;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+              if (i < ilo[kb] || i > ihi[kb]) x[kb][r] = kNegInf;
           }
         }
 #pragma unroll
@@ -237,25 +260,26 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
           for (int db = 0; db < NB; ++db) {
             const vec8<T> da = lds_col_operand<D, T>(dop_l, 16 * (2 * qb + h), 32 * db);
-            acc[db][0] = mfma32(da, pf[qb][0][h], acc[db][0]);
-            acc[db][1] = mfma32(da, pf[qb][1][h], acc[db][1]);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+              acc[db][kb] = mfma32(da, pf[qb][kb][h], acc[db][kb]);
           }
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_l + 32 * qb + 8 * g4 + 4 * hl);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x0[4 * g4 + e] = exp2_hw(__builtin_fmaf(x0[4 * g4 + e], c2, -l4[e]));
-            x1[4 * g4 + e] = exp2_hw(__builtin_fmaf(x1[4 * g4 + e], c2, -l4[e]));
-          }
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+              x[kb][4 * g4 + e] = exp2_hw(__builtin_fmaf(x[kb][4 * g4 + e], c2, -l4[e]));
         }
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          pf[qb][0][h] = frag_half<T>(x0, h);
-          pf[qb][1][h] = frag_half<T>(x1, h);
-          *reinterpret_cast<vec8<T>*>(dump + ((4 * qb + h) * 64 + lane) * 16) = pf[qb][0][h];
-          *reinterpret_cast<vec8<T>*>(dump + ((4 * qb + 2 + h) * 64 + lane) * 16) = pf[qb][1][h];
-        }
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            pf[qb][kb][h] = frag_half<T>(x[kb], h);
+            *reinterpret_cast<vec8<T>*>(dump_at(dump, qb, kb, h)) = pf[qb][kb][h];
+          }
       }
       finish(it, qs_next, ds);
       qs = qs_next;
@@ -273,21 +297,25 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         const char* do_l = smem + S::off_do + (ds ^ 1) * S::kTile;
         const float* dv_l = reinterpret_cast<const float*>(smem + S::off_dval + (ds ^ 1) * 256);
         const char* qq_l = smem + S::off_q + qs_prev * S::kTile;
-        const char* dump = smem + S::off_p + (2 * (ds ^ 1) + kh) * S::kHalfDump;
+        char* dump = smem + S::off_p + (ds ^ 1) * S::kDump;
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-          f32x16 x0 = f32x16{}, x1 = f32x16{};
+          f32x16 x[KB];
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) x[kb] = f32x16{};
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
             const vec8<T> ga = lds_row_chunk<D, T>(do_l, 32 * qb + c, 2 * t + hl);
-            x0 = mfma32(ga, frag[0][t], x0);
-            x1 = mfma32(ga, frag[1][t], x1);
-          }
-          sched_mfma_pipeline<2 * NT, 2, 1, 3>();
-          vec8<T> pp[4];                          // [kb][half]
 #pragma unroll
-          for (int f = 0; f < 4; ++f)
-            pp[f] = *reinterpret_cast<const vec8<T>*>(dump + ((4 * qb + f) * 64 + lane) * 16);
+            for (int kb = 0; kb < KB; ++kb) x[kb] = mfma32(ga, frag[kb][t], x[kb]);
+          }
+          sched_mfma_pipeline<KB * NT, KB, 1, 3>();
+          vec8<T> pp[KB][2];                      // [kb][half]
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              pp[kb][h] = *reinterpret_cast<const vec8<T>*>(dump_at(dump, qb, kb, h));
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
             const f32x4 d4 = *reinterpret_cast<const f32x4*>(dv_l + 32 * qb + 8 * g4 + 4 * hl);
@@ -295,22 +323,24 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
             for (int e = 0; e < 4; ++e) {
               const int r = 4 * g4 + e;
               // dK is scaled at the end
-              x0[r] = (float)pp[r >> 3][r & 7] * (x0[r] - d4[e]);
-              x1[r] = (float)pp[2 + (r >> 3)][r & 7] * (x1[r] - d4[e]);
+#pragma unroll
+              for (int kb = 0; kb < KB; ++kb)
+                x[kb][r] = (float)pp[kb][r >> 3][r & 7] * (x[kb][r] - d4[e]);
             }
           }
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            const vec8<T> s0 = frag_half<T>(x0, h);
-            const vec8<T> s1 = frag_half<T>(x1, h);
+            vec8<T> sf[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) sf[kb] = frag_half<T>(x[kb], h);
 #pragma unroll
             for (int db = 0; db < NB; ++db) {
               const vec8<T> qa = lds_col_operand<D, T>(qq_l, 16 * (2 * qb + h), 32 * db);
-              acc[db][0] = mfma32(qa, s0, acc[db][0]);
-              acc[db][1] = mfma32(qa, s1, acc[db][1]);
+#pragma unroll
+              for (int kb = 0; kb < KB; ++kb) acc[db][kb] = mfma32(qa, sf[kb], acc[db][kb]);
             }
           }
-          sched_mfma_pipeline<4 * NB, 2, 2, 2>();
+          sched_mfma_pipeline<2 * KB * NB, KB, 2, 2>();
         }
       }
       finish(it, qs_next, ds);
@@ -321,7 +351,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // role 0 writes dV, role 1 dK (times the softmax scale)
   const float sc = role == 0 ? 1.f : a.scale;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < KB; ++kb) {
     const int j = jbase + 32 * kb;
     if (j < lk) {
       T* dst = static_cast<T*>(role == 0 ? a.dv : a.dk) + koff + (int64_t)j * kstride;
