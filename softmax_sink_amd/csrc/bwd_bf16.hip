@@ -71,8 +71,9 @@ struct StepIdx {
   }
 };
 
-// dK/dV, key-tile outer. Wave w owns the 32 KB keys starting at
-// 32 KB (w % W) of the item (W waves per role) in role w / W:
+// dK/dV, key-tile outer. With W = kKvWavesPerRole waves per role and
+// KB = kKvKB key blocks per wave, wave w owns keys 32*KB*(w % W) .. +32*KB-1
+// of the item in role w / W:
 //   role 0: S = Q K^T, P = 2^(S scale log2e - lse log2e), dV^T += dO^T P
 //   role 1: dP = dO V^T, dS = P (dP - D),                  dK^T += Q^T dS
 // With KB = 2 (one wave per SIMD) every operand read from LDS feeds two MFMAs
