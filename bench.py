@@ -221,7 +221,7 @@ def main():
         del src, dst
     p = W.config(args.workload)
     train = args.workload in TRAIN
-    paged = args.workload == "decode_paged"
+    paged = "paged" in p.meta
     decode = args.workload in ("decode_softmax_n", "decode_paged")
     padded = p.meta.get("layout")          # "BNSD": a batch-padded layout
     D, Hq, Hk = p.head_dim, p.num_heads_q, p.num_heads_k
@@ -383,7 +383,7 @@ def main():
     res = {
         "metric": METRIC if train else
         ("sink-attention decode forward TFLOP/s (split-KV" + (", paged K/V)" if paged else ")")
-         if decode else "sink-attention forward TFLOP/s"),
+         if decode else "sink-attention forward TFLOP/s" + (" (paged K/V)" if paged else "")),
         "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": p.dtype, "data": "synthetic",

@@ -209,10 +209,11 @@ typedef struct {
  * sum and p->max_seqlen_k their maximum) and the HOST copy of the block
  * table, whose entries for the pages in use must lie in [0, num_blocks):
  * they are checked here and hashed into the header, and the device copy
- * passed to sink_attn_fwd_paged must equal it (not checked there). Only
- * short query groups are supported (max_seqlen_q * num_heads_q /
- * num_heads_k <= 64, the split-KV path) and only bf16 or fp16: otherwise
- * E_UNSUPPORTED. The table can only be used with sink_attn_fwd_paged.
+ * passed to sink_attn_fwd_paged must equal it (not checked there). Short
+ * query groups (max_seqlen_q * num_heads_q / num_heads_k <= 64) run the
+ * split-KV decode path, longer ones the tiled prefill path (a chunked
+ * prefill against the cache); bf16 or fp16 only (fp32: E_UNSUPPORTED). The
+ * table can only be used with sink_attn_fwd_paged.
  * Errors: E_INVALID, E_UNSUPPORTED, E_BUFFER_TOO_SMALL. */
 sink_attn_status sink_attn_metadata_paged(const sink_attn_problem* p,
                                           const sink_attn_paged_kv* kv,

@@ -231,9 +231,7 @@ sink_attn_status sink_attn_metadata_paged(const sink_attn_problem* p,
   if (st != SINK_ATTN_OK) return st;
   st = validate_cu_seqlens(*p, cu_seqlens_q_host, cu_k.data());
   if (st != SINK_ATTN_OK) return st;
-  if (p->dtype == SINK_ATTN_FP32 ||
-      static_cast<int64_t>(p->max_seqlen_q) * (p->num_heads_q / p->num_heads_k) > kDecMaxRows)
-    return SINK_ATTN_E_UNSUPPORTED;
+  if (p->dtype == SINK_ATTN_FP32) return SINK_ATTN_E_UNSUPPORTED;
   if (meta_host && meta_capacity_words < 0) return SINK_ATTN_E_INVALID;
   const PagedInfo info{*kv, block_table_host};
   int64_t bwd_bytes = 0;
@@ -302,11 +300,16 @@ sink_attn_status sink_attn_fwd_paged(const sink_attn_problem* p,
   const int64_t need = header_i64(meta_host, kFwdWsLo, kFwdWsHi);
   if (workspace_bytes < need) return SINK_ATTN_E_BUFFER_TOO_SMALL;
   if (need > 0 && (!workspace || !aligned16(workspace))) return SINK_ATTN_E_INVALID;
-  if (meta_host[kMode] != kModeDecode) return SINK_ATTN_E_UNSUPPORTED;
+  const int mode = meta_host[kMode];
 
   FwdArgs a = fwd_args(p, q, k_cache, v_cache, cu_seqlens_q, nullptr, nullptr, nullptr,
                        sink_logits, scale, out, lse);
-  if (!decode_args(a, p, meta_host, meta_dev, workspace)) return SINK_ATTN_E_META_MISMATCH;
+  if (mode == kModeDecode) {
+    if (!decode_args(a, p, meta_host, meta_dev, workspace)) return SINK_ATTN_E_META_MISMATCH;
+  } else {
+    a.items = meta_dev + meta_host[kFwdOff];
+    a.n_items = meta_host[kNFwd];
+  }
   a.block_table = block_table;
   a.seqused_k = seqused_kv;
   a.page_size = kv->block_size;
@@ -314,7 +317,7 @@ sink_attn_status sink_attn_fwd_paged(const sink_attn_problem* p,
   a.page_magic = static_cast<uint32_t>(((uint64_t(1) << 32) + kv->block_size - 1) /
                                        static_cast<uint64_t>(kv->block_size));
   const TimingHook t = take_timing();
-  const hipError_t e = launch_fwd_16(a, p->head_dim, p->dtype, kModeDecode, stream, t);
+  const hipError_t e = launch_fwd_16(a, p->head_dim, p->dtype, mode, stream, t);
   return e == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_E_HIP;
 }
 

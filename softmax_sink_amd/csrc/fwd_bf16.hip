@@ -34,16 +34,28 @@ namespace {
 using namespace dev;
 
 
-template <int D, typename T>
+// Block-table entries a kernel keeps in LDS: those of one 2048-key span
+// (kDecChunk keys; block size >= 16).
+constexpr int kMaxItemPages = 132;
+static_assert(kMaxItemPages >= 1 + (kDecChunk + 14) / 16, "page list too short");
+constexpr int kPageSpan = kDecChunk;
+
+// PAGED: keys and values come from paged caches through the block table
+// (only the tile addresses change). The block-table entries of the current
+// kPageSpan-key span of the sequence sit in LDS and are refilled when the
+// tile prefetch crosses into the next span.
+template <int D, typename T, bool PAGED>
 __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void fwd_prefill_kernel(FwdArgs a) {
   constexpr int BN = kFwdBN;
   constexpr int NT = D / 16;            // K chunks of the QK^T product
   constexpr int NB = D / 32;            // 32-column blocks of O^T
   constexpr int TILE = BN * D * 2;      // bytes per K or V tile
+  static_assert(kPageSpan % BN == 0, "tiles do not straddle page spans");
   // two buffers as two objects, so that the compiler can tell a prefetch
   // into one from reads of the other and does not wait for the prefetch
   __shared__ __attribute__((aligned(16))) char lds0[2 * TILE];
   __shared__ __attribute__((aligned(16))) char lds1[2 * TILE];
+  __shared__ int pages[PAGED ? kMaxItemPages : 1];
 
   const int item = blockIdx.x / a.hq;
   const int h = head_of_slot(blockIdx.x % a.hq, a.hq);
@@ -51,7 +63,9 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void fwd_prefill_kernel(FwdAr
   const int b = it[0], qt = it[1], kt_lo = it[2], kt_hi = it[3];
   const int kf_lo = it[4], kf_hi = it[5];
   const int q0 = q_start(a, b), lq = q_len(a, b);
-  const int k0 = k_start(a, b), lk = k_len(a, b);
+  int k0 = 0, lk;
+  if constexpr (PAGED) lk = a.seqused_k[b];
+  else { k0 = k_start(a, b); lk = k_len(a, b); }
   const int hk = h / a.group;
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -85,11 +99,39 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void fwd_prefill_kernel(FwdAr
   row_key_range(i, lq, lk, a.causal, a.win_left, a.win_right, jlo, jhi);
 
   TileDma<D> kl, vl;
+  PagedTileDma<D> pl;
   kl.init();
   vl.init();
+  pl.init();
+  // paged: block-table entries of the span holding key `key0` into LDS
+  // (the caller syncs before: no tile of the previous span is being issued)
+  int span0 = -1, off0 = 0;
+  auto fill_pages = [&](int key0) __attribute__((always_inline)) {
+    span0 = key0 / kPageSpan * kPageSpan;
+    const int p0 = span0 / a.page_size;
+    off0 = span0 - p0 * a.page_size;
+    const int span1 = min(lk, span0 + kPageSpan);
+    const int np = (off0 + span1 - span0 + a.page_size - 1) / a.page_size;
+    const int* bt = a.block_table + (int64_t)b * a.page_cols + p0;
+    for (int t = threadIdx.x; t < np; t += 256) pages[t] = bt[t];
+    __syncthreads();
+  };
+  // K and V rows [row0, row0 + BN) into one LDS buffer
+  auto load_kv = [&](int row0, char* dst) __attribute__((always_inline)) {
+    if constexpr (PAGED) {
+      const int last = min(lk, span0 + kPageSpan) - 1;
+      pl.load(static_cast<const T*>(a.k), (int64_t)hk * D, (int64_t)a.hk * D, pages, off0, span0,
+              row0, last, a.page_size, a.page_magic, dst);
+      pl.load(static_cast<const T*>(a.v), (int64_t)hk * D, (int64_t)a.hk * D, pages, off0, span0,
+              row0, last, a.page_size, a.page_magic, dst + TILE);
+    } else {
+      kl.load(kp, kstride, row0, lk, dst);
+      vl.load(vp, kstride, row0, lk, dst + TILE);
+    }
+  };
   if (kt_lo < kt_hi) {
-    kl.load(kp, kstride, kt_lo * BN, lk, lds0);
-    vl.load(vp, kstride, kt_lo * BN, lk, lds0 + TILE);
+    if constexpr (PAGED) fill_pages(kt_lo * BN);
+    load_kv(kt_lo * BN, lds0);
   }
   wait_vmem();
   __syncthreads();
@@ -100,8 +142,12 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void fwd_prefill_kernel(FwdAr
     constexpr int CUR = decltype(cur_c)::value;
     const bool more = kt + 1 < kt_hi;
     if (more) {
-      kl.load(kp, kstride, (kt + 1) * BN, lk, CUR == 0 ? lds1 : lds0);
-      vl.load(vp, kstride, (kt + 1) * BN, lk, (CUR == 0 ? lds1 : lds0) + TILE);
+      if constexpr (PAGED) {
+        // every wave issued tile kt (in the previous step) before the
+        // barrier that ended it, so the page list may be replaced now
+        if ((kt + 1) * BN >= span0 + kPageSpan) fill_pages((kt + 1) * BN);
+      }
+      load_kv((kt + 1) * BN, CUR == 0 ? lds1 : lds0);
     }
     const char* kt_lds = CUR == 0 ? lds0 : lds1;
     const char* vt_lds = (CUR == 0 ? lds0 : lds1) + TILE;
@@ -211,8 +257,6 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void fwd_prefill_kernel(FwdAr
 // is query row i of q-head hk*G + g. PAGED: keys and values come from paged
 // caches through the block table (only the tile addresses change).
 // ---------------------------------------------------------------------------
-constexpr int kMaxItemPages = 132;  // pages a kDecChunk-key item can touch (block size >= 16)
-static_assert(kMaxItemPages >= 1 + (kDecChunk + 14) / 16, "page list too short");
 
 template <int D, typename T, bool PAGED>
 __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void fwd_split_kernel(FwdArgs a) {
@@ -453,7 +497,10 @@ hipError_t launch_fwd_d(const FwdArgs& a, int mode, hipStream_t s, const TimingH
     hipLaunchKernelGGL((fwd_combine_kernel<D, T>), dim3((rows + 3) / 4), dim3(256), 0, s, a);
   } else {
     if (th.start) hipEventRecord(th.start, s);
-    hipLaunchKernelGGL((fwd_prefill_kernel<D, T>), dim3(a.n_items * a.hq), dim3(256), 0, s, a);
+    if (a.block_table)
+      hipLaunchKernelGGL((fwd_prefill_kernel<D, T, true>), dim3(a.n_items * a.hq), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((fwd_prefill_kernel<D, T, false>), dim3(a.n_items * a.hq), dim3(256), 0, s, a);
     if (th.stop) hipEventRecord(th.stop, s);
   }
   return hipGetLastError();

@@ -25,7 +25,9 @@ sequences, q length uniform in [1, 16], kv length uniform in [512, 32768],
 32/8 heads, D 128, bottom-right causal, n = 0.5), plus ``decode_paged``:
 the same draw with its keys and values scattered into 16-row pages of a
 paged cache in random page order (``paged_layout``, ``scatter_to_pages``),
-``gqa_window_bnsd``: the ``gqa_window`` draw laid out as BNSD
+``prefill_paged``: the ``prefill_varlen`` draw with its keys and values in
+16-row pages (a prefill against a paged cache), ``gqa_window_bnsd``: the
+``gqa_window`` draw laid out as BNSD
 (``pad_rows``), and ``train_varlen_d256``: the ``train_varlen`` lengths with
 16/16 heads of head_dim 256.
 """
@@ -267,11 +269,14 @@ def config(name):
         return make_problem(1, [128], [128], 1, 1, 64, dtype="fp32",
                             causal=False, sinks=0.0,
                             scale=np.float32(0.125), name=name)
-    if name == "prefill_varlen":
+    if name in ("prefill_varlen", "prefill_paged"):
         rng = np.random.default_rng(2)
         lens = rng.integers(64, 2049, 16)
-        return make_problem(2, lens, lens, 32, 32, 128, causal=True,
-                            name=name, rng=rng)
+        p = make_problem(2, lens, lens, 32, 32, 128, causal=True,
+                         name=name, rng=rng)
+        if name == "prefill_paged":
+            p.meta["paged"] = paged_layout(p.cu_k, DECODE_PAGE_ROWS, DECODE_PAGE_SEED)
+        return p
     if name == "train_varlen":
         rng = np.random.default_rng(3)
         lens = _train_lengths(rng)

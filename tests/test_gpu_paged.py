@@ -1,7 +1,7 @@
-"""Paged-KV forward (the split-KV decode path reading pages through a block
-table) through the C ABI: against the oracle, which gathers the pages
-itself, and bit for bit against the contiguous forward on the same keys and
-values. Needs an MI355X."""
+"""Paged-KV forward (the split-KV decode path, and the tiled path for long
+query groups, reading pages through a block table) through the C ABI:
+against the oracle, which gathers the pages itself, and bit for bit against
+the contiguous forward on the same keys and values. Needs an MI355X."""
 import math
 
 import numpy as np
@@ -66,6 +66,28 @@ def test_paged_decode_matches_oracle_and_contiguous(bs, D):
     assert e_out <= TOL["bf16"]["out"] and e_lse <= TOL["bf16"]["lse"]
 
 
+@pytest.mark.parametrize("bs,D", [(16, 128), (48, 128), (1024, 64), (32, 256)])
+def test_paged_prefill_matches_oracle_and_contiguous(bs, D):
+    # long query groups take the tiled forward; keys past 2048 make it refill
+    # its page list in the middle of a work item
+    wl = 1500 if bs == 48 else -1
+    p = W.make_problem(80 + bs + D, [300, 1, 129, 700], [300, 900, 2500, 4500], 8, 2, D,
+                       causal=True, win_left=wl, name=f"paged_prefill_bs{bs}_d{D}")
+    layout = W.paged_layout(p.cu_k, bs, seed=80 + bs, spare=4)
+    plan = B.PagedPlan(p.cu_q, layout.seqused, layout.block_table, layout.block_size,
+                       layout.num_blocks, p.num_heads_q, p.num_heads_k, D, True, (wl, -1))
+    assert int(plan.meta[14]) == 0          # the tiled (prefill) schedule
+    kc, vc, out, lse = _check_paged(p, layout)
+    kg, cu_k = O.gather_paged(W.bf16_bits_to_f32(kc), layout.block_table, layout.seqused, bs)
+    vg, _ = O.gather_paged(W.bf16_bits_to_f32(vc), layout.block_table, layout.seqused, bs)
+    ro, rl, _ = O.sink_attention_forward(p.as_f32("q"), kg, vg, p.cu_q, cu_k,
+                                         p.sinks.astype(np.float64), float(p.scale), True,
+                                         wl, -1)
+    e_out, e_lse = max_abs(out, ro), max_abs(lse, rl)
+    log(f"  vs oracle: max|d out|={e_out:.3e} max|d lse|={e_lse:.3e}")
+    assert e_out <= TOL["bf16"]["out"] and e_lse <= TOL["bf16"]["lse"]
+
+
 def test_paged_shared_prefix_pages_and_window():
     # two sequences share their first two pages (a common prompt prefix);
     # sliding window, no sink on some heads
@@ -96,5 +118,16 @@ def test_decode_paged_full_size():
         f"bs={layout.block_size}")
     kc, vc, out, lse = _check_paged(p, layout)
     s_out, s_lse = sampled_rows_error(p, out, lse, 256, 5)
+    log(f"  sampled rows vs oracle: {s_out:.3e} {s_lse:.3e}")
+    assert s_out <= TOL["bf16"]["out"] and s_lse <= TOL["bf16"]["lse"]
+
+
+def test_prefill_paged_full_size():
+    p = W.config("prefill_paged")
+    layout = p.meta["paged"]
+    log(f"prefill_paged: Tq={p.total_q} Tk={p.total_k} pages={layout.num_blocks} "
+        f"bs={layout.block_size}")
+    kc, vc, out, lse = _check_paged(p, layout)
+    s_out, s_lse = sampled_rows_error(p, out, lse, 256, 6)
     log(f"  sampled rows vs oracle: {s_out:.3e} {s_lse:.3e}")
     assert s_out <= TOL["bf16"]["out"] and s_lse <= TOL["bf16"]["lse"]

@@ -267,11 +267,25 @@ def test_paged_metadata_rejects():
     wrong_total = B.make_problem_paged(cu_q, used, 8, 2, 128, True)
     wrong_total.total_k += 1
     assert status(p=wrong_total) == B.E_INVALID
-    long_q = np.array([0, 40, 41, 42], np.int32)           # 40 rows x 4 heads > 64
-    assert status(p=B.make_problem_paged(long_q, used, 8, 2, 128, True), cu_q=long_q) == \
-        B.E_UNSUPPORTED
     assert status(p=B.make_problem_paged(cu_q, used, 8, 2, 128, True, dtype=B.FP32)) == \
         B.E_UNSUPPORTED
+    padded = B.make_problem_paged(cu_q, used, 8, 2, 128, True)
+    padded.layout_q = padded.layout_out = B.BSND
+    assert status(p=padded) == B.E_INVALID
+
+
+def test_paged_long_queries_take_the_prefill_schedule():
+    """40 query rows x 4 heads of a group exceed one split-KV group: the
+    paged table then carries the tiled forward items of the same lengths."""
+    p, kv, cu_q, used, table = _paged_case()
+    long_q = np.array([0, 40, 41, 42], np.int32)
+    pl = B.make_problem_paged(long_q, used, 8, 2, 128, True)
+    meta, fws = B.sink_attn_metadata_paged(pl, kv, long_q, used, table)
+    cu_k = np.r_[0, np.cumsum(used)].astype(np.int32)
+    _, (mc, _, _) = _meta(long_q, cu_k, 8, 2, 128, True)
+    assert meta[W_MODE] == 0 and mc[W_MODE] == 0 and fws == 0
+    assert _items(meta, W_NFWD, W_FWDOFF) == _items(mc, W_NFWD, W_FWDOFF)
+    assert meta[W_PAGED] == 1
 
 
 def test_paged_entries_only_checked_where_used():
