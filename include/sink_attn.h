@@ -79,7 +79,7 @@
 extern "C" {
 #endif
 
-#define SINK_ATTN_ABI_VERSION 3
+#define SINK_ATTN_ABI_VERSION 4
 
 typedef enum {
   SINK_ATTN_OK = 0,
@@ -189,19 +189,24 @@ sink_attn_status sink_attn_bwd(const sink_attn_problem* p,
 /* Paged K/V cache: the keys and values of a sequence live in fixed-size
  * pages of one cache tensor, found through a block table ("CANN
  * ops-transformer: flash_attn", Paged Attention parameter group and the
- * PA_BBND k/v layout; "hf-attention-normalizers", Differentiable Paged
- * Attention: the kernel reads physical pages through the block table and
- * never gathers a copy). Layouts:
- *   k_cache, v_cache : [num_blocks, block_size, num_heads_k, head_dim] (dtype)
+ * PA_BBND and PA_BNBD k/v layouts; "hf-attention-normalizers",
+ * Differentiable Paged Attention: the kernel reads physical pages through
+ * the block table and never gathers a copy). Layouts:
+ *   k_cache, v_cache : PA_BBND [num_blocks, block_size, num_heads_k, head_dim]
+ *                      or PA_BNBD [num_blocks, num_heads_k, block_size,
+ *                      head_dim] (dtype)
  *   block_table      : [batch, max_blocks_per_seq] int32
  *   seqused_kv       : [batch] int32, keys of sequence b
  * Key row r < seqused_kv[b] of sequence b is slot r % block_size of page
  * block_table[b][r / block_size]. Pages may be shared between sequences and
- * appear in any order. Only the forward is paged. */
+ * appear in any order. Only the forward is paged; the page's PA_NZ layout
+ * (16-wide column fractals) is not taken. */
+typedef enum { SINK_ATTN_PA_BBND = 0, SINK_ATTN_PA_BNBD = 1 } sink_attn_cache_layout;
 typedef struct {
   int32_t block_size;          /* 16..1024 and a multiple of 16 (CANN page) */
   int32_t max_blocks_per_seq;  /* columns of block_table, > 0              */
   int32_t num_blocks;          /* pages in each cache tensor, > 0          */
+  int32_t layout;              /* sink_attn_cache_layout                  */
 } sink_attn_paged_kv;
 
 /* Tile schedule for a paged forward. As sink_attn_metadata, with the key

@@ -54,8 +54,13 @@ class Problem(ctypes.Structure):
         "layout_q", "layout_out", "seq_q", "seq_k")]
 
 
+PA_BBND, PA_BNBD = 0, 1
+CACHE_LAYOUTS = {"BBND": PA_BBND, "BNBD": PA_BNBD}
+
+
 class PagedKV(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in ("block_size", "max_blocks_per_seq", "num_blocks")]
+    _fields_ = [(n, ctypes.c_int32) for n in ("block_size", "max_blocks_per_seq", "num_blocks",
+                                              "layout")]
 
 
 _lib = None
@@ -370,12 +375,13 @@ class PagedPlan:
 
     def __init__(self, cu_seqlens_q, seqused_kv, block_table, block_size, num_blocks,
                  num_heads_q, num_heads_k, head_dim, causal, window=(-1, -1),
-                 device="cuda", dtype="bf16"):
+                 device="cuda", dtype="bf16", cache_layout="BBND"):
         import torch
         self.cu_q_host = np.asarray(cu_seqlens_q, dtype=np.int32)
         self.seqused_host = np.asarray(seqused_kv, dtype=np.int32)
         self.block_table_host = np.ascontiguousarray(block_table, dtype=np.int32)
-        self.kv = PagedKV(int(block_size), int(self.block_table_host.shape[1]), int(num_blocks))
+        self.kv = PagedKV(int(block_size), int(self.block_table_host.shape[1]), int(num_blocks),
+                          CACHE_LAYOUTS[cache_layout])
         self.problem = make_problem_paged(self.cu_q_host, self.seqused_host, num_heads_q,
                                           num_heads_k, head_dim, causal, window[0],
                                           window[1], dtype_code(dtype))
@@ -440,7 +446,7 @@ def forward(plan, q, k, v, sinks, scale):
 
 def forward_paged(plan, q, k_cache, v_cache, sinks, scale):
     """Paged forward -> out, lse (k_cache, v_cache: [num_blocks, block_size,
-    Hk, D] bf16)."""
+    Hk, D], or [num_blocks, Hk, block_size, D] for a BNBD plan)."""
     import torch
     out = torch.empty_like(q)
     lse = torch.empty(plan.problem.num_heads_q, plan.problem.total_q,

@@ -316,6 +316,10 @@ sink_attn_status sink_attn_fwd_paged(const sink_attn_problem* p,
   a.page_cols = kv->max_blocks_per_seq;
   a.page_magic = static_cast<uint32_t>(((uint64_t(1) << 32) + kv->block_size - 1) /
                                        static_cast<uint64_t>(kv->block_size));
+  const int64_t bs = kv->block_size, hkn = p->num_heads_k, d = p->head_dim;
+  a.page_stride = bs * hkn * d;
+  if (kv->layout == SINK_ATTN_PA_BNBD) { a.page_row = d; a.page_head = bs * d; }
+  else { a.page_row = hkn * d; a.page_head = d; }
   const TimingHook t = take_timing();
   const hipError_t e = launch_fwd_16(a, p->head_dim, p->dtype, mode, stream, t);
   return e == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_E_HIP;

@@ -120,9 +120,9 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void fwd_prefill_kernel(FwdAr
   auto load_kv = [&](int row0, char* dst) __attribute__((always_inline)) {
     if constexpr (PAGED) {
       const int last = min(lk, span0 + kPageSpan) - 1;
-      pl.load(static_cast<const T*>(a.k), (int64_t)hk * D, (int64_t)a.hk * D, pages, off0, span0,
+      pl.load(static_cast<const T*>(a.k), hk * a.page_head, a.page_row, a.page_stride, pages, off0, span0,
               row0, last, a.page_size, a.page_magic, dst);
-      pl.load(static_cast<const T*>(a.v), (int64_t)hk * D, (int64_t)a.hk * D, pages, off0, span0,
+      pl.load(static_cast<const T*>(a.v), hk * a.page_head, a.page_row, a.page_stride, pages, off0, span0,
               row0, last, a.page_size, a.page_magic, dst + TILE);
     } else {
       kl.load(kp, kstride, row0, lk, dst);
@@ -327,10 +327,9 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void fwd_split_kernel(FwdArgs
   // K and V rows [row0, row0 + BN) of the item into one LDS buffer
   auto load_kv = [&](int row0, char* dst) __attribute__((always_inline)) {
     if constexpr (PAGED) {
-      // the cache layout is [num_blocks, block_size, Hk, D] whatever the q layout
-      pl.load(static_cast<const T*>(a.k), (int64_t)hk * D, (int64_t)a.hk * D, pages, off0, k_lo, row0,
+      pl.load(static_cast<const T*>(a.k), hk * a.page_head, a.page_row, a.page_stride, pages, off0, k_lo, row0,
               k_hi - 1, a.page_size, a.page_magic, dst);
-      pl.load(static_cast<const T*>(a.v), (int64_t)hk * D, (int64_t)a.hk * D, pages, off0, k_lo, row0,
+      pl.load(static_cast<const T*>(a.v), hk * a.page_head, a.page_row, a.page_stride, pages, off0, k_lo, row0,
               k_hi - 1, a.page_size, a.page_magic, dst + TILE);
     } else {
       kl.load(kp, kstride, row0, k_hi, dst);

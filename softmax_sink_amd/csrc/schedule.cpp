@@ -248,6 +248,7 @@ sink_attn_status validate_paged(const sink_attn_problem& p,
   const int64_t bs = kv->block_size;
   if (bs < 16 || bs > 1024 || bs % 16 != 0) return SINK_ATTN_E_INVALID;
   if (kv->max_blocks_per_seq <= 0 || kv->num_blocks <= 0) return SINK_ATTN_E_INVALID;
+  if (kv->layout != SINK_ATTN_PA_BBND && kv->layout != SINK_ATTN_PA_BNBD) return SINK_ATTN_E_INVALID;
   int64_t acc = 0;
   cu_k_out[0] = 0;
   for (int b = 0; b < p.batch; ++b) {
@@ -414,6 +415,7 @@ sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
     h[kPageSize] = paged->kv.block_size;
     h[kPageMaxBlocks] = paged->kv.max_blocks_per_seq;
     h[kPageNumBlocks] = paged->kv.num_blocks;
+    h[kPageLayout] = paged->kv.layout;
     h[kPageHash] = static_cast<int32_t>(hash);
   }
   int32_t* w = out + fwd_off;
@@ -443,7 +445,7 @@ sink_attn_status check_header(const sink_attn_problem& p, const int32_t* h,
     return SINK_ATTN_E_META_MISMATCH;
   if (h[kPaged] != (kv ? 1 : 0)) return SINK_ATTN_E_META_MISMATCH;
   if (kv && (h[kPageSize] != kv->block_size || h[kPageMaxBlocks] != kv->max_blocks_per_seq ||
-             h[kPageNumBlocks] != kv->num_blocks))
+             h[kPageNumBlocks] != kv->num_blocks || h[kPageLayout] != kv->layout))
     return SINK_ATTN_E_META_MISMATCH;
   return SINK_ATTN_OK;
 }

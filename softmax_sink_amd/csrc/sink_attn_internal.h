@@ -20,7 +20,7 @@ enum MetaWord : int {
   kFwdWsLo, kFwdWsHi, kBwdWsLo, kBwdWsHi, kCuHash, kMetaWords,
   kBwdPreBlocks,
   kPaged, kPageSize, kPageMaxBlocks, kPageNumBlocks, kPageHash,
-  kLayoutQ, kLayoutOut, kSeqQ, kSeqK, kUsedMask,
+  kLayoutQ, kLayoutOut, kSeqQ, kSeqK, kUsedMask, kPageLayout,
   kHeaderWords = 48
 };
 
@@ -136,6 +136,8 @@ struct FwdArgs {
   const int32_t* seqused_k;
   int page_size, page_cols;  // block_size, max_blocks_per_seq
   uint32_t page_magic;       // ceil(2^32 / block_size)
+  // element offset of (page p, slot s, kv-head h): p*page_stride + s*page_row + h*page_head
+  int64_t page_stride, page_row, page_head;
   int n_items;
   int batch, hq, hk, group, causal, win_left, win_right;
   int total_q, total_k;

@@ -102,11 +102,11 @@ struct TileDma {
 };
 
 // The same [64 x D] tile transfer for keys or values that live in a paged
-// cache ([num_blocks, block_size, Hk, D]): row r of the sequence is slot
-// (r - k_lo + off0) % block_size of the page pages[(r - k_lo + off0) /
-// block_size], where `pages` is an LDS copy of the block-table entries of
-// the work item, starting with the page that holds its first key k_lo at
-// slot off0. Rows past `row_last` fetch row_last. Each lane computes its own
+// cache: row r of the sequence is slot (r - k_lo + off0) % block_size of the
+// page pages[(r - k_lo + off0) / block_size], where `pages` is an LDS copy of
+// the block-table entries of the work item, starting with the page that
+// holds its first key k_lo at slot off0; (page p, slot s) of the kv-head
+// sits at element p * page_stride + s * row_stride + head_off of the cache. Rows past `row_last` fetch row_last. Each lane computes its own
 // 64-bit row address, so the FLAT form global_load_lds_dwordx4 is used, again
 // from inline assembly (no outputs; clobbers M0 and memory). The division by
 // block_size is a multiply-high with magic = ceil(2^32 / block_size), exact
@@ -126,7 +126,7 @@ struct PagedTileDma {
   }
   template <typename T>
   __device__ __forceinline__ void load(const T* cache, int64_t head_off, int64_t row_stride,
-                                       const int* pages, int off0, int k_lo, int row0,
+                                       int64_t page_stride, const int* pages, int off0, int k_lo, int row0,
                                        int row_last, int block_size, uint32_t magic,
                                        char* tile) const {
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
@@ -139,7 +139,7 @@ struct PagedTileDma {
       const int slot = (int)(num - pi * (uint32_t)block_size);
       const int64_t phys = pages[pi];
       const char* src = reinterpret_cast<const char*>(
-                            cache + (phys * block_size + slot) * row_stride + head_off) + lcol;
+                            cache + phys * page_stride + slot * row_stride + head_off) + lcol;
 #pragma unroll
       for (int sl = 0; sl < kSlices; ++sl)
         asm volatile(

@@ -196,10 +196,11 @@ def paged_layout(cu_k, block_size, seed, spare=0):
     return PagedLayout(int(block_size), table, lens.astype(np.int32), num_blocks)
 
 
-def scatter_to_pages(x, cu_k, layout):
-    """Packed rows x [Tk, ...] -> cache [num_blocks, block_size, ...] with
-    row r of sequence b in slot r % block_size of page
-    block_table[b, r // block_size]; slots no row maps to are 0."""
+def scatter_to_pages(x, cu_k, layout, cache_layout="BBND"):
+    """Packed rows x [Tk, Hk, D] -> cache [num_blocks, block_size, Hk, D]
+    (BBND; BNBD: [num_blocks, Hk, block_size, D]) with row r of sequence b
+    in slot r % block_size of page block_table[b, r // block_size]; slots no
+    row maps to are 0."""
     bs = layout.block_size
     cache = np.zeros((layout.num_blocks, bs) + x.shape[1:], dtype=x.dtype)
     for b in range(len(cu_k) - 1):
@@ -207,6 +208,10 @@ def scatter_to_pages(x, cu_k, layout):
         for pg in range((len(rows) + bs - 1) // bs):
             chunk = rows[pg * bs:(pg + 1) * bs]
             cache[layout.block_table[b, pg], :len(chunk)] = chunk
+    if cache_layout == "BNBD":
+        return np.ascontiguousarray(cache.transpose(0, 2, 1, 3))
+    if cache_layout != "BBND":
+        raise ValueError(cache_layout)
     return cache
 
 

@@ -106,3 +106,25 @@ def test_key_split_then_merge_equals_unsplit(dtype):
     e_lse = max_abs(lse.cpu().numpy(), rl)
     log(f"non-causal thirds ({dtype}): max|d out|={e_out:.3e} max|d lse|={e_lse:.3e}")
     assert e_out <= tol["out"] and e_lse <= tol["lse"]
+
+
+def test_cp_merge_full_size():
+    """The merge bench.py times (4 sink-free bf16 partials of 16640 tokens x
+    32 heads x D 128, seed 61), checked on 512 sampled tokens (every head)
+    against the oracle's merge of the same partials."""
+    from softmax_sink_amd import workloads as W
+    P, Hq, D = 4, 32, 128
+    Tq = W.config("prefill_varlen").total_q
+    outs, lses, sinks = W.merge_inputs(61, P, Tq, Hq, D)
+    po = torch.from_numpy(outs.view(np.int16)).view(torch.bfloat16).cuda()
+    out, lse = B.merge(po, torch.from_numpy(lses).cuda(), torch.from_numpy(sinks).cuda())
+    torch.cuda.synchronize()
+    idx = np.sort(np.random.default_rng(7).choice(Tq, 512, replace=False))
+    ro, rl = O.merge_partials(W.bf16_bits_to_f32(outs[:, idx]).astype(np.float64),
+                              lses[:, :, idx].astype(np.float64), sinks.astype(np.float64))
+    got = out[torch.from_numpy(idx).cuda()].float().cpu().numpy().astype(np.float64)
+    e_lse = max_abs(lse[:, torch.from_numpy(idx).cuda()].cpu().numpy(), rl)
+    mag = np.maximum(np.abs(ro), np.finfo(np.float32).tiny)
+    worst = float(np.max(np.abs(got - ro) / np.exp2(np.floor(np.log2(mag)) - 7)))
+    log(f"cp_merge full size: max|d lse|={e_lse:.3e}, worst error in bf16 steps {worst:.3f}")
+    assert e_lse <= TOL["fp32"]["lse"] and worst <= 1.0

@@ -131,3 +131,25 @@ def test_prefill_paged_full_size():
     s_out, s_lse = sampled_rows_error(p, out, lse, 256, 6)
     log(f"  sampled rows vs oracle: {s_out:.3e} {s_lse:.3e}")
     assert s_out <= TOL["bf16"]["out"] and s_lse <= TOL["bf16"]["lse"]
+
+
+@pytest.mark.parametrize("lq", [[1, 5, 16, 3], [300, 1, 129, 700]])
+def test_paged_bnbd_cache_equals_bbnd(lq):
+    """The PA_BNBD cache ([num_blocks, Hk, block_size, D]) gives the same bits
+    as the PA_BBND one, on the split-KV and on the tiled path."""
+    p = W.make_problem(90 + len(lq) + lq[0], lq, [700, 900, 2500, 4500], 8, 2, 128, causal=True,
+                       name="paged_bnbd")
+    layout = W.paged_layout(p.cu_k, 32, seed=91, spare=2)
+    res = []
+    for cl in ("BBND", "BNBD"):
+        plan = B.PagedPlan(p.cu_q, layout.seqused, layout.block_table, layout.block_size,
+                           layout.num_blocks, p.num_heads_q, p.num_heads_k, p.head_dim, True,
+                           cache_layout=cl)
+        kc = _bf16_dev(W.scatter_to_pages(p.k, p.cu_k, layout, cl))
+        vc = _bf16_dev(W.scatter_to_pages(p.v, p.cu_k, layout, cl))
+        out, lse = B.forward_paged(plan, to_dev(p, "q"), kc, vc, dev_sinks(p), float(p.scale))
+        torch.cuda.synchronize()
+        res.append((out, lse, int(plan.meta[14])))
+    log(f"paged BNBD vs BBND, mode {res[0][2]}")
+    assert torch.equal(res[0][0].view(torch.int16), res[1][0].view(torch.int16))
+    assert torch.equal(res[0][1].view(torch.int32), res[1][1].view(torch.int32))

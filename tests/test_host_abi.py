@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(L):
             "sink_attn_arm_timing"} <= names
     for n in names:
         assert hasattr(L, n), n
-    assert B.abi_version() == 3
+    assert B.abi_version() == 4
     for s in range(6):
         assert isinstance(B.status_string(s), str)
 
@@ -114,7 +114,7 @@ def test_metadata_two_call_protocol_and_sizes(L):
                               ctypes.byref(words), ctypes.byref(fws), ctypes.byref(bws))
     assert st == B.E_BUFFER_TOO_SMALL
     meta, f, b = B.sink_attn_metadata(p, cu, cu)
-    assert meta[0] == 0x4B4E4953 and meta[1] == 3 and len(meta) == words.value
+    assert meta[0] == 0x4B4E4953 and meta[1] == 4 and len(meta) == words.value
     # bwd workspace: D [Hq,Tq] fp32 + per-block dsink partials (no dQ accumulator)
     assert 300 * 8 * 4 <= b < 300 * 8 * 4 + 4096
     assert f == 0       # prefill mode needs no forward scratch
@@ -257,6 +257,7 @@ def test_paged_metadata_rejects():
     for bs in (0, 8, 24, 2048):
         assert status(kv=B.PagedKV(bs, kv.max_blocks_per_seq, kv.num_blocks)) == B.E_INVALID
     assert status(kv=B.PagedKV(16, kv.max_blocks_per_seq, 0)) == B.E_INVALID
+    assert status(kv=B.PagedKV(16, kv.max_blocks_per_seq, kv.num_blocks, 2)) == B.E_INVALID
     bad = table.copy(); bad[2, 0] = kv.num_blocks
     assert status(table=bad) == B.E_INVALID
     bad = table.copy(); bad[0, 0] = -1
@@ -311,6 +312,8 @@ def test_paged_fwd_argument_checks():
                                      a["lse"], a["ws"], a["wsb"], stream=0, check=False)
     assert fwdp(meta_c) == B.E_META_MISMATCH                  # contiguous table
     assert fwdp(meta, kv_=B.PagedKV(32, kv.max_blocks_per_seq, kv.num_blocks)) == B.E_META_MISMATCH
+    bnbd = B.PagedKV(kv.block_size, kv.max_blocks_per_seq, kv.num_blocks, B.PA_BNBD)
+    assert fwdp(meta, kv_=bnbd) == B.E_META_MISMATCH       # the table was made for PA_BBND
     assert fwdp(meta, bt=None) == B.E_INVALID
     assert fwdp(meta, used=None) == B.E_INVALID
     assert fwdp(meta, wsb=fws - 1) == B.E_BUFFER_TOO_SMALL

@@ -82,3 +82,20 @@ def test_pad_rows_places_every_row():
     assert seen == T * N
     with pytest.raises(ValueError):
         W.pad_rows(x, cu, S, "TND", 0.0)
+
+
+def test_scatter_to_pages_cache_layouts():
+    """BNBD holds the same (page, slot, head) elements as BBND with the head
+    and slot axes swapped (the page's [num_blocks, KV_N, block_size, D])."""
+    cu = np.array([0, 20, 21, 60], np.int32)
+    x = (np.arange(60 * 2 * 4, dtype=np.float32) + 1).reshape(60, 2, 4)
+    lay = W.paged_layout(cu, 16, seed=3, spare=1)
+    a = W.scatter_to_pages(x, cu, lay)
+    b = W.scatter_to_pages(x, cu, lay, "BNBD")
+    assert b.shape == (lay.num_blocks, 2, 16, 4)
+    for pg in range(lay.num_blocks):
+        for sl in range(16):
+            for h in range(2):
+                assert (a[pg, sl, h] == b[pg, h, sl]).all()
+    with pytest.raises(ValueError):
+        W.scatter_to_pages(x, cu, lay, "NZ")
