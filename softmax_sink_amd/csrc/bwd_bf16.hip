@@ -646,13 +646,19 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdArgs a)
         dp = mfma32(lds_row_chunk<D, T>(vt_lds, kb * 32 + c, 2 * t + hl), gf[t], dp);
       }
       sched_mfma_pipeline<2 * NT, 1, 1, 3>();
+      // mask (partial tiles only) as S = -inf, so that P is 0: one uniform
+      // branch around the whole block rather than one per element, which
+      // would cut the softmax into 16 basic blocks
+      if (partial) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int jj = kt * BN + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (jj < jlo || jj > jhi) s[r] = kNegInf;
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = exp2_hw(__builtin_fmaf(s[r], c2, -lse2));
-        if (partial) {
-          const int jj = kt * BN + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (jj < jlo || jj > jhi) p = 0.f;
-        }
+        const float p = exp2_hw(__builtin_fmaf(s[r], c2, -lse2));
         dp[r] = p * (dp[r] - dval);          // scale is applied to dQ at the end
       }
 #pragma unroll
