@@ -117,6 +117,27 @@ def test_bf16_zero_length_sequences():
     _check(p)
 
 
+def test_bf16_multi_query_attention():
+    # one kv-head for 16 q-heads (the GQA limit): the dK/dV kernel walks 16
+    # q-heads per key tile; head count not a multiple of 8 on the q side too
+    p = W.make_problem(49, [200, 37, 129], [260, 37, 300], 16, 1, 64, causal=True,
+                       win_left=90, name="mqa_d64")
+    _check(p)
+    p = W.make_problem(52, [70, 9], [70, 140], 12, 1, 128, causal=False, name="mqa_h12")
+    _check(p)
+
+
+def test_bf16_decode_group_at_split_limit():
+    # 4 query rows x 16 q-heads per kv-head = 64 rows: the largest group the
+    # split-KV path takes; one more row goes to the tiled path
+    p = W.make_problem(53, [4, 1, 4], [900, 3000, 64], 32, 2, 128, causal=True,
+                       name="decode_limit")
+    assert _check(p, bwd=False).plan.mode == 1
+    p = W.make_problem(54, [5, 1, 4], [900, 3000, 64], 32, 2, 128, causal=True,
+                       name="decode_limit_plus_one")
+    assert _check(p, bwd=False).plan.mode == 0
+
+
 @pytest.mark.parametrize("D", [128, 64])
 def test_bf16_decode_split_kv(D):
     # short query groups: split-KV kernel + combine (chunk boundaries crossed)
