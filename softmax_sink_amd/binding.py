@@ -8,9 +8,9 @@ functions ``sink_attn_metadata``, ``sink_attn_fwd``, ``sink_attn_bwd``,
 ``sink_attn_bwd_padded``, ``sink_attn_merge`` and ``sink_attn_arm_timing``
 mirror the C entry points one to one. ``Plan``, ``PagedPlan``,
 ``PaddedPlan``, ``forward``, ``forward_paged``, ``forward_padded``,
-``backward``, ``backward_padded``, ``SinkAttnFunction`` and
-``learnable_sink_attn_varlen`` are conveniences that allocate outputs and
-workspace with torch and call them.
+``backward``, ``backward_padded``, ``SinkAttnFunction``,
+``learnable_sink_attn_varlen`` and ``learnable_sink_attn_padded`` are
+conveniences that allocate outputs and workspace with torch and call them.
 
 If the library has not been built the first call raises: there is no other
 path.
@@ -556,6 +556,69 @@ def learnable_sink_attn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q
         softmax_scale = 1.0 / math.sqrt(q.shape[-1])
     return _SAF.apply(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
                       softmax_offset, softmax_scale, causal, tuple(window_size))
+
+
+def _padded_autograd_function():
+    import torch
+
+    class SinkAttnPaddedFunction(torch.autograd.Function):
+        """Autograd wrapper over the batch-padded (BSND / BNSD) calls. Rows
+        past the used lengths come out as zeros in out, dq, dk and dv."""
+
+        @staticmethod
+        def forward(ctx, q, k, v, softmax_offset, softmax_scale, causal, window_size, layout,
+                    layout_out, seqused_q, seqused_kv):
+            bsnd = layout == "BSND"
+            batch, seq_q = q.shape[0], q.shape[1] if bsnd else q.shape[2]
+            seq_k = k.shape[1] if bsnd else k.shape[2]
+            hq, hk = (q.shape[2], k.shape[2]) if bsnd else (q.shape[1], k.shape[1])
+            host = lambda t: None if t is None else t.detach().to("cpu", torch.int32).numpy()
+            plan = PaddedPlan(batch, seq_q, seq_k, host(seqused_q), host(seqused_kv), hq, hk,
+                              q.shape[3], causal, window_size, q.dtype, layout, layout_out,
+                              q.device)
+            padded = seqused_q is not None or seqused_kv is not None
+            q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+            sinks = softmax_offset.float().contiguous() if softmax_offset is not None else None
+            out = (torch.zeros if padded else torch.empty)(plan.out_shape(), dtype=q.dtype,
+                                                           device=q.device)
+            lse = torch.zeros(batch, hq, seq_q, dtype=torch.float32, device=q.device)
+            forward_padded(plan, q, k, v, sinks, softmax_scale, out, lse)
+            ctx.save_for_backward(q, k, v, out, lse, sinks)
+            ctx.plan, ctx.scale, ctx.padded = plan, softmax_scale, padded
+            ctx.has_sink = softmax_offset is not None
+            ctx.offset_dtype = softmax_offset.dtype if softmax_offset is not None else None
+            return out
+
+        @staticmethod
+        def backward(ctx, dout):
+            q, k, v, out, lse, sinks = ctx.saved_tensors
+            alloc = torch.zeros_like if ctx.padded else torch.empty_like
+            dq, dk, dv, dsink = backward_padded(ctx.plan, dout.contiguous(), q, k, v, out, lse,
+                                                sinks if ctx.has_sink else None, ctx.scale,
+                                                alloc(q), alloc(k), alloc(v))
+            if dsink is not None:
+                dsink = dsink.to(ctx.offset_dtype)
+            return dq, dk, dv, dsink, None, None, None, None, None, None, None
+
+    return SinkAttnPaddedFunction
+
+
+_SAPF = None
+
+
+def learnable_sink_attn_padded(q, k, v, softmax_offset, softmax_scale=None, causal=False,
+                               window_size=(-1, -1), layout="BSND", layout_out=None,
+                               seqused_q=None, seqused_kv=None):
+    """Batch-padded sink attention with autograd: q [B, S_q, Hq, D] and k, v
+    [B, S_k, Hk, D] for "BSND", [B, H, S, D] for "BNSD" (out may be BSND for
+    BNSD q); seqused_q / seqused_kv: int32 [B] rows in use (None: all)."""
+    global _SAPF
+    if _SAPF is None:
+        _SAPF = _padded_autograd_function()
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(q.shape[-1])
+    return _SAPF.apply(q, k, v, softmax_offset, softmax_scale, causal, tuple(window_size),
+                       layout, layout_out, seqused_q, seqused_kv)
 
 
 def softmax_n_attn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,

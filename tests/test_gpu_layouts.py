@@ -145,3 +145,41 @@ def test_fp32_padded_layouts():
          causal=True, wl=20)
     _run(307, [37, 5, 12], [50, 9, 3], 40, 64, 4, 2, 128, "BSND", dtype="fp32",
          causal=False)
+
+
+def test_padded_autograd_wrapper_matches_direct_calls():
+    """learnable_sink_attn_padded: the same bits as the direct padded calls on
+    the used rows, zeros on the padding rows of out and of the gradients."""
+    used_q, used_k, S_q, S_k = [50, 0, 33], [70, 5, 64], 64, 80
+    p = W.make_problem(310, used_q, used_k, 8, 2, 128, causal=True, name="padded_autograd")
+    nb = len(used_q)
+    q0 = _dev(W.pad_rows(p.q, p.cu_q, S_q, "BSND", 0), "bf16")
+    k0 = _dev(W.pad_rows(p.k, p.cu_k, S_k, "BSND", 0), "bf16")
+    v0 = _dev(W.pad_rows(p.v, p.cu_k, S_k, "BSND", 0), "bf16")
+    do = _dev(W.pad_rows(p.dout, p.cu_q, S_q, "BSND", 0), "bf16")
+    sinks = dev_sinks(p)
+    uq = torch.tensor(used_q, dtype=torch.int32, device="cuda")
+    uk = torch.tensor(used_k, dtype=torch.int32, device="cuda")
+    q, k, v = (t.clone().requires_grad_() for t in (q0, k0, v0))
+    s = sinks.clone().requires_grad_()
+    out = B.learnable_sink_attn_padded(q, k, v, s, float(p.scale), True, layout="BSND",
+                                       seqused_q=uq, seqused_kv=uk)
+    out.backward(do)
+    torch.cuda.synchronize()
+    plan = B.PaddedPlan(nb, S_q, S_k, np.array(used_q, np.int32), np.array(used_k, np.int32), 8, 2,
+                        128, True, dtype="bf16", layout="BSND")
+    ro, rl = B.forward_padded(plan, q0, k0, v0, sinks, float(p.scale),
+                              torch.zeros_like(q0), torch.zeros(nb, 8, S_q, device="cuda"))
+    rq, rk, rv, rs = B.backward_padded(plan, do, q0, k0, v0, ro, rl, sinks, float(p.scale),
+                                       torch.zeros_like(q0), torch.zeros_like(k0),
+                                       torch.zeros_like(v0))
+    torch.cuda.synchronize()
+    bits = lambda t: t.detach().contiguous().view(torch.int16)
+    assert torch.equal(bits(out), bits(ro))
+    for got, ref in ((q.grad, rq), (k.grad, rk), (v.grad, rv)):
+        assert torch.equal(bits(got), bits(ref))
+    assert torch.equal(s.grad, rs)
+    mq = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(
+        _pad_mask(used_q, S_q, "BSND"), tuple(q0.shape)))).cuda()
+    assert (out.detach()[mq] == 0).all() and (q.grad[mq] == 0).all()
+    log("padded autograd wrapper: equal to the direct calls, padding rows zero")
