@@ -372,8 +372,7 @@ def main():
         # for training, the prefill tile loop (QK^T, PV: 4*D) otherwise
         name = "bwd" if train else "fwd"
         flops = (8.0 * D * pairs) if train else fwd_flops
-        kname = ("bwd_dkdv_wide_kernel" if D > 128 else "bwd_dkdv_kernel") if train \
-            else "fwd_prefill_kernel"
+        kname = "bwd_dkdv_kernel" if train else "fwd_prefill_kernel"
         peak = PEAK_BF16_TFLOPS if p.dtype == "bf16" else PEAK_FP32_TFLOPS
         achieved = flops / (kavg[name] * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": kname, "achieved": achieved, "peak": peak,

@@ -11,8 +11,8 @@
 //
 // Two kernels, neither with atomics:
 //  * dK/dV (key-tile outer): one work item = 128 keys of one (sequence,
-//    kv-head), walking the live 64-row query tiles of every q-head of the
-//    GQA group; per step
+//    kv-head), walking the live query tiles (64 rows; 32 at D = 256) of
+//    every q-head of the GQA group; per step
 //      S = Q K^T, dP = dO V^T (M = query, N = key; Q, dO from LDS)
 //      P = 2^(S scale log2e - lse log2e), dS = scale P (dP - D)
 //      dV^T += dO^T P, dK^T += Q^T dS (dO^T, Q^T by transposed LDS reads)
@@ -35,20 +35,21 @@ namespace {
 
 using namespace dev;
 
-// LDS of the dK/dV kernel. Step j of a work item is one (q-head, 64-row
-// query tile). Role 1 works one step behind role 0, so three Q tiles are
+// LDS of the dK/dV kernel. Step j of a work item is one (q-head, BM-row
+// query tile; BM = 64, or 32 at D = 256 so that the five stages fit). Role 1 works one step behind role 0, so three Q tiles are
 // live at once (role 0's, role 1's and the one in flight) and two dO tiles;
 // lse and D rows travel with their Q and dO stages. P of a step is handed
 // from role 0 to role 1 as 16-bit MFMA fragments ("dumps", one per parity):
 // 2 query blocks x 2 halves x 4 key blocks of 32 fragments of 64 lanes x 16 B.
 template <int D>
 struct KvSmem {
-  static constexpr int kTile = kBwdBM * D * 2;          // one [64][D] 16-bit tile
+  static constexpr int BM = bwd_tile_rows(D);
+  static constexpr int kTile = BM * D * 2;              // one [BM][D] 16-bit tile
   static constexpr int off_q = 0;                       // Q of step j: stage j % 3
   static constexpr int off_do = off_q + 3 * kTile;      // dO of step j: stage j % 2
   static constexpr int off_lse = off_do + 2 * kTile;    // 3 x [64] fp32, log2 domain
   static constexpr int off_dval = off_lse + 3 * 256;    // 2 x [64] fp32
-  static constexpr int kDump = 16 * 64 * 16;            // one step's P: 16 fragments
+  static constexpr int kDump = (BM / 32) * 8 * 64 * 16;  // one step's P fragments
   static constexpr int off_p = off_dval + 2 * 256;      // P of step j: dump j % 2
   static constexpr int bytes = off_p + 2 * kDump;
 };
@@ -86,6 +87,8 @@ struct StepIdx {
 template <int D, typename T>
 __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using S = KvSmem<D>;
+  constexpr int BM = S::BM;
+  constexpr int QB = BM / 32;                    // 32-row query blocks per step
   constexpr int NT = D / 16;
   constexpr int NB = D / 32;
   constexpr int KB = kKvKB;
@@ -145,7 +148,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     return dump + ((((qb * 4 + frag0 + kb) * 2 + h) * 64) + lane) * 16;
   };
 
-  TileDma<D, kKvThreads> dma;
+  TileDma<D, kKvThreads, BM> dma;
   dma.init();
   // lse / D rows of a step: raw values in registers of wave 0 (converting at
   // once would wait for the load), written to LDS at the end of the iteration
@@ -153,9 +156,9 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   bool lse_live = false, dval_live = false;
 
   if (steps > 0) {
-    dma.load(qg, qstride, qt_lo * kBwdBM, lq, smem + S::off_q);
-    if (threadIdx.x < kBwdBM) {
-      const int row = qt_lo * kBwdBM + threadIdx.x;
+    dma.load(qg, qstride, qt_lo * BM, lq, smem + S::off_q);
+    if (threadIdx.x < BM) {
+      const int row = qt_lo * BM + threadIdx.x;
       const float l = a.lse[lbase + (int64_t)min(row, lq - 1) * a.g.l_row];
       reinterpret_cast<float*>(smem + S::off_lse)[threadIdx.x] =
           (row >= lq || l == kNegInf) ? __builtin_huge_valf() : l * kLog2e;
@@ -175,20 +178,20 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   auto prefetch = [&](int it, int qs_next, int ds) __attribute__((always_inline)) {
     if (it + 1 < steps) {
       const int qt = qt_lo + sq.t;
-      dma.load(qg + sq.g * a.g.q_head, qstride, qt * kBwdBM, lq,
+      dma.load(qg + sq.g * a.g.q_head, qstride, qt * BM, lq,
                smem + S::off_q + qs_next * S::kTile);
-      if (threadIdx.x < kBwdBM) {
-        const int row = qt * kBwdBM + threadIdx.x;
+      if (threadIdx.x < BM) {
+        const int row = qt * BM + threadIdx.x;
         lse_live = row < lq;
         lse_raw = a.lse[lbase + (int64_t)sq.g * a.g.l_head + (int64_t)min(row, lq - 1) * a.g.l_row];
       }
     }
     if (it < steps) {
       const int qt = qt_lo + sd.t;
-      dma.load(dg + sd.g * a.g.o_head, a.g.o_row, qt * kBwdBM, lq,
+      dma.load(dg + sd.g * a.g.o_head, a.g.o_row, qt * BM, lq,
                smem + S::off_do + ds * S::kTile);
-      if (threadIdx.x < kBwdBM) {
-        const int row = qt * kBwdBM + threadIdx.x;
+      if (threadIdx.x < BM) {
+        const int row = qt * BM + threadIdx.x;
         dval_live = row < lq;
         dval_raw = a.dval[rbase + (int64_t)sd.g * a.total_q + min(row, lq - 1)];
       }
@@ -198,7 +201,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // lse, +inf for rows past the sequence or with no kept key, so that their
   // P is 0), then wait for the tiles and publish everything.
   auto finish = [&](int it, int qs_next, int ds) __attribute__((always_inline)) {
-    if (threadIdx.x < kBwdBM) {
+    if (threadIdx.x < BM) {
       if (it + 1 < steps)
         reinterpret_cast<float*>(smem + S::off_lse + qs_next * 256)[threadIdx.x] =
             (!lse_live || lse_raw == kNegInf) ? __builtin_huge_valf() : lse_raw * kLog2e;
@@ -214,9 +217,9 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // The two roles run separate loops with the same barrier sequence (one
   // per iteration), so that each is register-allocated on its own.
   if (steps > 0 && role == 0) {
-    vec8<T> pf[2][KB][2];                         // P of the previous step [qb][kb][half]
+    vec8<T> pf[QB][KB][2];                         // P of the previous step [qb][kb][half]
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) pf[qb][kb][0] = pf[qb][kb][1] = vec8<T>{};
     int qs = 0;                                  // it % 3
@@ -236,13 +239,13 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       // block qb is 32qb + 8(r/4) + 4hl + r%4. After the last step the Q
       // stage holds stale (or never written) data; that P is never read.
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < QB; ++qb) {
         f32x16 x[KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) x[kb] = f32x16{};
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          const vec8<T> qa = lds_row_chunk<D, T>(q_l, 32 * qb + c, 2 * t + hl);
+          const vec8<T> qa = lds_row_chunk<D, T, BM>(q_l, 32 * qb + c, 2 * t + hl);
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) x[kb] = mfma32(qa, frag[kb][t], x[kb]);
         }
@@ -250,7 +253,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         if (partial) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int i = qt * kBwdBM + 32 * qb + 8 * (r >> 2) + 4 * hl + (r & 3);
+            const int i = qt * BM + 32 * qb + 8 * (r >> 2) + 4 * hl + (r & 3);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
               if (i < ilo[kb] || i > ihi[kb]) x[kb][r] = kNegInf;
@@ -260,7 +263,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int db = 0; db < NB; ++db) {
-            const vec8<T> da = lds_col_operand<D, T>(dop_l, 16 * (2 * qb + h), 32 * db);
+            const vec8<T> da = lds_col_operand<D, T, BM>(dop_l, 16 * (2 * qb + h), 32 * db);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
               acc[db][kb] = mfma32(da, pf[qb][kb][h], acc[db][kb]);
@@ -300,13 +303,13 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         const char* qq_l = smem + S::off_q + qs_prev * S::kTile;
         char* dump = smem + S::off_p + (ds ^ 1) * S::kDump;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < QB; ++qb) {
           f32x16 x[KB];
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) x[kb] = f32x16{};
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
-            const vec8<T> ga = lds_row_chunk<D, T>(do_l, 32 * qb + c, 2 * t + hl);
+            const vec8<T> ga = lds_row_chunk<D, T, BM>(do_l, 32 * qb + c, 2 * t + hl);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) x[kb] = mfma32(ga, frag[kb][t], x[kb]);
           }
@@ -336,7 +339,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
             for (int kb = 0; kb < KB; ++kb) sf[kb] = frag_half<T>(x[kb], h);
 #pragma unroll
             for (int db = 0; db < NB; ++db) {
-              const vec8<T> qa = lds_col_operand<D, T>(qq_l, 16 * (2 * qb + h), 32 * db);
+              const vec8<T> qa = lds_col_operand<D, T, BM>(qq_l, 16 * (2 * qb + h), 32 * db);
 #pragma unroll
               for (int kb = 0; kb < KB; ++kb) acc[db][kb] = mfma32(qa, sf[kb], acc[db][kb]);
             }
@@ -366,196 +369,6 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
                          acc[db][kb][4 * g4 + 2] * sc, acc[db][kb][4 * g4 + 3] * sc);
         }
     }
-  }
-}
-
-// dK/dV for D = 256, key-tile outer, one wave per SIMD. The two-role
-// kernel above does not fit at this width (five [64 x 256] stages alone fill
-// the 160 KB of LDS, and 64 keys of dK or dV take 256 accumulator registers
-// per lane). Here every wave owns 32 keys of the 128-key item, and the item
-// walks its query tiles twice:
-//   dV pass: S = Q K^T, P = 2^(S scale log2e - lse log2e), dV^T += dO^T P
-//   dK pass: S, P as above, dP = dO V^T, dS = P (dP - D), dK^T += Q^T dS
-// so that a pass holds one accumulator (128 registers per lane) and at most
-// K and V rows (64 + 64): doing both in one pass needs more registers than
-// a lane has. The price is recomputing S (a quarter more MFMA work) and
-// fetching Q and dO twice (from L2, mostly). Q and dO tiles (and their lse
-// / D rows) are double buffered in LDS: one barrier per step.
-constexpr int kWideStage = 2 * kBwdBM * 256 * 2 + 2 * kBwdBM * 4;   // Q, dO, lse, D
-
-template <typename T>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_wide_kernel(BwdArgs a) {
-  constexpr int D = 256;
-  constexpr int NT = D / 16;
-  constexpr int NB = D / 32;
-  constexpr int kTile = kBwdBM * D * 2;
-  constexpr int off_do = kTile, off_lse = 2 * kTile, off_dval = off_lse + kBwdBM * 4;
-  // the two stages as two objects (see fwd_prefill_kernel)
-  __shared__ __attribute__((aligned(16))) char st0[kWideStage];
-  __shared__ __attribute__((aligned(16))) char st1[kWideStage];
-
-  const int item = blockIdx.x / a.hk;
-  const int hk = blockIdx.x % a.hk;
-  const int* itw = a.items + item * kItemWords;
-  const int b = itw[0], kt = itw[1], qt_lo = itw[2], qt_hi = itw[3];
-  const int qf_lo = itw[4], qf_hi = itw[5];
-  const int q0 = q_start(a, b), lq = q_len(a, b);
-  const int k0 = k_start(a, b), lk = k_len(a, b);
-  const int G = a.group;
-
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int hl = lane >> 5, c = lane & 31;
-  const int j = kt * kBwdBN + 32 * w + c;          // this lane's key
-
-  const int64_t kstride = a.g.k_row;
-  const int64_t kro = (int64_t)k0 * a.g.k_seq + hk * a.g.k_head + (int64_t)j * kstride;
-  int ilo, ihi;
-  key_row_range(j, lq, lk, a.causal, a.win_left, a.win_right, ilo, ihi);
-  const int nq = qt_hi - qt_lo;
-  const int steps = nq * G;
-  const float c2 = a.scale * kLog2e;
-  const T* qg = static_cast<const T*>(a.q) + (int64_t)q0 * a.g.q_seq + (int64_t)hk * G * a.g.q_head;
-  const T* dg = static_cast<const T*>(a.dout) + (int64_t)q0 * a.g.o_seq +
-                (int64_t)hk * G * a.g.o_head;
-  const int64_t lbase = (int64_t)q0 * a.g.l_seq + (int64_t)hk * G * a.g.l_head;
-  const int64_t rbase = ((int64_t)hk * G) * a.total_q + q0;
-
-  TileDma<D> dma;
-  dma.init();
-  float lse_raw = 0.f, dval_raw = 0.f;
-  bool live = false;
-  // Q, dO of step (g, t) into a stage; lse / D rows into registers of the
-  // first 64 threads (written to LDS by publish())
-  auto fetch = [&](const StepIdx& sx, char* st) __attribute__((always_inline)) {
-    const int qt = qt_lo + sx.t;
-    dma.load(qg + sx.g * a.g.q_head, a.g.q_row, qt * kBwdBM, lq, st);
-    dma.load(dg + sx.g * a.g.o_head, a.g.o_row, qt * kBwdBM, lq, st + off_do);
-    if (threadIdx.x < kBwdBM) {
-      const int row = qt * kBwdBM + threadIdx.x;
-      const int rc = min(row, lq - 1);
-      live = row < lq;
-      lse_raw = a.lse[lbase + (int64_t)sx.g * a.g.l_head + (int64_t)rc * a.g.l_row];
-      dval_raw = a.dval[rbase + (int64_t)sx.g * a.total_q + rc];
-    }
-  };
-  // log2-domain lse, +inf where no P may survive (rows past the sequence,
-  // rows with no kept key), and D, then wait for the tiles and sync
-  auto publish = [&](char* st) __attribute__((always_inline)) {
-    if (threadIdx.x < kBwdBM) {
-      reinterpret_cast<float*>(st + off_lse)[threadIdx.x] =
-          (!live || lse_raw == kNegInf) ? __builtin_huge_valf() : lse_raw * kLog2e;
-      reinterpret_cast<float*>(st + off_dval)[threadIdx.x] = live ? dval_raw : 0.f;
-    }
-    wait_vmem();
-    __syncthreads();
-  };
-
-  // One pass over the steps; KP: the dK pass. Returns the accumulator
-  // (dV^T or dK^T, unscaled) of this lane's key.
-  auto pass = [&](auto kp_c, f32x16 (&acc)[NB]) __attribute__((always_inline)) {
-    constexpr bool KP = decltype(kp_c)::value;
-    vec8<T> kf[NT], vf[KP ? NT : 1];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int64_t e = kro + 16 * t + 8 * hl;
-      kf[t] = j < lk ? __builtin_bit_cast(vec8<T>, ld16(static_cast<const T*>(a.k) + e)) : vec8<T>{};
-      if constexpr (KP)
-        vf[t] = j < lk ? __builtin_bit_cast(vec8<T>, ld16(static_cast<const T*>(a.v) + e)) : vec8<T>{};
-    }
-#pragma unroll
-    for (int n = 0; n < NB; ++n) acc[n] = f32x16{};
-    StepIdx sc, sn;                               // current step, the one after
-    if (steps > 0) {
-      fetch(sc, st0);
-      publish(st0);
-    }
-    sn.next(nq);
-    auto step = [&](auto cur_c, int it) __attribute__((always_inline)) {
-      constexpr int CUR = decltype(cur_c)::value;
-      char* cur = CUR == 0 ? st0 : st1;
-      char* nxt = CUR == 0 ? st1 : st0;
-      if (it + 1 < steps) fetch(sn, nxt);
-      const char* q_l = cur;
-      const char* do_l = cur + off_do;
-      const float* lse_l = reinterpret_cast<const float*>(cur + off_lse);
-      const float* dv_l = reinterpret_cast<const float*>(cur + off_dval);
-      const int qt = qt_lo + sc.t;
-      const bool partial = qt < qf_lo || qt >= qf_hi;
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        // query row of slot r: qt*64 + 32qb + 8(r/4) + 4hl + r%4
-        f32x16 x = f32x16{}, dp = f32x16{};
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          x = mfma32(lds_row_chunk<D, T>(q_l, 32 * qb + c, 2 * t + hl), kf[t], x);
-          if constexpr (KP)
-            dp = mfma32(lds_row_chunk<D, T>(do_l, 32 * qb + c, 2 * t + hl), vf[t], dp);
-        }
-        sched_mfma_pipeline<(KP ? 2 : 1) * NT, 1, 1, 3>();
-        if (partial) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int i = qt * kBwdBM + 32 * qb + 8 * (r >> 2) + 4 * hl + (r & 3);
-            if (i < ilo || i > ihi) x[r] = kNegInf;
-          }
-        }
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_l + 32 * qb + 8 * g4 + 4 * hl);
-          f32x4 d4;
-          if constexpr (KP) d4 = *reinterpret_cast<const f32x4*>(dv_l + 32 * qb + 8 * g4 + 4 * hl);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g4 + e;
-            x[r] = exp2_hw(__builtin_fmaf(x[r], c2, -l4[e]));       // P
-            if constexpr (KP) x[r] = x[r] * (dp[r] - d4[e]);        // dS (unscaled)
-          }
-        }
-        // dV^T += dO^T P  or  dK^T += Q^T dS
-        const char* src = KP ? q_l : do_l;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const vec8<T> f = frag_half<T>(x, h);
-#pragma unroll
-          for (int db = 0; db < NB; ++db)
-            acc[db] = mfma32(lds_col_operand<D, T>(src, 16 * (2 * qb + h), 32 * db), f, acc[db]);
-        }
-        sched_mfma_pipeline<2 * NB, 1, 2, 2>();
-      }
-      if (it + 1 < steps) publish(nxt);
-      sc.next(nq);
-      sn.next(nq);
-    };
-    int it = 0;
-    for (; it + 1 < steps; it += 2) {
-      step(std::integral_constant<int, 0>{}, it);
-      step(std::integral_constant<int, 1>{}, it + 1);
-    }
-    if (it < steps) step(std::integral_constant<int, 0>{}, it);
-  };
-  auto store = [&](const f32x16 (&acc)[NB], void* dst, float sc) __attribute__((always_inline)) {
-    if (j >= lk) return;
-    T* p = static_cast<T*>(dst) + kro;
-#pragma unroll
-    for (int db = 0; db < NB; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = 32 * db + 8 * g4 + 4 * hl;
-        *reinterpret_cast<u32x2*>(p + d) =
-            pack4_bits<T>(acc[db][4 * g4] * sc, acc[db][4 * g4 + 1] * sc,
-                          acc[db][4 * g4 + 2] * sc, acc[db][4 * g4 + 3] * sc);
-      }
-  };
-  {
-    f32x16 acc[NB];
-    pass(std::false_type{}, acc);
-    store(acc, a.dv, 1.f);
-  }
-  __syncthreads();        // the dK pass refills stage 0
-  {
-    f32x16 acc[NB];
-    pass(std::true_type{}, acc);
-    store(acc, a.dk, a.scale);
   }
 }
 
@@ -699,19 +512,13 @@ template <int D, typename T>
 hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s, const TimingHook& th) {
   hipError_t e = launch_bwd_pre<D, T>(a, s);
   if (e != hipSuccess) return e;
-  if constexpr (D <= 128) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, T>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, KvSmem<D>::bytes);
-    if (e != hipSuccess) return e;
-  }
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, T>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, KvSmem<D>::bytes);
+  if (e != hipSuccess) return e;
   if (th.start) hipEventRecord(th.start, s);
-  if (a.n_items > 0) {
-    if constexpr (D <= 128)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, T>), dim3(a.n_items * a.hk), dim3(kKvThreads),
-                         KvSmem<D>::bytes, s, a);
-    else
-      hipLaunchKernelGGL((bwd_dkdv_wide_kernel<T>), dim3(a.n_items * a.hk), dim3(256), 0, s, a);
-  }
+  if (a.n_items > 0)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, T>), dim3(a.n_items * a.hk), dim3(kKvThreads),
+                       KvSmem<D>::bytes, s, a);
   if (th.stop) hipEventRecord(th.stop, s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -86,9 +86,9 @@ __device__ __forceinline__ float half_max(float x) {
 // D = 128 (256-byte rows): f = 4(r%4) + (r/4)%4, a permutation of 0..15 on
 //   any 16 consecutive rows whose upper two bits differ on 4 consecutive rows.
 // D = 64 (128-byte rows, two rows per bank sweep): f = 4((r/2)%2) + (r/4)%4.
-// D = 256: the 64-row tile is kept as two [64 x 128] slices (columns 0..127,
-//   then 128..255), each laid out as a D = 128 tile, so that every access
-//   pattern and tile transfer of D = 128 carries over slice by slice.
+// D = 256: a tile is kept as two [rows x 128] slices (columns 0..127, then
+//   128..255), each laid out as a D = 128 tile, so that every access pattern
+//   and tile transfer of D = 128 carries over slice by slice.
 // ---------------------------------------------------------------------------
 template <int D>
 __device__ __forceinline__ int swz(int r) {
@@ -99,30 +99,31 @@ __device__ __forceinline__ int swz(int r) {
 
 template <int D>
 constexpr int kSliceCols = D > 128 ? 128 : D;                 // columns per slice
-template <int D>
-constexpr int kSliceBytes = 64 * kSliceCols<D> * 2;          // bytes per 64-row slice
+template <int D, int ROWS = 64>
+constexpr int kSliceBytes = ROWS * kSliceCols<D> * 2;        // bytes per slice of ROWS rows
 
-// Byte offset of the 16-byte chunk `chunk` (columns 8*chunk..+7) of row r.
-template <int D>
+// Byte offset of the 16-byte chunk `chunk` (columns 8*chunk..+7) of row r
+// of a tile of ROWS rows.
+template <int D, int ROWS = 64>
 __device__ __forceinline__ int chunk_off(int r, int chunk) {
   constexpr int DS = kSliceCols<D>;
   constexpr int CPS = DS / 8;                                 // chunks per slice row
   if constexpr (D > DS)
-    return (chunk / CPS) * kSliceBytes<D> + r * (DS * 2) + (((chunk % CPS) ^ swz<DS>(r)) << 4);
+    return (chunk / CPS) * kSliceBytes<D, ROWS> + r * (DS * 2) + (((chunk % CPS) ^ swz<DS>(r)) << 4);
   else
     return r * (D * 2) + ((chunk ^ swz<D>(r)) << 4);
 }
 
 // Byte offset of element (r, col) (col a multiple of 4 elements).
-template <int D>
+template <int D, int ROWS = 64>
 __device__ __forceinline__ int tile_off(int r, int col) {
-  return chunk_off<D>(r, col >> 3) + ((col & 7) << 1);
+  return chunk_off<D, ROWS>(r, col >> 3) + ((col & 7) << 1);
 }
 
 // 16-byte chunk (8 elements starting at column 8*chunk) of row r.
-template <int D, typename T = bf16>
+template <int D, typename T = bf16, int ROWS = 64>
 __device__ __forceinline__ vec8<T> lds_row_chunk(const char* tile, int r, int chunk) {
-  return *reinterpret_cast<const vec8<T>*>(tile + chunk_off<D>(r, chunk));
+  return *reinterpret_cast<const vec8<T>*>(tile + chunk_off<D, ROWS>(r, chunk));
 }
 
 template <int D>
@@ -138,7 +139,7 @@ __device__ __forceinline__ s16x4 ds_read_tr(const char* p) {
 // MFMA operand whose K slots run down the rows of an LDS tile (rows
 // row0 + 8(i/4) + 4hl + i%4, i = 0..7) and whose M/N index is column
 // col0 + lane%32: two transposed reads.
-template <int D, typename T = bf16>
+template <int D, typename T = bf16, int ROWS = 64>
 __device__ __forceinline__ vec8<T> lds_col_operand(const char* tile, int row0, int col0) {
   const int lane = threadIdx.x & 63;
   const int grp = lane >> 4;          // 16-lane group
@@ -146,8 +147,8 @@ __device__ __forceinline__ vec8<T> lds_col_operand(const char* tile, int row0, i
   const int nu = lane & 15;
   const int r = row0 + 4 * hl + (nu >> 2);
   const int col = col0 + 16 * (grp & 1) + 4 * (nu & 3);
-  s16x4 lo = ds_read_tr(tile + tile_off<D>(r, col));
-  s16x4 hi = ds_read_tr(tile + tile_off<D>(r + 8, col));
+  s16x4 lo = ds_read_tr(tile + tile_off<D, ROWS>(r, col));
+  s16x4 hi = ds_read_tr(tile + tile_off<D, ROWS>(r + 8, col));
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(vec8<T>, v);

@@ -293,13 +293,14 @@ sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
       fwd.push_back(it);
     }
     // backward items: one per key tile
-    const int64_t bnq = (lq + kBwdBM - 1) / kBwdBM, bnk = (lk + kBwdBN - 1) / kBwdBN;
+    const int64_t bbm = bwd_tile_rows(p.head_dim);
+    const int64_t bnq = (lq + bbm - 1) / bbm, bnk = (lk + kBwdBN - 1) / kBwdBN;
     for (int64_t kt = 0; kt < bnk; ++kt) {
       cls.assign(static_cast<size_t>(bnq), kDead);
       const int64_t c0 = kt * kBwdBN, c1 = std::min(lk, c0 + kBwdBN);
       for (int64_t qt = 0; qt < bnq; ++qt) {
-        const int64_t r0 = qt * kBwdBM, r1 = std::min(lq, r0 + kBwdBM);
-        cls[qt] = classify(rb, r0, r1, c0, c1, kBwdBM, kBwdBN);
+        const int64_t r0 = qt * bbm, r1 = std::min(lq, r0 + bbm);
+        cls[qt] = classify(rb, r0, r1, c0, c1, bbm, kBwdBN);
       }
       Item it{};
       it.w[0] = b;
@@ -378,7 +379,7 @@ sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
   h[kMode] = mode;
   h[kWordFwdBM] = kFwdBM;
   h[kWordFwdBN] = kFwdBN;
-  h[kWordBwdBM] = kBwdBM;
+  h[kWordBwdBM] = bwd_tile_rows(p.head_dim);
   h[kWordBwdBN] = kBwdBN;
   h[kWordDecBN] = kDecBN;
   h[kWordDecChunk] = kDecChunk;
@@ -440,7 +441,7 @@ sink_attn_status check_header(const sink_attn_problem& p, const int32_t* h,
       h[kLayoutQ] != p.layout_q || h[kLayoutOut] != p.layout_out ||
       h[kSeqQ] != p.seq_q || h[kSeqK] != p.seq_k)
     return SINK_ATTN_E_META_MISMATCH;
-  if (h[kWordFwdBM] != kFwdBM || h[kWordFwdBN] != kFwdBN || h[kWordBwdBM] != kBwdBM ||
+  if (h[kWordFwdBM] != kFwdBM || h[kWordFwdBN] != kFwdBN || h[kWordBwdBM] != bwd_tile_rows(p.head_dim) ||
       h[kWordBwdBN] != kBwdBN || h[kWordDecBN] != kDecBN || h[kWordDecChunk] != kDecChunk)
     return SINK_ATTN_E_META_MISMATCH;
   if (h[kPaged] != (kv ? 1 : 0)) return SINK_ATTN_E_META_MISMATCH;

@@ -38,7 +38,10 @@ enum Mode : int32_t { kModePrefill = 0, kModeDecode = 1 };
 // compiled for exactly these values and the ABI layer checks them).
 constexpr int kFwdBM = 128;    // query rows per forward work item (4 waves x 32)
 constexpr int kFwdBN = 64;     // keys per forward tile step
-constexpr int kBwdBM = 64;     // query rows per backward tile step
+constexpr int kBwdBM = 64;     // query rows per backward tile step (D <= 128)
+// Query rows per backward tile step of a head dim: 32 at D = 256, where
+// five [64 x 256] tiles would not fit the LDS of the dK/dV kernel.
+constexpr int bwd_tile_rows(int head_dim) { return head_dim > 128 ? 32 : kBwdBM; }
 constexpr int kBwdBN = 128;    // keys per backward work item (2 halves of 64)
 constexpr int kDecBN = 64;     // keys per split-KV tile step
 constexpr int kDecChunk = 2048;// keys per split-KV work item

@@ -36,11 +36,12 @@ constexpr int kBufferWord3 = 0x00020000;
 // in bounds; every consumer gives them zero weight). Completion is waited
 // for with wait_vmem() before the barrier that publishes the tile.
 // A D = 256 tile moves as its two 128-column slices, one after the other.
-template <int D, int THREADS = 256>
+template <int D, int THREADS = 256, int ROWS = 64>
 struct TileDma {
   static constexpr int DS = kSliceCols<D>;
   static constexpr int kSlices = D / DS;
-  static constexpr int kPer = 64 * DS / 8 / THREADS;     // passes per slice
+  static constexpr int kPer = ROWS * DS / 8 / THREADS;   // passes per slice
+  static_assert(kPer >= 1 && ROWS * DS / 8 % THREADS == 0, "whole passes");
   static constexpr int kRowsPerPass = THREADS / (DS / 8);
   static_assert(kRowsPerPass % 16 == 0, "a pass must keep the row swizzle");
   int lrow;             // this lane's row in pass 0
@@ -97,7 +98,7 @@ struct TileDma {
                                        char* tile) const {
 #pragma unroll
     for (int sl = 0; sl < kSlices; ++sl)
-      issue<0, kPer>(prepare(base + sl * DS, stride, row0, nrows, tile + sl * kSliceBytes<D>));
+      issue<0, kPer>(prepare(base + sl * DS, stride, row0, nrows, tile + sl * (ROWS * DS * 2)));
   }
 };
 

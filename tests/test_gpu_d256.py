@@ -49,6 +49,19 @@ def test_d256_bf16_causal_gqa_ragged():
     _fwd_bwd(p, mode=0)
 
 
+def test_d256_backward_is_deterministic():
+    p = W.make_problem(207, [700, 130], [700, 400], 8, 2, 256, causal=True, name="d256_det")
+    g = GpuRun(p)
+    g.fwd()
+    first = [t.clone() for t in (lambda r: (g.dq, g.dk, g.dv, g.dsink))(g.bwd())]
+    for _ in range(2):
+        g.bwd()
+        for a, b in zip(first, (g.dq, g.dk, g.dv, g.dsink)):
+            assert torch.equal(a.view(torch.int16) if a.dtype != torch.float32 else a,
+                               b.view(torch.int16) if b.dtype != torch.float32 else b)
+    log("d256 backward: three runs equal bit for bit")
+
+
 def test_d256_fp16_window_unequal_lengths():
     p = W.make_problem(202, [150, 77, 400], [300, 77, 90], 4, 4, 256, dtype="fp16",
                        causal=False, win_left=37, win_right=20, name="d256_fp16_window")

@@ -474,6 +474,10 @@ def test_head_dim_256_for_16_bit_types_only():
         p = B.make_problem(cu, cu, 8, 2, 256, True, dtype=dt)
         meta, fws, bws = B.sink_attn_metadata(p, cu, cu)
         assert meta[5] == 256
+        # the backward walks 32-row query tiles at this width; the items are
+        # still the oracle's for the tile shape the header states
+        assert meta[W_BWDBM] == 32 and meta[W_BWDBN] == 128
+        assert _items(meta, W_NBWD, W_BWDOFF) == O.backward_items(cu, cu, 32, 128, True, -1, -1)
     for d, dt in ((256, B.FP32), (512, B.BF16), (192, B.BF16)):
         p = B.make_problem(cu, cu, 8, 2, d, True, dtype=dt)
         with pytest.raises(B.SinkAttnError) as e:
