@@ -115,10 +115,13 @@ def traffic_record(workload, kernel):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path)).get(workload)
-    if not rec or rec.get("kernel") != kernel:
+    if not rec or rec.get("kernel") != kernel or "sources" not in rec:
         return None
-    src = os.path.join(ROOT, "softmax_sink_amd", "csrc", rec["source"])
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+    # the kernel's source file and every header it includes, in order
+    h = hashlib.sha256()
+    for name in rec["sources"]:
+        h.update(open(os.path.join(ROOT, "softmax_sink_amd", "csrc", name), "rb").read())
+    if h.hexdigest() != rec["sources_sha256"]:
         return None
     return rec["hbm_bytes_per_launch"]
 
@@ -170,7 +173,8 @@ def bench_merge(args):
            "roofline": {"bound": "hbm", "kernel": "merge_kernel",
                         "achieved": nbytes / (kms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                         "unit": "GB/s", "frac": nbytes / (kms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                        "traffic": None, "launch_ms": kms, "bytes_per_launch": nbytes}}
+                        "traffic": traffic_record("cp_merge", "merge_kernel"),
+                        "launch_ms": kms, "bytes_per_launch": nbytes}}
     if not args.no_cpu_baseline:
         from threadpoolctl import threadpool_info
         rows, t = 0, time.perf_counter()
@@ -209,9 +213,6 @@ def main():
     from softmax_sink_amd import workloads as W
 
     torch.cuda.set_device(0)
-    if args.workload == "cp_merge":
-        bench_merge(args)
-        return
     if args.calibrate_copy:
         src = torch.empty(args.calibrate_copy, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -219,6 +220,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.workload == "cp_merge":
+        bench_merge(args)
+        return
     p = W.config(args.workload)
     train = args.workload in TRAIN
     paged = "paged" in p.meta
