@@ -162,9 +162,8 @@ def test_forward_is_deterministic_and_dkdv_too():
     o2, l2 = g.fwd()
     d2 = g.bwd()
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
-    assert np.array_equal(d1[1], d2[1]) and np.array_equal(d1[2], d2[2])
-    assert np.array_equal(d1[3], d2[3])
-    assert rel_l2(d1[0], d2[0]) < 1e-6          # dq: fp32 atomics, order may vary
+    for a, b in zip(d1, d2):                    # dq, dk, dv, dsink: no atomics anywhere
+        assert np.array_equal(a, b)
 
 
 def test_guard_bands_untouched():

@@ -113,3 +113,26 @@ def test_gqa_window_bnsd_equals_packed_bitwise():
     assert same(packed(dq), g.dq) and same(packed(dk), g.dk) and same(packed(dv), g.dv)
     assert torch.equal(ds, g.dsink)
     log("  BNSD forward and backward equal the packed results bit for bit")
+
+
+@pytest.mark.parametrize("name", ["train_varlen", "gqa_window", "train_varlen_d256",
+                                  "decode_softmax_n"])
+def test_full_size_runs_are_reproducible(name):
+    """Every output of a full-size workload is the same bits on a second and
+    a third run (no atomics, fixed reduction orders; a race would show here)."""
+    p = W.config(name)
+    g = GpuRun(p)
+    train = name != "decode_softmax_n"
+    runs = []
+    for _ in range(3):
+        g.fwd()
+        outs = [g.out.clone(), g.lse.clone()]
+        if train:
+            g.bwd()
+            outs += [g.dq.clone(), g.dk.clone(), g.dv.clone(), g.dsink.clone()]
+        runs.append(outs)
+    bits = lambda t: t.view(torch.int16) if t.dtype in (torch.bfloat16, torch.float16) else t
+    for r in runs[1:]:
+        for a, b in zip(runs[0], r):
+            assert torch.equal(bits(a), bits(b))
+    log(f"{name}: three runs equal bit for bit")
