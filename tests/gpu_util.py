@@ -61,7 +61,8 @@ def oracle_inputs(p, with_sink=True):
 def max_abs(a, b):
     a, b = np.asarray(a), np.asarray(b)
     both_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
-    d = np.where(both_inf, 0.0, np.abs(a - b))
+    with np.errstate(invalid="ignore"):           # inf - inf where both_inf
+        d = np.where(both_inf, 0.0, np.abs(a - b))
     return float(np.max(d)) if d.size else 0.0
 
 
