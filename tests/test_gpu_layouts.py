@@ -13,7 +13,7 @@ import torch
 import oracle as O
 from softmax_sink_amd import binding as B
 from softmax_sink_amd import workloads as W
-from tests.gpu_util import TOL, dev_sinks, log, max_abs, oracle_inputs, rel_l2
+from tests.gpu_util import TOL, dev_sinks, dsink_error, log, max_abs, oracle_inputs, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -102,7 +102,11 @@ def _run(seed, used_q, used_k, seq_q, seq_k, hq, hk, D, layout, layout_out=None,
                 dk=rel_l2(_unpad(dk_np, used_k, layout), rk),
                 dv=rel_l2(_unpad(dv_np, used_k, layout), rv))
     if sinks is not None:
-        errs["dsink"] = rel_l2(ds.cpu().numpy().astype(np.float64), rs)
+        ds_np = ds.cpu().numpy().astype(np.float64)
+        if dtype == "fp32":
+            errs["dsink_vs_terms"] = dsink_error(ds_np, rs, ro, rl, p.as_f32("dout"), p.sinks)
+        else:
+            errs["dsink"] = rel_l2(ds_np, rs)
     log("  bwd rel-L2 " + " ".join(f"{k}={v:.3e}" for k, v in errs.items()))
     assert all(v <= tol["grad"] for v in errs.values()), errs
     mk = _pad_mask(used_k, seq_k, layout)

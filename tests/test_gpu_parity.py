@@ -10,7 +10,7 @@ import torch
 import oracle as O
 from softmax_sink_amd import binding as B
 from softmax_sink_amd import workloads as W
-from tests.gpu_util import GpuRun, TOL, log, max_abs, oracle_inputs, rel_l2
+from tests.gpu_util import GpuRun, TOL, dsink_error, log, max_abs, oracle_inputs, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -32,7 +32,9 @@ def _check(p, with_sink=True, bwd=True, tol=None):
     dq, dk, dv, ds = g.bwd()
     rq, rk, rv, rs = O.sink_attention_backward(p.as_f32("dout"), *args)
     errs = dict(dq=rel_l2(dq, rq), dk=rel_l2(dk, rk), dv=rel_l2(dv, rv))
-    if with_sink:
+    if with_sink and p.dtype == "fp32":
+        errs["dsink_vs_terms"] = dsink_error(ds, rs, ro, rl, p.as_f32("dout"), p.sinks)
+    elif with_sink:
         errs["dsink"] = rel_l2(ds, rs)
     log("  bwd rel-L2 " + " ".join(f"{k}={v:.3e}" for k, v in errs.items()))
     assert all(v <= tol["grad"] for v in errs.values()), errs
