@@ -127,12 +127,74 @@ def _i32p(a):
 
 
 def _ptr(t):
-    """Device pointer of a tensor (or an int address), None -> NULL."""
+    """Device pointer of a tensor (or an int address), None -> NULL. A host
+    tensor or a strided view is refused here: the kernels address device
+    memory densely from the base pointer."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_cuda:
+        raise ValueError("tensor is not on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor is not contiguous")
     return t.data_ptr()
+
+
+def _torch_dtype(code):
+    import torch
+    return {FP32: torch.float32, BF16: torch.bfloat16, FP16: torch.float16}[int(code)]
+
+
+def _expect(t, name, shape, dtype):
+    """A tensor handed to the kernels must be on the GPU, contiguous, and of
+    the shape and dtype its plan implies: a shorter buffer would be read or
+    written past its end."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name}: expected {tuple(shape)} {dtype}, got "
+                         f"{tuple(t.shape)} {t.dtype}")
+
+
+def _expect_sinks(sinks, hq):
+    import torch
+    if sinks is not None:
+        _expect(sinks, "sinks", (hq,), torch.float32)
+
+
+def _expect_packed(plan, q=None, k=None, v=None, dout=None, out=None, lse=None):
+    """Shapes of the packed (TND) tensors of a Plan or PagedPlan."""
+    import torch
+    p = plan.problem
+    dt = _torch_dtype(p.dtype)
+    qs, ks = (p.total_q, p.num_heads_q, p.head_dim), (p.total_k, p.num_heads_k, p.head_dim)
+    for t, name, shape in ((q, "q", qs), (dout, "dout", qs), (out, "out", qs), (k, "k", ks),
+                           (v, "v", ks)):
+        if t is not None:
+            _expect(t, name, shape, dt)
+    if lse is not None:
+        _expect(lse, "lse", (p.num_heads_q, p.total_q), torch.float32)
+
+
+def _expect_padded(plan, q=None, k=None, v=None, dout=None, out=None, lse=None):
+    """Shapes of the batch-padded tensors of a PaddedPlan."""
+    import torch
+    p = plan.problem
+    dt = _torch_dtype(p.dtype)
+    if plan.layout == "BNSD":
+        qs, ks = (p.batch, p.num_heads_q, p.seq_q, p.head_dim), (p.batch, p.num_heads_k, p.seq_k, p.head_dim)
+    else:
+        qs, ks = (p.batch, p.seq_q, p.num_heads_q, p.head_dim), (p.batch, p.seq_k, p.num_heads_k, p.head_dim)
+    os_ = plan.out_shape()
+    for t, name, shape in ((q, "q", qs), (k, "k", ks), (v, "v", ks), (dout, "dout", os_),
+                           (out, "out", os_)):
+        if t is not None:
+            _expect(t, name, shape, dt)
+    if lse is not None:
+        _expect(lse, "lse", (p.batch, p.num_heads_q, p.seq_q), torch.float32)
 
 
 def make_problem(cu_q, cu_k, num_heads_q, num_heads_k, head_dim, causal,
@@ -308,6 +370,8 @@ def merge(partial_out, partial_lse, sinks, out_dtype=None):
     lse [Hq, Tq] (sink inclusive)."""
     import torch
     P, Tq, Hq, D = partial_out.shape
+    _expect(partial_lse.contiguous(), "partial_lse", (P, Hq, Tq), torch.float32)
+    _expect_sinks(sinks, Hq)
     out_dtype = out_dtype or partial_out.dtype
     out = torch.empty(Tq, Hq, D, dtype=out_dtype, device=partial_out.device)
     lse = torch.empty(Hq, Tq, dtype=torch.float32, device=partial_out.device)
@@ -435,6 +499,8 @@ def _workspace(nbytes, device):
 def forward(plan, q, k, v, sinks, scale):
     """-> out (q's dtype, THD), lse [Hq, Tq] fp32."""
     import torch
+    _expect_packed(plan, q=q, k=k, v=v)
+    _expect_sinks(sinks, plan.problem.num_heads_q)
     out = torch.empty_like(q)
     lse = torch.empty(plan.problem.num_heads_q, plan.problem.total_q,
                       dtype=torch.float32, device=q.device)
@@ -448,6 +514,13 @@ def forward_paged(plan, q, k_cache, v_cache, sinks, scale):
     """Paged forward -> out, lse (k_cache, v_cache: [num_blocks, block_size,
     Hk, D], or [num_blocks, Hk, block_size, D] for a BNBD plan)."""
     import torch
+    p, kv = plan.problem, plan.kv
+    _expect_packed(plan, q=q)
+    cache = ((kv.num_blocks, p.num_heads_k, kv.block_size, p.head_dim) if kv.layout == PA_BNBD
+             else (kv.num_blocks, kv.block_size, p.num_heads_k, p.head_dim))
+    _expect(k_cache, "k_cache", cache, _torch_dtype(p.dtype))
+    _expect(v_cache, "v_cache", cache, _torch_dtype(p.dtype))
+    _expect_sinks(sinks, p.num_heads_q)
     out = torch.empty_like(q)
     lse = torch.empty(plan.problem.num_heads_q, plan.problem.total_q,
                       dtype=torch.float32, device=q.device)
@@ -464,6 +537,8 @@ def forward_padded(plan, q, k, v, sinks, scale, out=None, lse=None):
     uninitialised)."""
     import torch
     p = plan.problem
+    _expect_padded(plan, q=q, k=k, v=v, out=out, lse=lse)
+    _expect_sinks(sinks, p.num_heads_q)
     if out is None:
         out = torch.empty(plan.out_shape(), dtype=q.dtype, device=q.device)
     if lse is None:
@@ -479,9 +554,12 @@ def backward_padded(plan, dout, q, k, v, out, lse, sinks, scale, dq=None, dk=Non
     """Padded-layout backward -> dq, dk, dv, dsink (rows past the used
     lengths keep what dq / dk / dv held)."""
     import torch
+    _expect_padded(plan, q=q, k=k, v=v, dout=dout, out=out, lse=lse)
+    _expect_sinks(sinks, plan.problem.num_heads_q)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    _expect_padded(plan, q=dq, k=dk, v=dv)
     dsink = (torch.empty(plan.problem.num_heads_q, dtype=torch.float32, device=q.device)
              if sinks is not None else None)
     ws = _workspace(plan.bwd_ws_bytes, q.device)
@@ -494,6 +572,8 @@ def backward_padded(plan, dout, q, k, v, out, lse, sinks, scale, dq=None, dk=Non
 def backward(plan, dout, q, k, v, out, lse, sinks, scale):
     """-> dq, dk, dv, dsink (dsink None without sinks)."""
     import torch
+    _expect_packed(plan, q=q, k=k, v=v, dout=dout, out=out, lse=lse)
+    _expect_sinks(sinks, plan.problem.num_heads_q)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dsink = (torch.empty(plan.problem.num_heads_q, dtype=torch.float32, device=q.device)
              if sinks is not None else None)

@@ -1,0 +1,71 @@
+"""The binding refuses tensors that the kernels would address wrongly -- a
+host tensor, a strided view, the wrong dtype or shape for the plan -- with a
+ValueError raised before anything is launched. Needs a GPU (the plans keep
+device copies of the metadata)."""
+import numpy as np
+import pytest
+import torch
+
+from softmax_sink_amd import binding as B
+from softmax_sink_amd import workloads as W
+from tests.gpu_util import dev_sinks, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _packed():
+    p = W.make_problem(5, [40, 17], [40, 17], 4, 2, 64, causal=True, name="checks")
+    plan = B.Plan(p.cu_q, p.cu_k, 4, 2, 64, True)
+    return p, plan, to_dev(p, "q"), to_dev(p, "k"), to_dev(p, "v"), dev_sinks(p)
+
+
+def test_forward_and_backward_refuse_misfit_tensors():
+    p, plan, q, k, v, s = _packed()
+    bad = {
+        "host q": (q.cpu(), k, v, s),
+        "strided q": (q.transpose(0, 1).contiguous().transpose(0, 1), k, v, s),
+        "fp16 q": (q.half(), k, v, s),
+        "short k": (q, k[:-1], v, s),
+        "wrong heads v": (q, k, v.reshape(p.total_k, 1, 128), s),
+        "fp64 sinks": (q, k, v, s.double()),
+        "short sinks": (q, k, v, s[:2]),
+    }
+    for name, (qq, kk, vv, ss) in bad.items():
+        with pytest.raises(ValueError):
+            B.forward(plan, qq, kk, vv, ss, 0.125)
+    out, lse = B.forward(plan, q, k, v, s, 0.125)
+    dout = torch.randn_like(out)
+    with pytest.raises(ValueError):
+        B.backward(plan, dout, q, k, v, out, lse.t().contiguous(), s, 0.125)
+    with pytest.raises(ValueError):
+        B.backward(plan, dout.float(), q, k, v, out, lse, s, 0.125)
+    dq, dk, dv, ds = B.backward(plan, dout, q, k, v, out, lse, s, 0.125)
+    torch.cuda.synchronize()
+    assert dq.shape == q.shape and ds.shape == s.shape
+
+
+def test_padded_paged_and_merge_refuse_misfit_tensors():
+    p = W.make_problem(6, [30, 30], [50, 50], 4, 2, 64, causal=True, name="checks_pad")
+    plan = B.PaddedPlan(2, 30, 50, None, None, 4, 2, 64, True, layout="BSND")
+    q = to_dev(p, "q").reshape(2, 30, 4, 64)
+    k = to_dev(p, "k").reshape(2, 50, 2, 64)
+    v = to_dev(p, "v").reshape(2, 50, 2, 64)
+    with pytest.raises(ValueError):            # BNSD shapes for a BSND plan
+        B.forward_padded(plan, q.transpose(1, 2).contiguous(), k, v, None, 0.125)
+    out, lse = B.forward_padded(plan, q, k, v, None, 0.125)
+    with pytest.raises(ValueError):
+        B.backward_padded(plan, torch.randn_like(out)[:, :-1], q, k, v, out, lse, None, 0.125)
+
+    layout = W.paged_layout(p.cu_k, 16, seed=6)
+    pplan = B.PagedPlan(p.cu_q, layout.seqused, layout.block_table, 16, layout.num_blocks,
+                        4, 2, 64, True)
+    kc = torch.zeros(layout.num_blocks, 2, 16, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):            # a BNBD-shaped cache for a BBND plan
+        B.forward_paged(pplan, to_dev(p, "q"), kc, kc, None, 0.125)
+
+    parts = torch.randn(2, 10, 4, 64, device="cuda").bfloat16()
+    with pytest.raises(ValueError):
+        B.merge(parts, torch.zeros(2, 10, 4, device="cuda"), None)
+    o, l = B.merge(parts, torch.zeros(2, 4, 10, device="cuda"), None)
+    torch.cuda.synchronize()
+    assert o.shape == (10, 4, 64) and l.shape == (4, 10)

@@ -86,8 +86,8 @@ def _run(seed, used_q, used_k, seq_q, seq_k, hq, hk, D, layout, layout_out=None,
         return
 
     # the backward must not read padding rows of out / lse / dO either
-    out[torch.from_numpy(np.ascontiguousarray(mq_out)).cuda()] = float("nan")
-    lse[torch.from_numpy(np.ascontiguousarray(np.broadcast_to(mq_lse, l_np.shape))).cuda()] = \
+    out[torch.from_numpy(np.array(mq_out, copy=True)).cuda()] = float("nan")
+    lse[torch.from_numpy(np.array(np.broadcast_to(mq_lse, l_np.shape), copy=True)).cuda()] = \
         float("nan")
     dout = _dev(W.pad_rows(p.dout, p.cu_q, seq_q, lout, nan), dtype)
     dq = torch.full_like(q, SENTINEL)
