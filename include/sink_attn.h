@@ -133,8 +133,10 @@ typedef struct {
  * items: per (sequence, query tile) the range of key tiles with at least one
  * kept element and, inside it, the range whose every element is kept; the
  * same per (sequence, key tile) for the backward; and split-KV items for
- * short query groups. Masked-out tiles are never visited. Copy the table
- * unchanged to device memory (meta_dev) for fwd/bwd.
+ * short query groups (max_seqlen_q * num_heads_q / num_heads_k <= 64:
+ * decode mode, where the forward runs them; the backward's dQ pass always
+ * walks the per-query-tile items). Masked-out tiles are never visited.
+ * Copy the table unchanged to device memory (meta_dev) for fwd/bwd.
  * Errors: E_INVALID (problem or cu_seqlens checks above, NULL pointers, a
  * padded layout), E_UNSUPPORTED, E_BUFFER_TOO_SMALL (meta_capacity_words <
  * *meta_words; the sizes are still written). */
@@ -218,7 +220,8 @@ typedef struct {
  * query groups (max_seqlen_q * num_heads_q / num_heads_k <= 64) run the
  * split-KV decode path, longer ones the tiled prefill path (a chunked
  * prefill against the cache); bf16 or fp16 only (fp32: E_UNSUPPORTED). The
- * table can only be used with sink_attn_fwd_paged.
+ * table can only be used with sink_attn_fwd_paged: it holds no backward
+ * items, and in decode mode no per-query-tile items.
  * Errors: E_INVALID, E_UNSUPPORTED, E_BUFFER_TOO_SMALL. */
 sink_attn_status sink_attn_metadata_paged(const sink_attn_problem* p,
                                           const sink_attn_paged_kv* kv,

@@ -209,22 +209,41 @@ def make_problem(cu_q, cu_k, num_heads_q, num_heads_k, head_dim, causal,
                    int(bool(causal)), int(win_left), int(win_right), int(dtype))
 
 
-def sink_attn_metadata(problem, cu_seqlens_q_host, cu_seqlens_k_host):
-    """-> (meta int32 array, fwd_workspace_bytes, bwd_workspace_bytes)."""
+def _metadata(name, call, words, out):
+    """The two-call protocol of the metadata entry points. call(meta_ptr,
+    capacity) runs the C function; words receives the table size. With `out`
+    (a C-contiguous int32 array, e.g. a view of pinned host memory) the table
+    is written straight into it in one call and the filled prefix returned."""
+    if out is not None:
+        if out.dtype != np.int32 or not out.flags.c_contiguous:
+            raise ValueError("out must be a C-contiguous int32 array")
+        st = call(_i32p(out), len(out))
+        if st == E_BUFFER_TOO_SMALL:
+            raise SinkAttnError(st, f"{name}: out holds {len(out)} words, "
+                                    f"the table needs {words.value}")
+        if st != OK:
+            raise SinkAttnError(st, name)
+        return out[:words.value]
+    st = call(None, 0)
+    if st != OK:
+        raise SinkAttnError(st, name)
+    meta = np.zeros(words.value, dtype=np.int32)
+    st = call(_i32p(meta), words.value)
+    if st != OK:
+        raise SinkAttnError(st, name)
+    return meta
+
+
+def sink_attn_metadata(problem, cu_seqlens_q_host, cu_seqlens_k_host, out=None):
+    """-> (meta int32 array, fwd_workspace_bytes, bwd_workspace_bytes); with
+    `out`, the table is written into it (see _metadata)."""
     L = lib()
     cq = np.ascontiguousarray(cu_seqlens_q_host, dtype=np.int32)
     ck = np.ascontiguousarray(cu_seqlens_k_host, dtype=np.int32)
     words, fws, bws = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
-    st = L.sink_attn_metadata(ctypes.byref(problem), _i32p(cq), _i32p(ck), None, 0,
-                              ctypes.byref(words), ctypes.byref(fws), ctypes.byref(bws))
-    if st != OK:
-        raise SinkAttnError(st, "sink_attn_metadata")
-    meta = np.zeros(words.value, dtype=np.int32)
-    st = L.sink_attn_metadata(ctypes.byref(problem), _i32p(cq), _i32p(ck), _i32p(meta),
-                              words.value, ctypes.byref(words), ctypes.byref(fws),
-                              ctypes.byref(bws))
-    if st != OK:
-        raise SinkAttnError(st, "sink_attn_metadata")
+    meta = _metadata("sink_attn_metadata", lambda m, cap: L.sink_attn_metadata(
+        ctypes.byref(problem), _i32p(cq), _i32p(ck), m, cap, ctypes.byref(words),
+        ctypes.byref(fws), ctypes.byref(bws)), words, out)
     return meta, fws.value, bws.value
 
 
@@ -245,22 +264,15 @@ def make_problem_padded(batch, seq_q, seq_k, seqused_q, seqused_kv, num_heads_q,
                    lay, lay_out, int(seq_q), int(seq_k))
 
 
-def sink_attn_metadata_padded(problem, seqused_q_host, seqused_kv_host):
+def sink_attn_metadata_padded(problem, seqused_q_host, seqused_kv_host, out=None):
     """-> (meta int32 array, fwd_workspace_bytes, bwd_workspace_bytes)."""
     L = lib()
     uq = None if seqused_q_host is None else np.ascontiguousarray(seqused_q_host, np.int32)
     uk = None if seqused_kv_host is None else np.ascontiguousarray(seqused_kv_host, np.int32)
     words, fws, bws = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
-    st = L.sink_attn_metadata_padded(ctypes.byref(problem), _i32p(uq), _i32p(uk), None, 0,
-                                     ctypes.byref(words), ctypes.byref(fws), ctypes.byref(bws))
-    if st != OK:
-        raise SinkAttnError(st, "sink_attn_metadata_padded")
-    meta = np.zeros(words.value, dtype=np.int32)
-    st = L.sink_attn_metadata_padded(ctypes.byref(problem), _i32p(uq), _i32p(uk), _i32p(meta),
-                                     words.value, ctypes.byref(words), ctypes.byref(fws),
-                                     ctypes.byref(bws))
-    if st != OK:
-        raise SinkAttnError(st, "sink_attn_metadata_padded")
+    meta = _metadata("sink_attn_metadata_padded", lambda m, cap: L.sink_attn_metadata_padded(
+        ctypes.byref(problem), _i32p(uq), _i32p(uk), m, cap, ctypes.byref(words),
+        ctypes.byref(fws), ctypes.byref(bws)), words, out)
     return meta, fws.value, bws.value
 
 
@@ -273,24 +285,16 @@ def make_problem_paged(cu_q, seqused_kv, num_heads_q, num_heads_k, head_dim, cau
 
 
 def sink_attn_metadata_paged(problem, kv, cu_seqlens_q_host, seqused_kv_host,
-                             block_table_host):
+                             block_table_host, out=None):
     """-> (meta int32 array, fwd_workspace_bytes)."""
     L = lib()
     cq = np.ascontiguousarray(cu_seqlens_q_host, dtype=np.int32)
     su = np.ascontiguousarray(seqused_kv_host, dtype=np.int32)
     bt = np.ascontiguousarray(block_table_host, dtype=np.int32)
     words, fws = ctypes.c_int64(), ctypes.c_int64()
-    st = L.sink_attn_metadata_paged(ctypes.byref(problem), ctypes.byref(kv), _i32p(cq),
-                                    _i32p(su), _i32p(bt), None, 0, ctypes.byref(words),
-                                    ctypes.byref(fws))
-    if st != OK:
-        raise SinkAttnError(st, "sink_attn_metadata_paged")
-    meta = np.zeros(words.value, dtype=np.int32)
-    st = L.sink_attn_metadata_paged(ctypes.byref(problem), ctypes.byref(kv), _i32p(cq),
-                                    _i32p(su), _i32p(bt), _i32p(meta), words.value,
-                                    ctypes.byref(words), ctypes.byref(fws))
-    if st != OK:
-        raise SinkAttnError(st, "sink_attn_metadata_paged")
+    meta = _metadata("sink_attn_metadata_paged", lambda m, cap: L.sink_attn_metadata_paged(
+        ctypes.byref(problem), ctypes.byref(kv), _i32p(cq), _i32p(su), _i32p(bt), m, cap,
+        ctypes.byref(words), ctypes.byref(fws)), words, out)
     return meta, fws.value
 
 

@@ -270,6 +270,15 @@ sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
                                 int64_t* words, int64_t* fwd_ws, int64_t* bwd_ws) {
   const int B = p.batch;
   const int G = p.num_heads_q / p.num_heads_k;
+  const int32_t mode =
+      (static_cast<int64_t>(p.max_seqlen_q) * G <= kDecMaxRows) ? kModeDecode
+                                                                : kModePrefill;
+  // Only items some call can read are built. A paged table serves the
+  // forward alone: no backward items, and in decode mode (the forward runs
+  // the split-KV items) no per-query-tile items either. Other tables keep
+  // both, as the backward's dQ pass walks the per-query-tile items.
+  const bool want_bwd = paged == nullptr;
+  const bool want_fwd = want_bwd || mode == kModePrefill;
   std::vector<Item> fwd, bwd, dec;
   std::vector<int32_t> dec_seq(2 * static_cast<size_t>(B), 0);
   std::vector<int> cls;
@@ -278,7 +287,8 @@ sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
     const int64_t lq = cu_q[b + 1] - cu_q[b], lk = cu_k[b + 1] - cu_k[b];
     const RowBounds rb = row_bounds(p, lq, lk);
     // forward items: one per query tile
-    const int64_t nqt = (lq + kFwdBM - 1) / kFwdBM, nkt = (lk + kFwdBN - 1) / kFwdBN;
+    const int64_t nqt = want_fwd ? (lq + kFwdBM - 1) / kFwdBM : 0;
+    const int64_t nkt = (lk + kFwdBN - 1) / kFwdBN;
     for (int64_t qt = 0; qt < nqt; ++qt) {
       cls.assign(static_cast<size_t>(nkt), kDead);
       const int64_t r0 = qt * kFwdBM, r1 = std::min(lq, r0 + kFwdBM);
@@ -294,7 +304,8 @@ sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
     }
     // backward items: one per key tile
     const int64_t bbm = bwd_tile_rows(p.head_dim);
-    const int64_t bnq = (lq + bbm - 1) / bbm, bnk = (lk + kBwdBN - 1) / kBwdBN;
+    const int64_t bnq = (lq + bbm - 1) / bbm;
+    const int64_t bnk = want_bwd ? (lk + kBwdBN - 1) / kBwdBN : 0;
     for (int64_t kt = 0; kt < bnk; ++kt) {
       cls.assign(static_cast<size_t>(bnq), kDead);
       const int64_t c0 = kt * kBwdBN, c1 = std::min(lk, c0 + kBwdBN);
@@ -339,9 +350,6 @@ sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
   sort_items(fwd, B);
   sort_items(bwd, B);
 
-  const int32_t mode =
-      (static_cast<int64_t>(p.max_seqlen_q) * G <= kDecMaxRows) ? kModeDecode
-                                                                : kModePrefill;
   const int64_t pre_blocks = (p.total_q + kPreRows - 1) / kPreRows;
   const FwdWorkspace fw = fwd_workspace_layout(dec_rows, p.head_dim, p.dtype, mode);
   const BwdWorkspace bw = bwd_workspace_layout(p.total_q, p.num_heads_q,

@@ -237,6 +237,9 @@ def test_paged_metadata_matches_oracle_schedule():
         cu_k = np.r_[0, np.cumsum(used)].astype(np.int32)
         ditems, per_seq = O.decode_items(cu_q, cu_k, meta[W_DECBN], meta[W_DECCHUNK], True, -1, -1)
         assert _items(meta, W_NDEC, W_DECOFF, 4) == ditems
+        # a paged table serves the forward only: in decode mode it holds
+        # neither backward nor per-query-tile items
+        assert meta[W_NBWD] == 0 and meta[W_NFWD] == 0
         # the same problem through the contiguous call gives the same schedule
         meta_c, _, _ = B.sink_attn_metadata(p, cu_q, cu_k)
         assert meta_c[W_PAGED] == 0
