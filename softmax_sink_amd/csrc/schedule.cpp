@@ -85,16 +85,32 @@ void spans(const std::vector<int>& cls, int32_t* out4) {
 // then tile index. Heavy work starts first, and the blocks that run at the
 // same time mostly belong to one sequence, so they share its K/V (forward)
 // or Q/dO (backward) tiles in L2.
+// The items arrive grouped by sequence, each group in tile order, so the
+// sequences are ordered once and each group is stably ordered by its live
+// tile counts (linear when they are all equal, as in decode batches).
 void sort_items(std::vector<Item>& v, int batch) {
   std::vector<int64_t> work(static_cast<size_t>(batch), 0);
-  for (const Item& it : v) work[it.w[0]] += it.w[3] - it.w[2];
-  std::sort(v.begin(), v.end(), [&](const Item& x, const Item& y) {
-    if (work[x.w[0]] != work[y.w[0]]) return work[x.w[0]] > work[y.w[0]];
-    if (x.w[0] != y.w[0]) return x.w[0] < y.w[0];
-    const int lx = x.w[3] - x.w[2], ly = y.w[3] - y.w[2];
-    if (lx != ly) return lx > ly;
-    return x.w[1] < y.w[1];
+  std::vector<size_t> first(static_cast<size_t>(batch) + 1, 0);
+  for (const Item& it : v) {
+    work[it.w[0]] += it.w[3] - it.w[2];
+    ++first[static_cast<size_t>(it.w[0]) + 1];
+  }
+  for (int b = 0; b < batch; ++b) first[b + 1] += first[b];
+  std::vector<int> order(static_cast<size_t>(batch));
+  for (int b = 0; b < batch; ++b) order[b] = b;
+  std::sort(order.begin(), order.end(), [&](int x, int y) {
+    return work[x] != work[y] ? work[x] > work[y] : x < y;
   });
+  std::vector<Item> out;
+  out.reserve(v.size());
+  for (int b : order) {
+    const size_t lo = out.size();
+    out.insert(out.end(), v.begin() + first[b], v.begin() + first[b + 1]);
+    std::stable_sort(out.begin() + lo, out.end(), [](const Item& x, const Item& y) {
+      return x.w[3] - x.w[2] > y.w[3] - y.w[2];
+    });
+  }
+  v.swap(out);
 }
 
 uint32_t fnv1a(const int32_t* a, int64_t n, uint32_t h) {
