@@ -515,12 +515,12 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s, const TimingHook& th) {
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, T>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, KvSmem<D>::bytes);
   if (e != hipSuccess) return e;
-  if (th.start) hipEventRecord(th.start, s);
+  hipError_t ev = record_event(th.start, s);
   if (a.n_items > 0)
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, T>), dim3(a.n_items * a.hk), dim3(kKvThreads),
                        KvSmem<D>::bytes, s, a);
-  if (th.stop) hipEventRecord(th.stop, s);
-  e = hipGetLastError();
+  ev = first_error(ev, record_event(th.stop, s));
+  e = first_error(hipGetLastError(), ev);
   if (e != hipSuccess) return e;
   if (a.n_items_q > 0)
     hipLaunchKernelGGL((bwd_dq_kernel<D, T>), dim3(a.n_items_q * a.hq), dim3(256), 0, s, a);

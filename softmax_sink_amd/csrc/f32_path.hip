@@ -149,10 +149,10 @@ __global__ __launch_bounds__(128) void bwd_dkdv_f32_kernel(BwdArgs a) {
 template <int D>
 hipError_t launch_fwd_f32_d(const FwdArgs& a, hipStream_t s, const TimingHook& th) {
   const int rows = a.total_q * a.hq;
-  if (th.start) hipEventRecord(th.start, s);
+  hipError_t ev = record_event(th.start, s);
   hipLaunchKernelGGL(fwd_f32_kernel<D>, dim3((rows + 127) / 128), dim3(128), 0, s, a);
-  if (th.stop) hipEventRecord(th.stop, s);
-  return hipGetLastError();
+  ev = first_error(ev, record_event(th.stop, s));
+  return first_error(hipGetLastError(), ev);
 }
 
 template <int D>
@@ -160,11 +160,11 @@ hipError_t launch_bwd_f32_d(const BwdArgs& a, hipStream_t s, const TimingHook& t
   hipError_t e = launch_bwd_pre<D, float>(a, s);
   if (e != hipSuccess) return e;
   const int rq = a.total_q * a.hq, rk = a.total_k * a.hk;
-  if (th.start) hipEventRecord(th.start, s);
+  hipError_t ev = record_event(th.start, s);
   hipLaunchKernelGGL(bwd_dq_f32_kernel<D>, dim3((rq + 127) / 128), dim3(128), 0, s, a);
   hipLaunchKernelGGL(bwd_dkdv_f32_kernel<D>, dim3((rk + 127) / 128), dim3(128), 0, s, a);
-  if (th.stop) hipEventRecord(th.stop, s);
-  e = hipGetLastError();
+  ev = first_error(ev, record_event(th.stop, s));
+  e = first_error(hipGetLastError(), ev);
   if (e != hipSuccess) return e;
   return launch_dsink_finalize(a, s);
 }

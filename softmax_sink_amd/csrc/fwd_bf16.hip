@@ -483,26 +483,25 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(FwdArgs a) {
 
 template <int D, typename T>
 hipError_t launch_fwd_d(const FwdArgs& a, int mode, hipStream_t s, const TimingHook& th) {
+  hipError_t ev = record_event(th.start, s);
   if (mode == kModeDecode) {
-    if (th.start) hipEventRecord(th.start, s);
     if (a.n_items > 0) {
       if (a.block_table)
         hipLaunchKernelGGL((fwd_split_kernel<D, T, true>), dim3(a.n_items * a.hk), dim3(256), 0, s, a);
       else
         hipLaunchKernelGGL((fwd_split_kernel<D, T, false>), dim3(a.n_items * a.hk), dim3(256), 0, s, a);
     }
-    if (th.stop) hipEventRecord(th.stop, s);
+    ev = first_error(ev, record_event(th.stop, s));
     const int rows = a.total_q * a.hq;
     hipLaunchKernelGGL((fwd_combine_kernel<D, T>), dim3((rows + 3) / 4), dim3(256), 0, s, a);
   } else {
-    if (th.start) hipEventRecord(th.start, s);
     if (a.block_table)
       hipLaunchKernelGGL((fwd_prefill_kernel<D, T, true>), dim3(a.n_items * a.hq), dim3(256), 0, s, a);
     else
       hipLaunchKernelGGL((fwd_prefill_kernel<D, T, false>), dim3(a.n_items * a.hq), dim3(256), 0, s, a);
-    if (th.stop) hipEventRecord(th.stop, s);
+    ev = first_error(ev, record_event(th.stop, s));
   }
-  return hipGetLastError();
+  return first_error(hipGetLastError(), ev);
 }
 
 template <typename T>

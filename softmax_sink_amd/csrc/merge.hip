@@ -129,12 +129,12 @@ hipError_t launch_tp(const MergeArgs& a, int head_dim, int out_dtype, hipStream_
 
 hipError_t launch_merge(const MergeArgs& a, int head_dim, int part_dtype, int out_dtype,
                         hipStream_t s, const TimingHook& t) {
-  if (t.start) (void)hipEventRecord(t.start, s);
+  hipError_t ev = record_event(t.start, s);
   const hipError_t e = part_dtype == SINK_ATTN_BF16   ? launch_tp<dev::bf16>(a, head_dim, out_dtype, s)
                        : part_dtype == SINK_ATTN_FP16 ? launch_tp<dev::f16>(a, head_dim, out_dtype, s)
                                                       : launch_tp<float>(a, head_dim, out_dtype, s);
-  if (t.stop) (void)hipEventRecord(t.stop, s);
-  return e;
+  ev = first_error(ev, record_event(t.stop, s));
+  return first_error(e, ev);
 }
 
 }  // namespace sinkattn

@@ -186,6 +186,14 @@ struct TimingHook {
   hipEvent_t stop = nullptr;
 };
 
+// Records `e` on `s` when a timing event was armed; the launchers fold the
+// status into their own.
+inline hipError_t record_event(hipEvent_t e, hipStream_t s) {
+  return e ? hipEventRecord(e, s) : hipSuccess;
+}
+// The first failure of two calls made in that order.
+inline hipError_t first_error(hipError_t a, hipError_t b) { return a != hipSuccess ? a : b; }
+
 // 16-bit inputs (dtype SINK_ATTN_BF16 or SINK_ATTN_FP16), MFMA kernels
 hipError_t launch_fwd_16(const FwdArgs& a, int head_dim, int dtype, int mode,
                          hipStream_t s, const TimingHook& t);

@@ -27,8 +27,9 @@ constexpr int kBufferWord3 = 0x00020000;
 // form additionally turns every LDS wait into lgkmcnt(0). The kernels
 // instead wait for their prefetches explicitly (wait_vmem() before the
 // barrier that publishes a tile) and never touch a tile in flight. The
-// assembly has no outputs; its address operands are read at issue, and it
-// clobbers M0 and memory. A lane
+// assembly has no outputs; its address operands are read at issue, the LDS
+// destination comes in M0 as an input operand (the compiler writes M0
+// itself, so it knows the register's value), and it clobbers memory. A lane
 // therefore fetches the logical chunk that belongs at its physical position:
 // chunk (lane % (D/8)) ^ swz(row). Every pass advances the row by a multiple
 // of 16, which leaves swz(row) unchanged, so one offset per lane serves all
@@ -85,12 +86,11 @@ struct TileDma {
       const int row = min(lrow + s * kRowsPerPass, t.lim);
       const uint32_t voff = (uint32_t)(row * t.stride2 + lcol);
       asm volatile(
-          "s_mov_b32 m0, %2\n\t"
           "s_nop 0\n\t"
           "buffer_load_dwordx4 %1, %0, 0 offen lds"
           :
-          : "s"(t.rsrc), "v"(voff), "s"(t.lds + s * THREADS * 16)
-          : "memory", "m0");
+          : "s"(t.rsrc), "v"(voff), "{m0}"(t.lds + s * THREADS * 16)
+          : "memory");
     }
   }
   template <typename T>
@@ -109,7 +109,7 @@ struct TileDma {
 // holds its first key k_lo at slot off0; (page p, slot s) of the kv-head
 // sits at element p * page_stride + s * row_stride + head_off of the cache. Rows past `row_last` fetch row_last. Each lane computes its own
 // 64-bit row address, so the FLAT form global_load_lds_dwordx4 is used, again
-// from inline assembly (no outputs; clobbers M0 and memory). The division by
+// from inline assembly (no outputs; M0 an input operand; clobbers memory). The division by
 // block_size is a multiply-high with magic = ceil(2^32 / block_size), exact
 // here because the numerator stays below 2^12.
 template <int D, int THREADS = 256>
@@ -144,12 +144,11 @@ struct PagedTileDma {
 #pragma unroll
       for (int sl = 0; sl < kSlices; ++sl)
         asm volatile(
-            "s_mov_b32 m0, %1\n\t"
             "s_nop 0\n\t"
             "global_load_lds_dwordx4 %0, off"
             :
-            : "v"(src + sl * DS * 2), "s"(lds0 + sl * kSliceBytes<D> + s * THREADS * 16)
-            : "memory", "m0");
+            : "v"(src + sl * DS * 2), "{m0}"(lds0 + sl * kSliceBytes<D> + s * THREADS * 16)
+            : "memory");
     }
   }
 };
