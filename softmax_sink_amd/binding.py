@@ -410,6 +410,18 @@ def sink_attn_arm_timing(start, stop):
         raise SinkAttnError(st, "sink_attn_arm_timing")
 
 
+def _upload(arr, device):
+    """Host array -> device tensor without stalling the host: the bytes are
+    staged in pinned memory and copied on the current stream (a plain copy
+    from pageable memory would first wait for all the work queued on it).
+    torch's pinned-memory cache keeps the staging block until the copy ran."""
+    import torch
+    host = torch.from_numpy(np.ascontiguousarray(arr))
+    if torch.device(device).type != "cuda":
+        return host.to(device)
+    return host.pin_memory().to(device, non_blocking=True)
+
+
 # ---------------------------------------------------------------------------
 # Conveniences over the C entry points (allocation with torch only).
 # ---------------------------------------------------------------------------
@@ -428,9 +440,9 @@ class Plan:
         self.meta, self.fwd_ws_bytes, self.bwd_ws_bytes = sink_attn_metadata(
             self.problem, self.cu_q_host, self.cu_k_host)
         self.device = device
-        self.meta_dev = torch.from_numpy(self.meta).to(device)
-        self.cu_q = torch.from_numpy(self.cu_q_host).to(device)
-        self.cu_k = torch.from_numpy(self.cu_k_host).to(device)
+        self.meta_dev = _upload(self.meta, device)
+        self.cu_q = _upload(self.cu_q_host, device)
+        self.cu_k = _upload(self.cu_k_host, device)
 
     @property
     def mode(self):
@@ -455,10 +467,10 @@ class PagedPlan:
                                           window[1], dtype_code(dtype))
         self.meta, self.fwd_ws_bytes = sink_attn_metadata_paged(
             self.problem, self.kv, self.cu_q_host, self.seqused_host, self.block_table_host)
-        self.meta_dev = torch.from_numpy(self.meta).to(device)
-        self.cu_q = torch.from_numpy(self.cu_q_host).to(device)
-        self.seqused = torch.from_numpy(self.seqused_host).to(device)
-        self.block_table = torch.from_numpy(self.block_table_host).to(device)
+        self.meta_dev = _upload(self.meta, device)
+        self.cu_q = _upload(self.cu_q_host, device)
+        self.seqused = _upload(self.seqused_host, device)
+        self.block_table = _upload(self.block_table_host, device)
 
 
 class PaddedPlan:
@@ -480,11 +492,11 @@ class PaddedPlan:
                                            dtype_code(dtype), layout, layout_out)
         self.meta, self.fwd_ws_bytes, self.bwd_ws_bytes = sink_attn_metadata_padded(
             self.problem, self.used_q_host, self.used_k_host)
-        self.meta_dev = torch.from_numpy(self.meta).to(device)
+        self.meta_dev = _upload(self.meta, device)
         self.used_q = (None if self.used_q_host is None
-                       else torch.from_numpy(self.used_q_host).to(device))
+                       else _upload(self.used_q_host, device))
         self.used_k = (None if self.used_k_host is None
-                       else torch.from_numpy(self.used_k_host).to(device))
+                       else _upload(self.used_k_host, device))
 
     def out_shape(self):
         p = self.problem

@@ -8,7 +8,7 @@ import torch
 
 from softmax_sink_amd import binding as B
 from softmax_sink_amd import workloads as W
-from tests.gpu_util import dev_sinks, to_dev
+from tests.gpu_util import dev_sinks, log, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -69,3 +69,36 @@ def test_padded_paged_and_merge_refuse_misfit_tensors():
     o, l = B.merge(parts, torch.zeros(2, 4, 10, device="cuda"), None)
     torch.cuda.synchronize()
     assert o.shape == (10, 4, 64) and l.shape == (4, 10)
+
+
+def test_plan_does_not_wait_for_queued_work():
+    """Building a plan (metadata on the host, small copies to the device)
+    returns while earlier work is still queued: its copies are staged in
+    pinned memory instead of waiting for the stream to drain. ~60 ms of
+    matrix products are queued first."""
+    import time
+
+    a = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    p = W.make_problem(5, [40, 17, 300], [40, 17, 300], 4, 2, 64, causal=True, name="async")
+    b = a @ a                                   # warm both paths up first
+    B.Plan(p.cu_q, p.cu_k, 4, 2, 64, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(60):
+        b = a @ a
+    queued = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    plan = B.Plan(p.cu_q, p.cu_k, 4, 2, 64, True)
+    built = time.perf_counter() - t1
+    t2 = time.perf_counter()
+    torch.cuda.synchronize()
+    drained = time.perf_counter() - t2
+    log(f"queued {queued * 1e3:.1f} ms of products; plan built in {built * 1e3:.2f} ms; "
+        f"the queue drained {drained * 1e3:.1f} ms later")
+    # the queue was still busy after the plan was built, and building it took
+    # a small fraction of that time
+    assert drained > 0.01, (queued, built, drained)
+    assert built < 0.25 * (built + drained), (queued, built, drained)
+    assert np.array_equal(plan.meta_dev.cpu().numpy(), plan.meta)
+    assert np.array_equal(plan.cu_q.cpu().numpy(), p.cu_q)
+    del b
