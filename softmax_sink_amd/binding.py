@@ -600,6 +600,13 @@ def backward(plan, dout, q, k, v, out, lse, sinks, scale):
     return dq, dk, dv, dsink
 
 
+def _host_i32(x):
+    """cu_seqlens as a host int32 array (a tensor on the GPU is copied back)."""
+    if hasattr(x, "cpu"):
+        x = x.cpu().numpy()
+    return np.ascontiguousarray(x, dtype=np.int32)
+
+
 def _autograd_function():
     import torch
 
@@ -611,7 +618,7 @@ def _autograd_function():
         @staticmethod
         def forward(ctx, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
                     max_seqlen_k, softmax_offset, softmax_scale, causal, window_size):
-            plan = Plan(cu_seqlens_q.cpu().numpy(), cu_seqlens_k.cpu().numpy(),
+            plan = Plan(_host_i32(cu_seqlens_q), _host_i32(cu_seqlens_k),
                         q.shape[1], k.shape[1], q.shape[2], causal, window_size,
                         q.dtype, q.device)
             if plan.problem.max_seqlen_q != max_seqlen_q or plan.problem.max_seqlen_k != max_seqlen_k:
@@ -644,7 +651,10 @@ def learnable_sink_attn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q
                                max_seqlen_k, softmax_offset, softmax_scale=None,
                                causal=False, window_size=(-1, -1)):
     """Packed (THD) attention with a learnable per-head sink logit; default
-    scale 1/sqrt(head_dim) as in the "slime" wrapper."""
+    scale 1/sqrt(head_dim) as in the "slime" wrapper. The tile schedule is
+    built on the host from cu_seqlens: pass them as host (CPU) tensors or
+    arrays, as a data loader has them, to spare a device-to-host copy (which
+    waits for the queued work) on every call."""
     global _SAF
     if _SAF is None:
         _SAF = _autograd_function()

@@ -439,7 +439,12 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void fwd_split_kernel(FwdArgs
 }
 
 // One wave per (token, q-head) row: merge the chunk partials of its sequence
-// by their maxima, add the sink once, normalise.
+// by their maxima, add the sink once, normalise. The wave's lanes work side
+// by side so that the row costs a few memory latencies rather than a chain
+// of them: a 64-way search finds the sequence of a packed token (one round
+// for up to 64 sequences), lane j reads the (m, l) partials of chunk j, and
+// the O partials of all chunks are then requested back to back, each
+// chunk's row and weight broadcast from its lane. Sums run in a fixed order.
 template <int D, typename T>
 __global__ __launch_bounds__(256) void fwd_combine_kernel(FwdArgs a) {
   const int lane = threadIdx.x & 63;
@@ -447,30 +452,74 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(FwdArgs a) {
   if (row >= a.total_q * a.hq) return;
   const int t = row / a.hq, h = row % a.hq;
   int b, i;                                     // sequence and row of token t
-  q_row_of(a, t, b, i);
+  if (a.g.seq_q) {
+    b = t / a.g.seq_q;
+    i = t - b * a.g.seq_q;
+  } else {
+    // cu_q[lo] <= t < cu_q[hi] throughout; lane 0 always tests cu_q[lo]
+    int lo = 0, hi = a.batch;
+    while (hi - lo > 1) {
+      const int step = (hi - lo + 63) / 64;
+      const int idx = lo + lane * step;
+      const bool below = idx < hi && a.cu_q[idx] <= t;
+      const int j = 63 - __builtin_clzll(__ballot(below));
+      const int nlo = lo + j * step;
+      hi = min(nlo + step, hi);
+      lo = nlo;
+    }
+    b = lo;
+    i = t - a.cu_q[b];
+  }
   const int q0 = q_start(a, b), lq = q_len(a, b);
   if (i >= lq) return;                          // padding of a padded layout
   const int first = a.dec_seq[2 * b], n = a.dec_seq[2 * b + 1];
   const float sink = a.sinks ? a.sinks[h] : kNegInf;
+  // pass 1: the largest chunk maximum (lanes over chunks)
   float mt = sink * kLog2e;
-  for (int s = 0; s < n; ++s) {
-    const int prow = a.items[(first + s) * kItemWords + 4] + h * lq + i;
-    mt = fmaxf(mt, a.ws_m[prow]);
+  for (int g = 0; g < n; g += 64) {
+    const int s = g + lane;
+    if (s < n) mt = fmaxf(mt, a.ws_m[a.items[(first + s) * kItemWords + 4] + h * lq + i]);
   }
+  for (int o = 32; o > 0; o >>= 1) mt = fmaxf(mt, __shfl_xor(mt, o));
   const float mu = mt == kNegInf ? 0.f : mt;
-  float lt = exp2_hw(sink * kLog2e - mu);
+  // pass 2: weights, denominator and O
   constexpr int PER = D / 64;
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  for (int s = 0; s < n; ++s) {
-    const int prow = a.items[(first + s) * kItemWords + 4] + h * lq + i;
-    const float f = exp2_hw(a.ws_m[prow] - mu);
-    lt += a.ws_l[prow] * f;
-    const float* po = a.ws_o + (int64_t)prow * D + lane * PER;
+  float lpart = 0.f;
+  for (int g = 0; g < n; g += 64) {
+    const int s = g + lane;
+    int prow = 0;
+    float f = 0.f;
+    if (s < n) {
+      prow = a.items[(first + s) * kItemWords + 4] + h * lq + i;
+      f = exp2_hw(a.ws_m[prow] - mu);
+      lpart += a.ws_l[prow] * f;
+    }
+    const int cnt = min(64, n - g);
+    const int fbits = __float_as_int(f);
+    // eight chunks at a time: all eight loads are in flight before the
+    // first product; a slot past the last chunk re-reads chunk c0 with
+    // weight 0, which leaves the sum as it was
+    for (int c0 = 0; c0 < cnt; c0 += 8) {
+      float v[8][PER], fc[8];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] += po[e] * f;
+      for (int u = 0; u < 8; ++u) {
+        const int c = c0 + u < cnt ? c0 + u : c0;
+        const float* po = a.ws_o + (int64_t)__builtin_amdgcn_readlane(prow, c) * D + lane * PER;
+        fc[u] = c0 + u < cnt ? __int_as_float(__builtin_amdgcn_readlane(fbits, c)) : 0.f;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) v[u][e] = po[e];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] += v[u][e] * fc[u];
+    }
   }
+  for (int o = 32; o > 0; o >>= 1) lpart += __shfl_xor(lpart, o);
+  const float lt = lpart + exp2_hw(sink * kLog2e - mu);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   T* op = static_cast<T*>(a.out) + (int64_t)q0 * a.g.o_seq + (int64_t)i * a.g.o_row +
           h * a.g.o_head + lane * PER;
