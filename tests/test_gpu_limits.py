@@ -113,3 +113,24 @@ def test_one_long_sequence_forward_backward():
     e["dv_keys"] = rel_l2(np.array(got_v), np.array(ref_v))
     log("  identities / sampled keys rel-L2 " + " ".join(f"{k}={v:.3e}" for k, v in e.items()))
     assert all(v <= TOL["bf16"]["grad"] for v in e.values()), e
+
+
+def test_split_kv_combine_with_many_sequences_some_empty():
+    """300 sequences (a two-round search for each token's sequence in the
+    combine), about a fifth of them without queries and some without keys:
+    every row against the oracle."""
+    rng = np.random.default_rng(107)
+    lq = rng.integers(1, 5, 300)
+    lq[rng.random(300) < 0.2] = 0
+    lk = rng.integers(1, 3000, 300)
+    lk[rng.random(300) < 0.05] = 0
+    p = W.make_problem(107, lq, lk, 8, 2, 128, causal=True, name="many_seq_decode")
+    log(f"many_seq_decode: batch 300, {int((lq == 0).sum())} without queries, "
+        f"{int((lk == 0).sum())} without keys, Tq={p.total_q} Tk={p.total_k}")
+    g = GpuRun(p)
+    assert g.plan.mode == 1
+    out, lse = g.fwd()
+    ro, rl, _ = O.sink_attention_forward(*oracle_inputs(p))
+    e_out, e_lse = max_abs(out, ro), max_abs(lse, rl)
+    log(f"  max|d out|={e_out:.3e} max|d lse|={e_lse:.3e}")
+    assert e_out <= TOL["bf16"]["out"] and e_lse <= TOL["bf16"]["lse"]
