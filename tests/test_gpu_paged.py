@@ -153,3 +153,47 @@ def test_paged_bnbd_cache_equals_bbnd(lq):
     log(f"paged BNBD vs BBND, mode {res[0][2]}")
     assert torch.equal(res[0][0].view(torch.int16), res[1][0].view(torch.int16))
     assert torch.equal(res[0][1].view(torch.int32), res[1][1].view(torch.int32))
+
+
+@pytest.mark.parametrize("gib", [3.9, 4.2])
+def test_paged_cache_past_2_and_4_gib(gib):
+    """The used pages sit at the top of a cache of 3.9 GiB (byte offsets past
+    2^31) or 4.2 GiB (past 2^32): the 64-bit row addresses of the paged
+    transfer reach them, and both the tiled and the split-KV path give the
+    contiguous forward's bits."""
+    bs, hk, hq, D = 16, 8, 16, 128
+    num_blocks = int(gib * 2 ** 30) // (bs * hk * D * 2)
+    rng = np.random.default_rng(int(gib * 10))
+    for lens_q in ([300, 2, 700], [3, 1, 8]):
+        p = W.make_problem(int(gib * 10) + lens_q[0], lens_q, [900, 2500, 700], hq, hk, D,
+                           causal=True, name=f"paged_{gib}gib")
+        lens_k = np.diff(p.cu_k)
+        need = (lens_k + bs - 1) // bs
+        top = np.arange(num_blocks - int(need.sum()), num_blocks, dtype=np.int32)
+        rng.shuffle(top)
+        table = np.zeros((len(lens_k), int(need.max())), np.int32)
+        rows_k = np.zeros((int(need.sum()) * bs, hk, D), np.uint16)
+        rows_v = np.zeros_like(rows_k)
+        at = 0
+        for b, n in enumerate(need):
+            table[b, :n] = top[at:at + n]
+            seg = slice(int(p.cu_k[b]), int(p.cu_k[b + 1]))
+            rows_k[at * bs:at * bs + lens_k[b]] = p.k[seg]
+            rows_v[at * bs:at * bs + lens_k[b]] = p.v[seg]
+            at += int(n)
+        kc = torch.zeros(num_blocks, bs, hk, D, dtype=torch.bfloat16, device="cuda")
+        vc = torch.zeros_like(kc)
+        ids = torch.from_numpy(np.concatenate([table[b, :n] for b, n in enumerate(need)])
+                               .astype(np.int64)).cuda()
+        kc[ids] = _bf16_dev(rows_k).reshape(-1, bs, hk, D)
+        vc[ids] = _bf16_dev(rows_v).reshape(-1, bs, hk, D)
+        plan = B.PagedPlan(p.cu_q, lens_k, table, bs, num_blocks, hq, hk, D, True)
+        log(f"paged cache {gib} GiB ({num_blocks} pages), mode {int(plan.meta[14])}, "
+            f"pages {int(top.min())}..{int(top.max())}")
+        out, lse = B.forward_paged(plan, to_dev(p, "q"), kc, vc, dev_sinks(p), float(p.scale))
+        g = GpuRun(p)
+        g.fwd()
+        assert torch.equal(out.view(torch.int16), g.out.view(torch.int16))
+        assert torch.equal(lse.view(torch.int32), g.lse.view(torch.int32))
+        del kc, vc
+        torch.cuda.empty_cache()
