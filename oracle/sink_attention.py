@@ -32,7 +32,7 @@ Sources (pages; each function below cites the passage it follows):
   Differentiable Paged Attention: the paged path reads K/V pages through a
   block table (the CANN page gives the page layout and the table).
 
-Readings where the pages are silent (each is also listed in the design doc):
+Readings where the pages are silent:
 
 * LSE convention: ``lse`` returned here is sink-INCLUSIVE,
   ln(e^s + sum_kept e^S). ``lse_excl`` (the CANN page's formula) is also

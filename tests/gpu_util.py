@@ -26,7 +26,7 @@ def dev_sinks(p):
     return torch.from_numpy(np.ascontiguousarray(p.sinks)).cuda()
 
 
-class GpuRun:
+class HipRun:
     """Device copies of a workloads.Problem and the HIP results on them."""
 
     def __init__(self, p, with_sink=True):

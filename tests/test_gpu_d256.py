@@ -13,7 +13,7 @@ import torch
 import oracle as O
 from softmax_sink_amd import binding as B
 from softmax_sink_amd import workloads as W
-from tests.gpu_util import GpuRun, TOL, dev_sinks, log, max_abs, oracle_inputs, rel_l2, to_dev
+from tests.gpu_util import HipRun, TOL, dev_sinks, log, max_abs, oracle_inputs, rel_l2, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -22,7 +22,7 @@ def _fwd_bwd(p, bwd=True, mode=None):
     log(f"case {p.name}: lens_q={np.diff(p.cu_q).tolist()} lens_k={np.diff(p.cu_k).tolist()} "
         f"H={p.num_heads_q}/{p.num_heads_k} D={p.head_dim} dtype={p.dtype} causal={p.causal} "
         f"win=({p.win_left},{p.win_right})")
-    g = GpuRun(p)
+    g = HipRun(p)
     if mode is not None:
         assert g.plan.mode == mode
     out, lse = g.fwd()
@@ -51,7 +51,7 @@ def test_d256_bf16_causal_gqa_ragged():
 
 def test_d256_backward_is_deterministic():
     p = W.make_problem(207, [700, 130], [700, 400], 8, 2, 256, causal=True, name="d256_det")
-    g = GpuRun(p)
+    g = HipRun(p)
     g.fwd()
     first = [t.clone() for t in (lambda r: (g.dq, g.dk, g.dv, g.dsink))(g.bwd())]
     for _ in range(2):

@@ -11,7 +11,7 @@ import torch
 import oracle as O
 from softmax_sink_amd import binding as B
 from softmax_sink_amd import workloads as W
-from tests.gpu_util import GpuRun, TOL, dev_sinks, log, max_abs, oracle_inputs, rel_l2, to_dev
+from tests.gpu_util import HipRun, TOL, dev_sinks, log, max_abs, oracle_inputs, rel_l2, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 def _fwd_bwd(p, bwd=True):
     log(f"case {p.name}: lens_q={np.diff(p.cu_q).tolist()} lens_k={np.diff(p.cu_k).tolist()} "
         f"H={p.num_heads_q}/{p.num_heads_k} D={p.head_dim} dtype={p.dtype}")
-    g = GpuRun(p)
+    g = HipRun(p)
     out, lse = g.fwd()
     assert g.q.dtype == torch.float16
     args = oracle_inputs(p)
@@ -63,7 +63,7 @@ def test_fp16_paged_decode_equals_contiguous():
                        dtype="fp16")
     out, lse = B.forward_paged(plan, to_dev(p, "q"), cache(p.k), cache(p.v), dev_sinks(p),
                                float(p.scale))
-    g = GpuRun(p)
+    g = HipRun(p)
     g.fwd()
     assert torch.equal(out.view(torch.int16), g.out.view(torch.int16))
     assert torch.equal(lse.view(torch.int32), g.lse.view(torch.int32))

@@ -10,7 +10,7 @@ import torch
 
 import oracle as O
 from softmax_sink_amd import workloads as W
-from tests.gpu_util import GpuRun, TOL, log, max_abs, oracle_inputs, rel_l2, sampled_rows_error
+from tests.gpu_util import HipRun, TOL, log, max_abs, oracle_inputs, rel_l2, sampled_rows_error
 
 pytestmark = pytest.mark.gpu
 
@@ -40,7 +40,7 @@ def test_max_batch_split_kv_forward():
     lq, lk = rng.integers(1, 4, 65535), rng.integers(1, 41, 65535)
     p = W.make_problem(101, lq, lk, 2, 1, 64, causal=True, name="max_batch_decode", rng=rng)
     log(f"max batch split-KV: B={p.batch} Tq={p.total_q} Tk={p.total_k}")
-    g = GpuRun(p)
+    g = HipRun(p)
     g.fwd()
     assert g.plan.mode == 1
     seqs = sorted(set(rng.integers(0, p.batch, 60).tolist()) | {0, p.batch - 1})
@@ -52,7 +52,7 @@ def test_max_batch_tiled_forward_backward():
     lens = rng.integers(1, 81, 65535)
     p = W.make_problem(102, lens, lens, 1, 1, 64, causal=True, name="max_batch_prefill", rng=rng)
     log(f"max batch tiled: B={p.batch} Tq={p.total_q}")
-    g = GpuRun(p)
+    g = HipRun(p)
     g.fwd()
     assert g.plan.mode == 0
     grads = g.bwd()
@@ -64,7 +64,7 @@ def test_one_long_sequence_forward_backward():
     L, hq, hk, D = 65536, 4, 1, 128
     p = W.make_problem(103, [L], [L], hq, hk, D, causal=True, name="long_sequence")
     log(f"one sequence of {L} tokens, {hq}/{hk} heads, D {D}")
-    g = GpuRun(p)
+    g = HipRun(p)
     out, lse = g.fwd()
     dq, dk, dv, ds = g.bwd()
     for x in (dq, dk, dv, ds):
@@ -127,7 +127,7 @@ def test_split_kv_combine_with_many_sequences_some_empty():
     p = W.make_problem(107, lq, lk, 8, 2, 128, causal=True, name="many_seq_decode")
     log(f"many_seq_decode: batch 300, {int((lq == 0).sum())} without queries, "
         f"{int((lk == 0).sum())} without keys, Tq={p.total_q} Tk={p.total_k}")
-    g = GpuRun(p)
+    g = HipRun(p)
     assert g.plan.mode == 1
     out, lse = g.fwd()
     ro, rl, _ = O.sink_attention_forward(*oracle_inputs(p))

@@ -11,7 +11,7 @@ import torch
 import oracle as O
 from softmax_sink_amd import binding as B
 from softmax_sink_amd import workloads as W
-from tests.gpu_util import (GpuRun, TOL, dev_sinks, log, max_abs, sampled_rows_error,
+from tests.gpu_util import (HipRun, TOL, dev_sinks, log, max_abs, sampled_rows_error,
                             to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -39,7 +39,7 @@ def _check_paged(p, layout):
         f"H={p.num_heads_q}/{p.num_heads_k} D={p.head_dim}")
     kc, vc, out, lse = _run_paged(p, layout)
     # the contiguous forward on the same data: identical tiles, identical bits
-    g = GpuRun(p)
+    g = HipRun(p)
     g.fwd()
     same_out = torch.equal(out.view(torch.int16), g.out.view(torch.int16))
     same_lse = torch.equal(lse.view(torch.int32), g.lse.view(torch.int32))
@@ -191,7 +191,7 @@ def test_paged_cache_past_2_and_4_gib(gib):
         log(f"paged cache {gib} GiB ({num_blocks} pages), mode {int(plan.meta[14])}, "
             f"pages {int(top.min())}..{int(top.max())}")
         out, lse = B.forward_paged(plan, to_dev(p, "q"), kc, vc, dev_sinks(p), float(p.scale))
-        g = GpuRun(p)
+        g = HipRun(p)
         g.fwd()
         assert torch.equal(out.view(torch.int16), g.out.view(torch.int16))
         assert torch.equal(lse.view(torch.int32), g.lse.view(torch.int32))

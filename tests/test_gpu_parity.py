@@ -10,7 +10,7 @@ import torch
 import oracle as O
 from softmax_sink_amd import binding as B
 from softmax_sink_amd import workloads as W
-from tests.gpu_util import GpuRun, TOL, dsink_error, log, max_abs, oracle_inputs, rel_l2
+from tests.gpu_util import HipRun, TOL, dsink_error, log, max_abs, oracle_inputs, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -20,7 +20,7 @@ def _check(p, with_sink=True, bwd=True, tol=None):
         f"H={p.num_heads_q}/{p.num_heads_k} D={p.head_dim} causal={p.causal} "
         f"win=({p.win_left},{p.win_right}) dtype={p.dtype} sink={with_sink}")
     tol = tol or TOL[p.dtype]
-    g = GpuRun(p, with_sink)
+    g = HipRun(p, with_sink)
     out, lse = g.fwd()
     args = oracle_inputs(p, with_sink)
     ro, rl, _ = O.sink_attention_forward(*args)
@@ -158,7 +158,7 @@ def test_bf16_decode_window_and_no_sink():
 
 def test_forward_is_deterministic_and_dkdv_too():
     p = W.make_problem(53, [333, 190], [333, 190], 4, 2, 128, causal=True, name="determinism")
-    g = GpuRun(p)
+    g = HipRun(p)
     o1, l1 = g.fwd()
     d1 = g.bwd()
     o2, l2 = g.fwd()
@@ -170,7 +170,7 @@ def test_forward_is_deterministic_and_dkdv_too():
 
 def test_guard_bands_untouched():
     p = W.make_problem(54, [129, 64], [129, 64], 4, 2, 128, causal=True, name="guard")
-    g = GpuRun(p)
+    g = HipRun(p)
     pad = 4096
     Tq, Tk, Hq, Hk, D = p.total_q, p.total_k, 4, 2, 128
 
@@ -198,7 +198,7 @@ def test_guard_bands_untouched():
 def test_autograd_wrapper_matches_direct_calls():
     p = W.make_problem(55, [120, 77], [120, 77], 4, 2, 128, causal=True, win_left=50,
                        name="autograd")
-    g = GpuRun(p)
+    g = HipRun(p)
     out, lse = g.fwd()
     dq, dk, dv, ds = g.bwd()
     q = g.q.clone().requires_grad_(True)

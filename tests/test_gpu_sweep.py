@@ -119,7 +119,7 @@ def test_random_paged(idx):
     import torch
 
     from softmax_sink_amd import binding as B
-    from tests.gpu_util import GpuRun, TOL, dev_sinks, max_abs, oracle_inputs, to_dev
+    from tests.gpu_util import HipRun, TOL, dev_sinks, max_abs, oracle_inputs, to_dev
     import oracle as O
 
     p, with_sink, layout, cache_layout = _draw_paged(idx)
@@ -137,7 +137,7 @@ def test_random_paged(idx):
     sinks = dev_sinks(p) if with_sink else None
     out, lse = B.forward_paged(plan, to_dev(p, "q"), kc, vc, sinks, float(p.scale))
     torch.cuda.synchronize()
-    g = GpuRun(p, with_sink)
+    g = HipRun(p, with_sink)
     g.fwd()
     same = (torch.equal(out.view(torch.int16), g.out.view(torch.int16)) and
             torch.equal(lse.view(torch.int32), g.lse.view(torch.int32)))

@@ -8,7 +8,7 @@ import torch
 
 import oracle as O
 from softmax_sink_amd import workloads as W
-from tests.gpu_util import GpuRun, TOL, log, max_abs, oracle_inputs, rel_l2
+from tests.gpu_util import HipRun, TOL, log, max_abs, oracle_inputs, rel_l2
 from tests.gpu_util import sampled_rows_error as _sampled_rows
 
 pytestmark = pytest.mark.gpu
@@ -23,7 +23,7 @@ def _fwd_heads(p, g, out, lse, heads):
 def test_prefill_varlen_full_size():
     p = W.config("prefill_varlen")
     log(f"prefill_varlen: Tq={p.total_q} lens={np.diff(p.cu_q).tolist()}")
-    g = GpuRun(p)
+    g = HipRun(p)
     out, lse = g.fwd()
     e_out, e_lse = _fwd_heads(p, g, out, lse, [0, 9, 22, 31])
     s_out, s_lse = _sampled_rows(p, out, lse, 256, 1)
@@ -45,7 +45,7 @@ def test_prefill_varlen_full_size():
 def test_training_workloads_full_size(name, heads, dsink_heads):
     p = W.config(name)
     log(f"{name}: Tq={p.total_q} lens={np.diff(p.cu_q).tolist()} H={p.num_heads_q}/{p.num_heads_k}")
-    g = GpuRun(p)
+    g = HipRun(p)
     out, lse = g.fwd()
     dq, dk, dv, ds = g.bwd()
     log("  GPU done; oracle on q-heads " + str(heads))
@@ -71,7 +71,7 @@ def test_training_workloads_full_size(name, heads, dsink_heads):
 def test_decode_softmax_n_full_size():
     p = W.config("decode_softmax_n")
     log(f"decode_softmax_n: Tq={p.total_q} Tk={p.total_k}")
-    g = GpuRun(p)
+    g = HipRun(p)
     assert g.plan.mode == 1
     out, lse = g.fwd()
     lk = np.diff(p.cu_k)
@@ -94,7 +94,7 @@ def test_gqa_window_bnsd_equals_packed_bitwise():
     p = W.config("gqa_window_bnsd")
     S = int(np.diff(p.cu_q)[0])
     log(f"gqa_window_bnsd: B={p.batch} S={S} H={p.num_heads_q}/{p.num_heads_k}")
-    g = GpuRun(p)
+    g = HipRun(p)
     g.fwd()
     g.bwd()
     plan = B.PaddedPlan(p.batch, S, S, None, None, p.num_heads_q, p.num_heads_k, p.head_dim,
@@ -121,7 +121,7 @@ def test_full_size_runs_are_reproducible(name):
     """Every output of a full-size workload is the same bits on a second and
     a third run (no atomics, fixed reduction orders; a race would show here)."""
     p = W.config(name)
-    g = GpuRun(p)
+    g = HipRun(p)
     train = name != "decode_softmax_n"
     runs = []
     for _ in range(3):
