@@ -14,7 +14,7 @@ sequence lengths, q, k, v, dO, sinks):
 * sink logits are fp32: drawn N(0, 1) per q-head ("learnable offset"), or a
   constant ln n for softmax_n problems.
 
-The named configurations follow the five workloads of the benchmark spec:
+Five named configurations are the reference workloads:
 ``softmax1_fp32`` (1 x 128 x 128, 1 head, D 64, n = 1, non-causal),
 ``prefill_varlen`` (16 sequences, lengths uniform in [64, 2048], 32/32
 heads, D 128, causal), ``train_varlen`` (8 sequences summing to 32768
