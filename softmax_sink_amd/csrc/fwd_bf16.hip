@@ -120,10 +120,9 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void fwd_prefill_kernel(FwdAr
   auto load_kv = [&](int row0, char* dst) __attribute__((always_inline)) {
     if constexpr (PAGED) {
       const int last = min(lk, span0 + kPageSpan) - 1;
-      pl.load(static_cast<const T*>(a.k), hk * a.page_head, a.page_row, a.page_stride, pages, off0, span0,
-              row0, last, a.page_size, a.page_magic, dst);
-      pl.load(static_cast<const T*>(a.v), hk * a.page_head, a.page_row, a.page_stride, pages, off0, span0,
-              row0, last, a.page_size, a.page_magic, dst + TILE);
+      pl.load_kv(static_cast<const T*>(a.k), static_cast<const T*>(a.v), hk * a.page_head, a.page_row,
+                 a.page_stride, pages, off0, span0, row0, last, a.page_size, a.page_magic, dst,
+                 dst + TILE);
     } else {
       kl.load(kp, kstride, row0, lk, dst);
       vl.load(vp, kstride, row0, lk, dst + TILE);
@@ -327,10 +326,9 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void fwd_split_kernel(FwdArgs
   // K and V rows [row0, row0 + BN) of the item into one LDS buffer
   auto load_kv = [&](int row0, char* dst) __attribute__((always_inline)) {
     if constexpr (PAGED) {
-      pl.load(static_cast<const T*>(a.k), hk * a.page_head, a.page_row, a.page_stride, pages, off0, k_lo, row0,
-              k_hi - 1, a.page_size, a.page_magic, dst);
-      pl.load(static_cast<const T*>(a.v), hk * a.page_head, a.page_row, a.page_stride, pages, off0, k_lo, row0,
-              k_hi - 1, a.page_size, a.page_magic, dst + TILE);
+      pl.load_kv(static_cast<const T*>(a.k), static_cast<const T*>(a.v), hk * a.page_head, a.page_row,
+                 a.page_stride, pages, off0, k_lo, row0, k_hi - 1, a.page_size, a.page_magic, dst,
+                 dst + TILE);
     } else {
       kl.load(kp, kstride, row0, k_hi, dst);
       kl.load(vp, kstride, row0, k_hi, dst + TILE);

@@ -125,30 +125,41 @@ struct PagedTileDma {
     lcol = (((threadIdx.x % (DS / 8)) ^ swz<DS>(lrow)) * 16);
     wave_off = __builtin_amdgcn_readfirstlane((threadIdx.x / 64) * 1024);
   }
+  // The K and V tiles of the same rows: each lane finds its row's page slot
+  // once and issues both transfers (the two caches share their layout).
   template <typename T>
-  __device__ __forceinline__ void load(const T* cache, int64_t head_off, int64_t row_stride,
-                                       int64_t page_stride, const int* pages, int off0, int k_lo, int row0,
-                                       int row_last, int block_size, uint32_t magic,
-                                       char* tile) const {
-    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(tile + wave_off));
+  __device__ __forceinline__ void load_kv(const T* kcache, const T* vcache, int64_t head_off,
+                                          int64_t row_stride, int64_t page_stride, const int* pages,
+                                          int off0, int k_lo, int row0, int row_last, int block_size,
+                                          uint32_t magic, char* ktile, char* vtile) const {
+    const uint32_t kl0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(ktile + wave_off));
+    const uint32_t vl0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(vtile + wave_off));
 #pragma unroll
     for (int s = 0; s < kPer; ++s) {
       const int row = min(row0 + lrow + s * kRowsPerPass, row_last);
       const uint32_t num = (uint32_t)(row - k_lo + off0);
       const uint32_t pi = __umulhi(num, magic);
       const int slot = (int)(num - pi * (uint32_t)block_size);
-      const int64_t phys = pages[pi];
-      const char* src = reinterpret_cast<const char*>(
-                            cache + phys * page_stride + slot * row_stride + head_off) + lcol;
+      const int64_t elem = (int64_t)pages[pi] * page_stride + slot * row_stride + head_off;
+      const char* ks = reinterpret_cast<const char*>(kcache + elem) + lcol;
+      const char* vs = reinterpret_cast<const char*>(vcache + elem) + lcol;
 #pragma unroll
-      for (int sl = 0; sl < kSlices; ++sl)
+      for (int sl = 0; sl < kSlices; ++sl) {
         asm volatile(
             "s_nop 0\n\t"
             "global_load_lds_dwordx4 %0, off"
             :
-            : "v"(src + sl * DS * 2), "{m0}"(lds0 + sl * kSliceBytes<D> + s * THREADS * 16)
+            : "v"(ks + sl * DS * 2), "{m0}"(kl0 + sl * kSliceBytes<D> + s * THREADS * 16)
             : "memory");
+        asm volatile(
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %0, off"
+            :
+            : "v"(vs + sl * DS * 2), "{m0}"(vl0 + sl * kSliceBytes<D> + s * THREADS * 16)
+            : "memory");
+      }
     }
   }
 };
