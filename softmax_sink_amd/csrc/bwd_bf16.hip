@@ -115,7 +115,10 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // role 0 holds K rows (B operand of S = Q K^T), role 1 V rows (of dP = dO V^T)
   const T* fp = static_cast<const T*>(role == 0 ? a.k : a.v) + koff;
   vec8<T> frag[KB][NT];
-  int ilo[KB], ihi[KB];
+  // kept query rows of each key as start and span of one unsigned range
+  // test; a key without rows gets a start above every row index
+  int ilo[KB];
+  uint32_t ispan[KB];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     const int j = jbase + 32 * kb;
@@ -123,7 +126,10 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     for (int t = 0; t < NT; ++t)
       frag[kb][t] = j < lk ? __builtin_bit_cast(vec8<T>, ld16(fp + (int64_t)j * kstride + 16 * t + 8 * hl))
                            : vec8<T>{};
-    key_row_range(j, lq, lk, a.causal, a.win_left, a.win_right, ilo[kb], ihi[kb]);
+    int lo, hi;
+    key_row_range(j, lq, lk, a.causal, a.win_left, a.win_right, lo, hi);
+    ilo[kb] = hi < lo ? 1 << 30 : lo;
+    ispan[kb] = hi < lo ? 0u : (uint32_t)(hi - lo);
   }
 
   f32x16 acc[NB][KB];                            // role 0: dV^T, role 1: dK^T
@@ -256,7 +262,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
             const int i = qt * BM + 32 * qb + 8 * (r >> 2) + 4 * hl + (r & 3);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
-              if (i < ilo[kb] || i > ihi[kb]) x[kb][r] = kNegInf;
+              if ((uint32_t)(i - ilo[kb]) > ispan[kb]) x[kb][r] = kNegInf;
           }
         }
 #pragma unroll
@@ -424,6 +430,10 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdArgs a)
   const float c2 = a.scale * kLog2e;
   int jlo, jhi;
   row_key_range(i, lq, lk, a.causal, a.win_left, a.win_right, jlo, jhi);
+  // the partial-tile mask as one unsigned range test; a row without keys
+  // gets a start above every key index
+  const int jlo_m = jhi < jlo ? 1 << 30 : jlo;
+  const uint32_t jspan = jhi < jlo ? 0u : (uint32_t)(jhi - jlo);
 
   f32x16 o[NB];
 #pragma unroll
@@ -466,7 +476,7 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdArgs a)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int jj = kt * BN + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (jj < jlo || jj > jhi) s[r] = kNegInf;
+          if ((uint32_t)(jj - jlo_m) > jspan) s[r] = kNegInf;
         }
       }
 #pragma unroll

@@ -97,6 +97,10 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void fwd_prefill_kernel(FwdAr
 
   int jlo, jhi;
   row_key_range(i, lq, lk, a.causal, a.win_left, a.win_right, jlo, jhi);
+  // the partial-tile mask as one unsigned range test; a row without keys
+  // gets a start above every key index, so that every j - jlo wraps high
+  const int jlo_m = jhi < jlo ? 1 << 30 : jlo;
+  const uint32_t jspan = jhi < jlo ? 0u : (uint32_t)(jhi - jlo);
 
   TileDma<D> kl, vl;
   PagedTileDma<D> pl;
@@ -163,13 +167,12 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void fwd_prefill_kernel(FwdAr
 
     // mask (partial tiles only): key of slot r is kt*BN + 32kb + 8(r/4) + 4hl + r%4
     if (kt < kf_lo || kt >= kf_hi) {
+      const int d0 = kt * BN + 4 * hl - jlo_m;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = kt * BN + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (j < jlo || j > jhi) s[kb][r] = kNegInf;
-        }
+        for (int r = 0; r < 16; ++r)
+          if ((uint32_t)(d0 + kb * 32 + 8 * (r >> 2) + (r & 3)) > jspan) s[kb][r] = kNegInf;
     }
 
     float mx = kNegInf;
