@@ -1,7 +1,7 @@
 """Throughput of packed (THD) sink attention on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                [--no-cpu-baseline]
+                [--no-cpu-baseline] [--no-configs]
 
 One step = the whole hot path over one batch: the host tile schedule
 (sink_attn_metadata, sink_attn_metadata_paged or sink_attn_metadata_padded)
@@ -10,6 +10,11 @@ reading a paged K/V cache, or sink_attn_fwd_padded for a batch-padded
 layout) and, for training workloads, the backward (sink_attn_bwd or
 sink_attn_bwd_padded), all through the C ABI on torch's current stream. Inputs are resident in HBM
 before timing starts. Prints one JSON line.
+
+With the default workload (train_varlen, the configuration the headline
+metric is quoted on) the line also carries "configs": the prefill, GQA
+sliding-window training and decode configurations timed in the same run,
+each in its own launch configuration.
 
 FLOPs count only kept (query row, key, q-head) pairs: 4*D per pair forward,
 10*D backward (the backward recomputes S). Bytes (decode) count K and V read
@@ -69,7 +74,6 @@ def cpu_baseline(p, train, seconds):
     taken in a fixed order (median-length sequence first, heads in order)
     until about `seconds` of work has been done."""
     import oracle as O
-    from threadpoolctl import threadpool_info
     lens = np.diff(p.cu_q)
     order = list(np.argsort(lens, kind="stable"))
     order = order[len(order) // 2:] + order[:len(order) // 2][::-1]
@@ -98,13 +102,58 @@ def cpu_baseline(p, train, seconds):
             break
     dt = time.perf_counter() - t0
     flops = pairs * p.head_dim * (14 if train else 4)
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    threads = blas_threads()
     seqs = sorted({b for b, _ in done})
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", **host_cores(),
             "sample": f"{len(done)} (sequence, q-head) slices from sequences {seqs}: "
                       f"{'forward+backward' if train else 'forward'}, {pairs} kept pairs, "
                       f"{dt:.1f} s (FLOPs counted as in value)"}
+
+
+def blas_threads():
+    """Threads of the BLAS library NumPy calls (the oracle's matrix products
+    run on these; its elementwise work runs on one core)."""
+    from threadpoolctl import threadpool_info
+    return max([i.get("num_threads", 1) for i in threadpool_info()
+                if i.get("user_api") == "blas"] or [1])
+
+
+def host_cores():
+    """The host's logical CPUs, the CPUs this process may run on, and the
+    BLAS thread count, reported beside the oracle's rate."""
+    return {"cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
+            "blas_threads": blas_threads()}
+
+
+def other_configs():
+    """The other reference configurations, each timed in its own default
+    launch configuration (forward-only workloads: 100 steps after 20; the
+    GQA window training step: 10 after 3): step time, throughput and the
+    dominant kernel's share of its roofline."""
+    import torch
+    out = {}
+    for name, steps, warmup in (("prefill_varlen", 100, 20), ("gqa_window", 10, 3),
+                                ("decode_softmax_n", 100, 20)):
+        print(f"# configuration {name}", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+        r, _, _ = run_workload(name, steps, warmup, progress=False)
+        roof = r["roofline"]
+        c = {"metric": r["metric"], "ms_per_step": r["ms_per_step"], "steps": steps,
+             "warmup": warmup, "dtype": r["dtype"]}
+        if "value_gbs" in r:
+            c.update(value=r["value_gbs"], unit="GB/s",
+                     frac_of_hbm_peak=r["value_gbs"] / PEAK_HBM_GBS, tflops=r["value"])
+        else:
+            c.update(value=r["value"], unit="TFLOP/s", frac_of_bf16_peak=r["value"] / PEAK_BF16_TFLOPS)
+        c["roofline"] = {k: roof[k] for k in ("bound", "kernel", "achieved", "peak", "unit",
+                                              "frac", "launch_ms")}
+        c["config"] = {k: r["config"][k] for k in ("batch", "total_q", "total_k", "heads_q",
+                                                   "heads_kv", "head_dim", "causal", "window",
+                                                   "seed", "kept_pairs", "passes")}
+        out[name] = c
+    torch.cuda.empty_cache()
+    return out
 
 
 def traffic_record(workload, kernel):
@@ -176,7 +225,6 @@ def bench_merge(args):
                         "traffic": traffic_record("cp_merge", "merge_kernel"),
                         "launch_ms": kms, "bytes_per_launch": nbytes}}
     if not args.no_cpu_baseline:
-        from threadpoolctl import threadpool_info
         rows, t = 0, time.perf_counter()
         while time.perf_counter() - t < min(args.cpu_seconds, 5.0):
             a = rows % Tq
@@ -184,57 +232,23 @@ def bench_merge(args):
             O.merge_partials(W.bf16_bits_to_f32(outs[:, a:b]), lses[:, :, a:b], sinks)
             rows += b - a
         dt = time.perf_counter() - t
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
         res["cpu_baseline"] = {"value": nbytes * rows / Tq / dt / 1e9, "unit": "GB/s",
-                               "cores": int(threads), "kind": "oracle",
+                               "cores": 1, "kind": "oracle", **host_cores(),
                                "sample": f"{rows} of {Tq} token rows (all heads), {dt:.1f} s"}
     print(json.dumps(res), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None,
-                    help="timed steps (default: 10 for training workloads, 100 otherwise)")
-    ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed steps first (default: 3 for training workloads, 20 otherwise)")
-    ap.add_argument("--workload", default="train_varlen")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
-                    help="first run a plain device-to-device copy of BYTES bytes "
-                         "three times (reference for HBM traffic counters)")
-    args = ap.parse_args()
-    # A forward-only step takes well under a millisecond: ten of them time a
-    # few milliseconds of work, which reads 5-15% slower than a longer run.
-    if args.steps is None:
-        args.steps = 10 if args.workload in TRAIN else 100
-    if args.warmup is None:
-        args.warmup = 3 if args.workload in TRAIN else 20
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the library has no multi-GPU path "
-              f"(asked for --gpus {args.gpus})", file=sys.stderr)
-        sys.exit(2)
-
+def run_workload(name, steps, warmup, progress=True):
+    """Times `steps` steps of workload `name` after `warmup` untimed ones.
+    Returns (result dict, the workload's Problem, training?)."""
     import torch
     from softmax_sink_amd import binding as B
     from softmax_sink_amd import workloads as W
 
-    torch.cuda.set_device(0)
-    if args.calibrate_copy:
-        src = torch.empty(args.calibrate_copy, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-    if args.workload == "cp_merge":
-        bench_merge(args)
-        return
-    p = W.config(args.workload)
-    train = args.workload in TRAIN
+    p = W.config(name)
+    train = name in TRAIN
     paged = "paged" in p.meta
-    decode = args.workload in ("decode_softmax_n", "decode_paged")
+    decode = name in ("decode_softmax_n", "decode_paged")
     padded = p.meta.get("layout")          # "BNSD": a batch-padded layout
     D, Hq, Hk = p.head_dim, p.num_heads_q, p.num_heads_k
     if padded:
@@ -344,18 +358,19 @@ def main():
             if timed:
                 main_events.append(("bwd", b0, b1))
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i, False)
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
-    for i in range(args.steps):
-        step(args.warmup + i, True)
-        print(f"# step {i + 1}/{args.steps} enqueued", file=sys.stderr, flush=True)
+    for i in range(steps):
+        step(warmup + i, True)
+        if progress:
+            print(f"# step {i + 1}/{steps} enqueued", file=sys.stderr, flush=True)
     t1.record()
     torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
+    ms = t0.elapsed_time(t1) / steps
 
     pairs = kept_pairs(p.cu_q, p.cu_k, p.causal, p.win_left, p.win_right) * Hq
     fwd_flops = 4.0 * D * pairs
@@ -376,7 +391,7 @@ def main():
         achieved = alg_bytes / (kavg["fwd"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": "fwd_split_kernel", "achieved": achieved,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                "traffic": traffic_record(args.workload, "fwd_split_kernel"),
+                "traffic": traffic_record(name, "fwd_split_kernel"),
                 "launch_ms": kavg["fwd"], "bytes_per_launch": alg_bytes}
     else:
         # dominant kernel: the dK/dV loop (S, dP, dV, dK: 8*D per kept pair)
@@ -388,16 +403,16 @@ def main():
         achieved = flops / (kavg[name] * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": kname, "achieved": achieved, "peak": peak,
                 "unit": "TFLOP/s", "frac": achieved / peak,
-                "traffic": traffic_record(args.workload, kname),
+                "traffic": traffic_record(name, kname),
                 "launch_ms": kavg[name], "flop_per_launch": flops}
     res = {
         "metric": METRIC if train else
         ("sink-attention decode forward TFLOP/s (split-KV" + (", paged K/V)" if paged else ")")
          if decode else "sink-attention forward TFLOP/s" + (" (paged K/V)" if paged else "")),
-        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": p.dtype, "data": "synthetic",
-        "config": {"workload": args.workload, "batch": p.batch, "total_q": p.total_q,
+        "config": {"workload": name, "batch": p.batch, "total_q": p.total_q,
                    "total_k": p.total_k, "heads_q": Hq, "heads_kv": Hk, "head_dim": D,
                    "causal": p.causal, "window": [p.win_left, p.win_right],
                    "seed": p.seed, "kept_pairs": pairs,
@@ -411,6 +426,55 @@ def main():
     }
     if decode:
         res["value_gbs"] = alg_bytes / (ms * 1e-3) / 1e9
+    return res, p, train
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 10 for training workloads, 100 otherwise)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default: 3 for training workloads, 20 otherwise)")
+    ap.add_argument("--workload", default="train_varlen")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="with the default workload, skip timing the other reference "
+                         "configurations (prefill_varlen, gqa_window, decode_softmax_n)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="first run a plain device-to-device copy of BYTES bytes "
+                         "three times (reference for HBM traffic counters)")
+    args = ap.parse_args()
+    # A forward-only step takes well under a millisecond: ten of them time a
+    # few milliseconds of work, which reads 5-15% slower than a longer run.
+    if args.steps is None:
+        args.steps = 10 if args.workload in TRAIN else 100
+    if args.warmup is None:
+        args.warmup = 3 if args.workload in TRAIN else 20
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from softmax_sink_amd import binding as B
+    from softmax_sink_amd import workloads as W
+
+    torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        src = torch.empty(args.calibrate_copy, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.workload == "cp_merge":
+        bench_merge(args)
+        return
+    res, p, train = run_workload(args.workload, args.steps, args.warmup)
+    if args.workload == "train_varlen" and not args.no_configs:
+        res["configs"] = other_configs()
     if not args.no_cpu_baseline:
         print("# timing the oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(p, train, args.cpu_seconds)

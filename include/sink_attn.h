@@ -32,6 +32,17 @@
  *   dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i,
  *   dv_j = sum_i P_ij dO_i  (dk, dv summed over the q-heads of a group),
  *   dsink_h = -sum_i e^{s_h - lse_i} D_i.
+ * D_i is formed from the stored out (in the input dtype), as the "slime"
+ * page's backward feeds its rounded output to the vanilla backward. For a
+ * single head, dsink is a sum of random-sign terms over all of that head's
+ * rows and can cancel by two orders of magnitude; the rounding of out to
+ * bf16 (at most half a bf16 step per element) then moves it by a few
+ * percent of its value (about 5% on one head of a 32k-token causal batch),
+ * while the [num_heads_q] vector as a whole stays within 2e-2 relative L2 of
+ * the exact gradient. In fp32, dsink is exact to about 1e-5 of the sum of
+ * its terms' magnitudes.
+ * Windows of max_seqlen_q + max_seqlen_k or more exclude no key and are
+ * treated as unbounded.
  *
  * Layouts (all contiguous, row-major, base pointers 16-byte aligned). The
  * packed TND layout of the sink_attn_fwd / _bwd / _fwd_paged calls:

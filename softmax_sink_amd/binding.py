@@ -54,6 +54,17 @@ class Problem(ctypes.Structure):
         "layout_q", "layout_out", "seq_q", "seq_k")]
 
 
+def _problem(*fields):
+    """Problem from Python ints, each checked to fit its int32 field (ctypes
+    would silently keep only the low 32 bits, e.g. turn a window of
+    2**32 + 5 into 5)."""
+    vals = [int(x) for x in fields]
+    for (name, _), x in zip(Problem._fields_, vals):
+        if not -2 ** 31 <= x < 2 ** 31:
+            raise ValueError(f"{name} = {x} does not fit an int32 field")
+    return Problem(*vals)
+
+
 PA_BBND, PA_BNBD = 0, 1
 CACHE_LAYOUTS = {"BBND": PA_BBND, "BNBD": PA_BNBD}
 
@@ -203,10 +214,10 @@ def make_problem(cu_q, cu_k, num_heads_q, num_heads_k, head_dim, causal,
     cu_q = np.asarray(cu_q, dtype=np.int32)
     cu_k = np.asarray(cu_k, dtype=np.int32)
     lq, lk = np.diff(cu_q), np.diff(cu_k)
-    return Problem(len(cu_q) - 1, num_heads_q, num_heads_k, head_dim,
-                   int(cu_q[-1]), int(cu_k[-1]),
-                   int(lq.max()) if len(lq) else 0, int(lk.max()) if len(lk) else 0,
-                   int(bool(causal)), int(win_left), int(win_right), int(dtype))
+    return _problem(len(cu_q) - 1, num_heads_q, num_heads_k, head_dim,
+                    int(cu_q[-1]), int(cu_k[-1]),
+                    int(lq.max()) if len(lq) else 0, int(lk.max()) if len(lk) else 0,
+                    int(bool(causal)), win_left, win_right, dtype)
 
 
 def _metadata(name, call, words, out):
@@ -257,11 +268,11 @@ def make_problem_padded(batch, seq_q, seq_k, seqused_q, seqused_kv, num_heads_q,
     lk = np.full(batch, seq_k) if seqused_kv is None else np.asarray(seqused_kv)
     lay = LAYOUTS[layout]
     lay_out = lay if layout_out is None else LAYOUTS[layout_out]
-    return Problem(int(batch), num_heads_q, num_heads_k, head_dim,
-                   int(batch) * int(seq_q), int(batch) * int(seq_k),
-                   int(lq.max()) if len(lq) else 0, int(lk.max()) if len(lk) else 0,
-                   int(bool(causal)), int(win_left), int(win_right), int(dtype),
-                   lay, lay_out, int(seq_q), int(seq_k))
+    return _problem(int(batch), num_heads_q, num_heads_k, head_dim,
+                    int(batch) * int(seq_q), int(batch) * int(seq_k),
+                    int(lq.max()) if len(lq) else 0, int(lk.max()) if len(lk) else 0,
+                    int(bool(causal)), win_left, win_right, dtype,
+                    lay, lay_out, int(seq_q), int(seq_k))
 
 
 def sink_attn_metadata_padded(problem, seqused_q_host, seqused_kv_host, out=None):

@@ -38,6 +38,17 @@ sink_attn_status common_checks(const sink_attn_problem* p,
   return check_header(*p, meta_host, kv);
 }
 
+// Window bound handed to the kernels. A window of max_seqlen_q +
+// max_seqlen_k or more never excludes a key (the bottom-right aligned row
+// position lies in [-max_seqlen_q, max_seqlen_k)), so it is passed on as
+// unbounded (-1): the kernels' 32-bit mask arithmetic then stays within
+// +-2^30 (validate_problem bounds every sequence below 2^28 rows).
+int kernel_window(int32_t w, const sink_attn_problem* p) {
+  if (w < 0) return -1;
+  return static_cast<int64_t>(w) >= static_cast<int64_t>(p->max_seqlen_q) + p->max_seqlen_k
+             ? -1 : w;
+}
+
 FwdArgs fwd_args(const sink_attn_problem* p, const void* q, const void* k,
                  const void* v, const int32_t* cu_q, const int32_t* cu_k,
                  const int32_t* used_q, const int32_t* used_k,
@@ -50,7 +61,9 @@ FwdArgs fwd_args(const sink_attn_problem* p, const void* q, const void* k,
   a.out = out; a.lse = lse;
   a.batch = p->batch; a.hq = p->num_heads_q; a.hk = p->num_heads_k;
   a.group = p->num_heads_q / p->num_heads_k;
-  a.causal = p->causal; a.win_left = p->win_left; a.win_right = p->win_right;
+  a.causal = p->causal;
+  a.win_left = kernel_window(p->win_left, p);
+  a.win_right = kernel_window(p->win_right, p);
   a.total_q = p->total_q; a.total_k = p->total_k;
   a.scale = scale;
   return a;
@@ -154,7 +167,9 @@ sink_attn_status bwd_impl(const sink_attn_problem* p, const int32_t* meta_host,
   a.part = reinterpret_cast<float*>(base + w.part_off);
   a.batch = p->batch; a.hq = p->num_heads_q; a.hk = p->num_heads_k;
   a.group = p->num_heads_q / p->num_heads_k;
-  a.causal = p->causal; a.win_left = p->win_left; a.win_right = p->win_right;
+  a.causal = p->causal;
+  a.win_left = kernel_window(p->win_left, p);
+  a.win_right = kernel_window(p->win_right, p);
   a.total_q = p->total_q; a.total_k = p->total_k;
   a.scale = scale;
   const TimingHook t = take_timing();

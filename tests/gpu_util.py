@@ -52,6 +52,17 @@ class HipRun:
         return f(dq), f(dk), f(dv), (ds.cpu().numpy().astype(np.float64) if ds is not None else None)
 
 
+def per_head(fn, heads, workers=8):
+    """fn(h) for every head in `heads`, on a thread pool with one BLAS thread
+    per call: the oracle's elementwise NumPy work (exp, masks) runs on one
+    core per call, so heads side by side use the host's cores. Returns the
+    results in the order of `heads`."""
+    import concurrent.futures as cf
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1), cf.ThreadPoolExecutor(workers) as ex:
+        return list(ex.map(fn, heads))
+
+
 def oracle_inputs(p, with_sink=True):
     sinks = p.sinks.astype(np.float64) if with_sink else np.full(p.num_heads_q, -np.inf)
     return (p.as_f32("q"), p.as_f32("k"), p.as_f32("v"), p.cu_q, p.cu_k, sinks,

@@ -2,8 +2,8 @@
 {64, 128, 256}) through the C ABI: prefill forward and backward, split-KV
 decode, paged decode, a padded layout and the context-parallel merge, against
 the oracle with the bf16 tolerances. At this width the tiles live in LDS as
-two 128-column slices and dK/dV come from a two-pass kernel. Needs an
-MI355X."""
+two 128-column slices, and the dK/dV kernel walks 32-row query tiles so that
+its five stages fit the LDS. Needs an MI355X."""
 import math
 
 import numpy as np

@@ -212,3 +212,27 @@ def test_autograd_wrapper_matches_direct_calls():
     assert rel_l2(q.grad.float().cpu().numpy(), dq) < 1e-3
     assert np.array_equal(k.grad.float().cpu().numpy(), dk)
     assert np.array_equal(s.grad.cpu().numpy(), ds)
+
+
+@pytest.mark.parametrize("dtype,lens_q", [("bf16", [150, 77, 400]), ("fp32", [60, 7, 90]),
+                                          ("bf16", [3, 1, 5])])
+def test_int32_max_windows_equal_unbounded(dtype, lens_q):
+    """Windows of 2^31 - 1 (non-causal, both sides; causal, left) give the
+    same bits as unbounded windows: the host hands such windows to the
+    kernels as unbounded, so their 32-bit mask arithmetic cannot wrap. The
+    third case takes the split-KV decode path."""
+    big = 2 ** 31 - 1
+    lens_k = [300, 77, 90]
+    for causal, wl, wr in ((False, big, big), (True, big, 0)):
+        res = []
+        for w in ((wl, wr), (-1, 0 if causal else -1)):
+            p = W.make_problem(43, lens_q, lens_k, 4, 2, 64, dtype=dtype, causal=causal,
+                               win_left=w[0], win_right=w[1], name="int32_max_window")
+            log(f"case int32 max window: dtype={dtype} causal={causal} win={w}")
+            g = HipRun(p)
+            g.fwd()
+            g.bwd()
+            res.append([g.out, g.lse, g.dq, g.dk, g.dv, g.dsink])
+        bits = lambda t: t.view(torch.int16) if t.dtype in (torch.bfloat16, torch.float16) else t
+        for a, b in zip(*res):
+            assert torch.equal(bits(a), bits(b))

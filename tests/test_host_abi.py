@@ -486,3 +486,35 @@ def test_head_dim_256_for_16_bit_types_only():
         with pytest.raises(B.SinkAttnError) as e:
             B.sink_attn_metadata(p, cu, cu)
         assert e.value.status == B.E_UNSUPPORTED
+
+
+def test_huge_windows_schedule_as_unbounded():
+    """A window of max_seqlen_q + max_seqlen_k or more excludes no key: the
+    schedule (and, in the GPU tests, every output) equals the unbounded one,
+    also at the int32 limit, where the kernels' 32-bit mask arithmetic would
+    otherwise wrap."""
+    cu_q = np.array([0, 5, 300, 301], np.int32)
+    cu_k = np.array([0, 200, 210, 600], np.int32)
+    big = 2 ** 31 - 1
+    for causal, wl, wr in ((True, big, 0), (False, big, big), (False, -1, big),
+                           (False, 210 + 390, 600)):
+        base_wl = -1 if wl >= 600 else wl
+        base_wr = -1 if wr >= 600 else wr
+        if causal:
+            base_wr = wr
+        m1 = _check_against_oracle(cu_q, cu_k, causal, wl, wr)
+        m0 = _check_against_oracle(cu_q, cu_k, causal, base_wl, base_wr)
+        for nw, ow in ((W_NFWD, W_FWDOFF), (W_NBWD, W_BWDOFF)):
+            assert _items(m1, nw, ow) == _items(m0, nw, ow)
+
+
+def test_problem_fields_must_fit_int32():
+    cu = np.array([0, 10], np.int32)
+    with pytest.raises(ValueError):
+        B.make_problem(cu, cu, 4, 2, 128, False, 2 ** 32 + 5, -1)
+    with pytest.raises(ValueError):
+        B.make_problem(cu, cu, 4, 2, 128, False, -1, -2 ** 31 - 1)
+    with pytest.raises(ValueError):
+        B.make_problem_padded(2, 8, 8, None, None, 4, 2, 128, False, 2 ** 40, -1)
+    p = B.make_problem(cu, cu, 4, 2, 128, False, 2 ** 31 - 1, 2 ** 31 - 1)
+    assert p.win_left == 2 ** 31 - 1 and p.win_right == 2 ** 31 - 1

@@ -543,3 +543,39 @@ def test_keep_row_is_a_row_of_keep_mask():
             full = O.keep_mask(lq, lk, causal, wl, wr)
             for i in range(lq):
                 assert np.array_equal(O.keep_row(i, lq, lk, causal, wl, wr), full[i])
+
+
+@pytest.mark.parametrize("mask", [(True, -1, -1), (True, 4, 0), (False, 3, 2), (False, -1, -1)])
+def test_sampled_rows_equal_full_problem_rows(mask):
+    """sink_attention_rows (the oracle behind the sampled-row checks of the
+    full-size workloads) returns, for every (token, q-head), exactly the row
+    of the full forward (out, lse) and backward (dq): packed batch with empty
+    query and key sequences between non-empty ones (a token right after an
+    empty sequence belongs to the next non-empty one), GQA (6 q-heads on 2
+    kv-heads), windows, and sequences with Lq > Lk and Lq < Lk."""
+    causal, wl, wr = mask
+    rng = np.random.default_rng(27)
+    lens = [(5, 9), (0, 4), (0, 0), (7, 3), (4, 0), (6, 6), (1, 11)]
+    Hq, Hk, D, scale = 6, 2, 8, 0.35
+    cu_q = np.r_[0, np.cumsum([a for a, _ in lens])]
+    cu_k = np.r_[0, np.cumsum([b for _, b in lens])]
+    q = _rand(rng, cu_q[-1], Hq, D)
+    k = _rand(rng, cu_k[-1], Hk, D)
+    v = _rand(rng, cu_k[-1], Hk, D)
+    dout = _rand(rng, cu_q[-1], Hq, D)
+    sinks = np.array([0.2, -0.7, 1.3, -np.inf, 0.0, 2.1])
+    out, lse, _ = O.sink_attention_forward(q, k, v, cu_q, cu_k, sinks, scale, causal, wl, wr)
+    dq = O.sink_attention_backward(dout, q, k, v, cu_q, cu_k, sinks, scale, causal, wl, wr)[0]
+    rows = [(t, h) for t in range(cu_q[-1]) for h in range(Hq)]
+    got = O.sink_attention_rows(q, k, v, cu_q, cu_k, sinks, scale, causal, wl, wr, rows,
+                                dout=dout)
+    for (t, h), r in zip(rows, got):
+        np.testing.assert_allclose(r["out"], out[t, h], rtol=1e-13, atol=1e-15)
+        assert (r["lse"] == lse[h, t]) or abs(r["lse"] - lse[h, t]) <= 1e-13 * abs(lse[h, t])
+        np.testing.assert_allclose(r["dq"], dq[t, h], rtol=1e-12, atol=1e-14)
+    # the checks above see rows of every kind: kept keys, fully masked rows
+    # with a sink (lse = s; the sequence with no keys gives them), and with
+    # no sink (lse = -inf)
+    t_empty = cu_q[4]                       # first row of the (4, 0) sequence
+    assert np.isneginf(lse[3, t_empty]) and lse[0, t_empty] == sinks[0]
+    assert np.isfinite(lse[3]).any()
