@@ -127,32 +127,35 @@ def host_cores():
 
 
 def other_configs():
-    """The other reference configurations, each timed in its own default
-    launch configuration (forward-only workloads: 100 steps after 20; the
-    GQA window training step: 10 after 3): step time, throughput and the
-    dominant kernel's share of its roofline."""
-    import torch
+    """The other reference configurations, each timed in a process of its
+    own (as a standalone run of this script would time it) and in its own
+    default launch configuration (forward-only workloads: 100 steps after
+    20; the GQA window training step: 10 after 3): step time, throughput and
+    the dominant kernel's share of its roofline."""
+    import subprocess
     out = {}
-    for name, steps, warmup in (("prefill_varlen", 100, 20), ("gqa_window", 10, 3),
-                                ("decode_softmax_n", 100, 20)):
+    for name in ("prefill_varlen", "gqa_window", "decode_softmax_n"):
         print(f"# configuration {name}", file=sys.stderr, flush=True)
-        torch.cuda.empty_cache()
-        r, _, _ = run_workload(name, steps, warmup, progress=False)
-        roof = r["roofline"]
-        c = {"metric": r["metric"], "ms_per_step": r["ms_per_step"], "steps": steps,
-             "warmup": warmup, "dtype": r["dtype"]}
-        if "value_gbs" in r:
-            c.update(value=r["value_gbs"], unit="GB/s",
-                     frac_of_hbm_peak=r["value_gbs"] / PEAK_HBM_GBS, tflops=r["value"])
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--workload", name,
+                            "--no-cpu-baseline"], capture_output=True, text=True, timeout=600)
+        lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+        if r.returncode != 0 or not lines:
+            raise RuntimeError(f"configuration {name} failed (exit {r.returncode}):\n"
+                               f"{r.stderr[-2000:]}")
+        d = json.loads(lines[-1])
+        roof = d["roofline"]
+        c = {"metric": d["metric"], "ms_per_step": d["ms_per_step"], "steps": d["steps"],
+             "warmup": d["warmup"], "dtype": d["dtype"]}
+        if "value_gbs" in d:
+            c.update(value=d["value_gbs"], unit="GB/s",
+                     frac_of_hbm_peak=d["value_gbs"] / PEAK_HBM_GBS, tflops=d["value"])
         else:
-            c.update(value=r["value"], unit="TFLOP/s", frac_of_bf16_peak=r["value"] / PEAK_BF16_TFLOPS)
+            c.update(value=d["value"], unit="TFLOP/s",
+                     frac_of_bf16_peak=d["value"] / PEAK_BF16_TFLOPS)
         c["roofline"] = {k: roof[k] for k in ("bound", "kernel", "achieved", "peak", "unit",
-                                              "frac", "launch_ms")}
-        c["config"] = {k: r["config"][k] for k in ("batch", "total_q", "total_k", "heads_q",
-                                                   "heads_kv", "head_dim", "causal", "window",
-                                                   "seed", "kept_pairs", "passes")}
+                                              "frac", "traffic", "launch_ms")}
+        c["config"] = d["config"]
         out[name] = c
-    torch.cuda.empty_cache()
     return out
 
 
@@ -396,15 +399,15 @@ def run_workload(name, steps, warmup, progress=True):
     else:
         # dominant kernel: the dK/dV loop (S, dP, dV, dK: 8*D per kept pair)
         # for training, the prefill tile loop (QK^T, PV: 4*D) otherwise
-        name = "bwd" if train else "fwd"
+        phase = "bwd" if train else "fwd"
         flops = (8.0 * D * pairs) if train else fwd_flops
         kname = "bwd_dkdv_kernel" if train else "fwd_prefill_kernel"
         peak = PEAK_BF16_TFLOPS if p.dtype == "bf16" else PEAK_FP32_TFLOPS
-        achieved = flops / (kavg[name] * 1e-3) / 1e12
+        achieved = flops / (kavg[phase] * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": kname, "achieved": achieved, "peak": peak,
                 "unit": "TFLOP/s", "frac": achieved / peak,
                 "traffic": traffic_record(name, kname),
-                "launch_ms": kavg[name], "flop_per_launch": flops}
+                "launch_ms": kavg[phase], "flop_per_launch": flops}
     res = {
         "metric": METRIC if train else
         ("sink-attention decode forward TFLOP/s (split-KV" + (", paged K/V)" if paged else ")")

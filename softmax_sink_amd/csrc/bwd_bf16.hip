@@ -249,6 +249,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         f32x16 x[KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) x[kb] = f32x16{};
+        mfma_priority_high();
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           const vec8<T> qa = lds_row_chunk<D, T, BM>(q_l, 32 * qb + c, 2 * t + hl);
@@ -274,6 +275,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
             for (int kb = 0; kb < KB; ++kb)
               acc[db][kb] = mfma32(da, pf[qb][kb][h], acc[db][kb]);
           }
+        mfma_priority_low();
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_l + 32 * qb + 8 * g4 + 4 * hl);
@@ -313,6 +315,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
           f32x16 x[KB];
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) x[kb] = f32x16{};
+          mfma_priority_high();
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
             const vec8<T> ga = lds_row_chunk<D, T, BM>(do_l, 32 * qb + c, 2 * t + hl);
@@ -320,6 +323,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
             for (int kb = 0; kb < KB; ++kb) x[kb] = mfma32(ga, frag[kb][t], x[kb]);
           }
           sched_mfma_pipeline<KB * NT, KB, 1, 3>();
+          mfma_priority_low();
           vec8<T> pp[KB][2];                      // [kb][half]
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb)
@@ -338,6 +342,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
                 x[kb][r] = (float)pp[kb][r >> 3][r & 7] * (x[kb][r] - d4[e]);
             }
           }
+          mfma_priority_high();
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             vec8<T> sf[KB];
@@ -351,6 +356,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
             }
           }
           sched_mfma_pipeline<2 * KB * NB, KB, 2, 2>();
+          mfma_priority_low();
         }
       }
       finish(it, qs_next, ds);
@@ -463,12 +469,14 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdArgs a)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 s = f32x16{}, dp = f32x16{};
+      mfma_priority_high();
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         s = mfma32(lds_row_chunk<D, T>(kt_lds, kb * 32 + c, 2 * t + hl), qf[t], s);
         dp = mfma32(lds_row_chunk<D, T>(vt_lds, kb * 32 + c, 2 * t + hl), gf[t], dp);
       }
       sched_mfma_pipeline<2 * NT, 1, 1, 3>();
+      mfma_priority_low();
       // mask (partial tiles only) as S = -inf, so that P is 0: one uniform
       // branch around the whole block rather than one per element, which
       // would cut the softmax into 16 basic blocks
@@ -484,6 +492,7 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdArgs a)
         const float p = exp2_hw(__builtin_fmaf(s[r], c2, -lse2));
         dp[r] = p * (dp[r] - dval);          // scale is applied to dQ at the end
       }
+      mfma_priority_high();
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const vec8<T> sf = frag_half<T>(dp, hh);
@@ -492,6 +501,7 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdArgs a)
           o[n] = mfma32(lds_col_operand<D, T>(kt_lds, 32 * kb + 16 * hh, 32 * n), sf, o[n]);
       }
       sched_mfma_pipeline<2 * NB, 1, 2, 2>();
+      mfma_priority_low();
     }
     wait_vmem();        // the next tile has landed in LDS
     __syncthreads();

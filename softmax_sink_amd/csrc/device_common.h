@@ -212,6 +212,15 @@ __device__ __forceinline__ void sched_mfma_pipeline() {
   sched_group<kSchedMfma, LEAD * MFMAS>();
 }
 
+// Wave priority around the MFMA-dense stretches of a tile step (s_setprio
+// 1 before, 0 after): when the two waves of a SIMD both have an instruction
+// ready, the one feeding the matrix pipe issues first, and the other's
+// softmax / dS arithmetic fills the cycles the MFMAs leave free. Measured on
+// the training step: 1-3% faster end to end (the forward, dK/dV and dQ
+// kernels each a little faster), the prefill forward unchanged.
+__device__ __forceinline__ void mfma_priority_high() { __builtin_amdgcn_s_setprio(1); }
+__device__ __forceinline__ void mfma_priority_low() { __builtin_amdgcn_s_setprio(0); }
+
 // Global 16-byte load / store helpers.
 __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);

@@ -157,6 +157,7 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void fwd_prefill_kernel(FwdAr
 
     // S^T for the two 32-key blocks of the tile
     f32x16 s[2] = {f32x16{}, f32x16{}};
+    mfma_priority_high();
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
@@ -164,6 +165,7 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void fwd_prefill_kernel(FwdAr
         s[kb] = mfma32(lds_row_chunk<D, T>(kt_lds, kb * 32 + c, 2 * t + hl), qf[t], s[kb]);
     }
     sched_mfma_pipeline<2 * NT, 1, 1, 3>();
+    mfma_priority_low();
 
     // mask (partial tiles only): key of slot r is kt*BN + 32kb + 8(r/4) + 4hl + r%4
     if (kt < kf_lo || kt >= kf_hi) {
@@ -213,6 +215,7 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void fwd_prefill_kernel(FwdAr
     l += psum;
 
     // O^T += V^T P^T over the 4 16-key chunks of the tile
+    mfma_priority_high();
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
 #pragma unroll
@@ -220,6 +223,7 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void fwd_prefill_kernel(FwdAr
         o[n] = mfma32(lds_col_operand<D, T>(vt_lds, 16 * t, 32 * n), pf[t], o[n]);
     }
     sched_mfma_pipeline<4 * NB, 1, 2, 2>();
+    mfma_priority_low();
 
     wait_vmem();        // the next tile has landed in LDS
     __syncthreads();

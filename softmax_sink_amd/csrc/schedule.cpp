@@ -292,9 +292,14 @@ sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
   // Only items some call can read are built. A paged table serves the
   // forward alone: no backward items, and in decode mode (the forward runs
   // the split-KV items) no per-query-tile items either. Other tables keep
-  // both, as the backward's dQ pass walks the per-query-tile items.
+  // both, as the backward's dQ pass walks the per-query-tile items. Split-KV
+  // items exist in decode mode only (a prefill table would otherwise carry
+  // them for nothing, and their partial-row count, query rows x q-heads x
+  // key chunks, would cap a single prefill sequence near 370k tokens at 32
+  // heads).
   const bool want_bwd = paged == nullptr;
   const bool want_fwd = want_bwd || mode == kModePrefill;
+  const bool want_dec = mode == kModeDecode;
   std::vector<Item> fwd, bwd, dec;
   std::vector<int32_t> dec_seq(2 * static_cast<size_t>(B), 0);
   std::vector<int> cls;
@@ -338,7 +343,7 @@ sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
     // split-KV items: the union of the rows' kept keys, rounded out to
     // kDecBN tiles, cut into kDecChunk-key pieces
     dec_seq[2 * b] = static_cast<int32_t>(dec.size());
-    if (lq > 0 && lk > 0) {
+    if (want_dec && lq > 0 && lk > 0) {
       int64_t jlo = kInf, jhi = -1;
       for (int64_t i = 0; i < lq; ++i) {
         const int64_t a = std::max<int64_t>(0, rb.lo(i));

@@ -57,6 +57,13 @@ def _check_against_oracle(cu_q, cu_k, causal, wl, wr, hq=4, hk=2):
     assert _items(meta, W_NFWD, W_FWDOFF) == O.forward_items(cu_q, cu_k, fbm, fbn, causal, wl, wr)
     assert _items(meta, W_NBWD, W_BWDOFF) == O.backward_items(cu_q, cu_k, bbm, bbn, causal, wl, wr)
     ditems, per_seq = O.decode_items(cu_q, cu_k, meta[W_DECBN], meta[W_DECCHUNK], causal, wl, wr)
+    if meta[W_MODE] == 0:
+        # prefill tables carry no split-KV items (the per-sequence table is
+        # all zeros); compare the oracle's split items in decode mode only
+        assert meta[W_NDEC] == 0 and meta[W_DECROWS] == 0
+        seq = meta[meta[W_DECSEQ]: meta[W_DECSEQ] + 2 * (len(cu_q) - 1)]
+        assert not seq.any()
+        return meta
     assert _items(meta, W_NDEC, W_DECOFF, 4) == ditems
     seq = meta[meta[W_DECSEQ]: meta[W_DECSEQ] + 2 * (len(cu_q) - 1)].reshape(-1, 2)
     assert [tuple(int(x) for x in r) for r in seq] == per_seq
@@ -85,6 +92,26 @@ def test_schedule_matches_oracle_random():
         cu_q = np.r_[0, np.cumsum(lq)].astype(np.int32)
         cu_k = np.r_[0, np.cumsum(lk)].astype(np.int32)
         _check_against_oracle(cu_q, cu_k, causal, wl, wr)
+
+
+def test_split_kv_schedule_matches_oracle_random():
+    """Decode-mode tables (query rows x GQA group <= 64): split-KV items,
+    per-sequence table and partial-row bases against the oracle."""
+    rng = np.random.default_rng(321)
+    n_decode = 0
+    for trial in range(60):
+        Bn = int(rng.integers(1, 7))
+        lq = rng.integers(0, 33, Bn)
+        lk = rng.integers(0, 5000, Bn)
+        lq[0] = max(1, lq[0]); lk[0] = max(1, lk[0])
+        causal = bool(rng.integers(0, 2))
+        wl = int(rng.choice([-1, 0, 1, 17, 64, 2100]))
+        wr = 0 if causal and rng.integers(0, 2) else (-1 if causal else int(rng.choice([-1, 0, 5, 100])))
+        cu_q = np.r_[0, np.cumsum(lq)].astype(np.int32)
+        cu_k = np.r_[0, np.cumsum(lk)].astype(np.int32)
+        m = _check_against_oracle(cu_q, cu_k, causal, wl, wr, hq=4, hk=2)
+        n_decode += int(m[W_MODE] == 1)
+    assert n_decode == 60
 
 
 def test_schedule_matches_oracle_on_workload_lengths():
@@ -518,3 +545,4 @@ def test_problem_fields_must_fit_int32():
         B.make_problem_padded(2, 8, 8, None, None, 4, 2, 128, False, 2 ** 40, -1)
     p = B.make_problem(cu, cu, 4, 2, 128, False, 2 ** 31 - 1, 2 ** 31 - 1)
     assert p.win_left == 2 ** 31 - 1 and p.win_right == 2 ** 31 - 1
+
