@@ -320,6 +320,37 @@ sink_attn_status sink_attn_bwd_padded(const sink_attn_problem* p,
                                       void* workspace, int64_t workspace_bytes,
                                       hipStream_t stream);
 
+/* Bytes of the device array behind sink_attn_bwd_noalloc (64 MiB). */
+#define SINK_ATTN_NOALLOC_SCRATCH_BYTES (64LL << 20)
+
+/* Backward that allocates nothing and takes no workspace, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. Arguments, results and
+ * errors as sink_attn_bwd (TND layout), without workspace and
+ * workspace_bytes. Its scratch (the row terms D and the dsink partials,
+ * bwd_workspace_bytes of the metadata: about 4 * num_heads_q * total_q
+ * bytes) lives in a static device array of SINK_ATTN_NOALLOC_SCRATCH_BYTES
+ * that the library holds on every GPU it runs on until the process ends;
+ * its address is looked up once per device, on the first call with that
+ * device current. The current device must be the one `stream` belongs to.
+ * Every call on a GPU shares that GPU's array: calls that overlap on one
+ * GPU (on two streams, or two host threads) race and give wrong results;
+ * calls ordered on one stream are safe. The kernels write every scratch
+ * word before reading it, so nothing is cleared between calls.
+ * Errors: as sink_attn_bwd; E_BUFFER_TOO_SMALL when the metadata's
+ * bwd_workspace_bytes exceed SINK_ATTN_NOALLOC_SCRATCH_BYTES; E_HIP when
+ * the array's address cannot be obtained. */
+sink_attn_status sink_attn_bwd_noalloc(const sink_attn_problem* p,
+                                       const int32_t* meta_host,
+                                       const int32_t* meta_dev,
+                                       const void* dout, const void* q, const void* k,
+                                       const void* v, const void* out, const float* lse,
+                                       const int32_t* cu_seqlens_q,
+                                       const int32_t* cu_seqlens_k,
+                                       const float* sink_logits, float scale,
+                                       void* dq, void* dk, void* dv, float* dsink,
+                                       hipStream_t stream);
+
 /* Context-parallel merge. "CANN ops-transformer: flash_attn", Note on
  * softmax_lse: ring attention combines partial results through their lse.
  * Each of num_parts partials is the attention of the same queries over a

@@ -98,6 +98,8 @@ def lib():
                                     vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp,
                                     ctypes.c_int64, vp]
         L.sink_attn_bwd.restype = ctypes.c_int
+        L.sink_attn_bwd_noalloc.argtypes = L.sink_attn_bwd.argtypes[:17] + [vp]
+        L.sink_attn_bwd_noalloc.restype = ctypes.c_int
         L.sink_attn_metadata_paged.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(PagedKV),
                                                i32p, i32p, i32p, i32p, ctypes.c_int64, i64p,
                                                i64p]
@@ -406,6 +408,23 @@ def sink_attn_bwd(problem, meta_host, meta_dev, dout, q, k, v, out, lse, cu_q, c
     if check and st != OK:
         raise SinkAttnError(st, "sink_attn_bwd")
     return st
+
+
+def sink_attn_bwd_noalloc(problem, meta_host, meta_dev, dout, q, k, v, out, lse, cu_q, cu_k,
+                          sinks, scale, dq, dk, dv, dsink, stream=None, check=True):
+    """sink_attn_bwd without a workspace: the library's static device
+    scratch array (SINK_ATTN_NOALLOC_SCRATCH_BYTES per GPU) holds it."""
+    st = lib().sink_attn_bwd_noalloc(ctypes.byref(problem), _i32p(meta_host), _ptr(meta_dev),
+                                     _ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                     _ptr(lse), _ptr(cu_q), _ptr(cu_k), _ptr(sinks),
+                                     float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsink),
+                                     _stream(stream))
+    if check and st != OK:
+        raise SinkAttnError(st, "sink_attn_bwd_noalloc")
+    return st
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def sink_attn_arm_timing(start, stop):

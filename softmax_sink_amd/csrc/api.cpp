@@ -1,14 +1,45 @@
 // C ABI of libsinkattn.so: argument checks, workspace carving and kernel
 // dispatch. Declarations and the contract are in include/sink_attn.h.
+#include <hip/hip_runtime.h>
+
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <vector>
 
 #include "sink_attn_internal.h"
 
 using namespace sinkattn;
 
+// Scratch of sink_attn_bwd_noalloc: one copy per GPU, held until the
+// process ends. Host code never passes this name to a kernel (on the host it
+// is only a stand-in for the symbol); it uses the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) char scratch[SINK_ATTN_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+// Device address of `scratch` per device id, looked up once per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 thread_local TimingHook g_timing;
 
@@ -359,6 +390,30 @@ sink_attn_status sink_attn_bwd(const sink_attn_problem* p,
   return bwd_impl(p, meta_host, meta_dev, dout, q, k, v, out, lse, cu_seqlens_q,
                   cu_seqlens_k, nullptr, nullptr, sink_logits, scale, dq, dk, dv, dsink,
                   workspace, workspace_bytes, stream);
+}
+
+sink_attn_status sink_attn_bwd_noalloc(const sink_attn_problem* p,
+                                       const int32_t* meta_host,
+                                       const int32_t* meta_dev, const void* dout,
+                                       const void* q, const void* k, const void* v,
+                                       const void* out, const float* lse,
+                                       const int32_t* cu_seqlens_q,
+                                       const int32_t* cu_seqlens_k,
+                                       const float* sink_logits, float scale, void* dq,
+                                       void* dk, void* dv, float* dsink,
+                                       hipStream_t stream) {
+  sink_attn_status st = common_checks(p, meta_host, meta_dev, scale);
+  if (st != SINK_ATTN_OK) return st;
+  st = check_family(p, meta_host, false, nullptr, nullptr);
+  if (st != SINK_ATTN_OK) return st;
+  if (!cu_seqlens_q || !cu_seqlens_k) return SINK_ATTN_E_INVALID;
+  if (header_i64(meta_host, kBwdWsLo, kBwdWsHi) > SINK_ATTN_NOALLOC_SCRATCH_BYTES)
+    return SINK_ATTN_E_BUFFER_TOO_SMALL;
+  void* ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return SINK_ATTN_E_HIP;
+  return bwd_impl(p, meta_host, meta_dev, dout, q, k, v, out, lse, cu_seqlens_q,
+                  cu_seqlens_k, nullptr, nullptr, sink_logits, scale, dq, dk, dv, dsink, ws,
+                  SINK_ATTN_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 sink_attn_status sink_attn_bwd_padded(const sink_attn_problem* p,

@@ -546,3 +546,17 @@ def test_problem_fields_must_fit_int32():
     p = B.make_problem(cu, cu, 4, 2, 128, False, 2 ** 31 - 1, 2 ** 31 - 1)
     assert p.win_left == 2 ** 31 - 1 and p.win_right == 2 ** 31 - 1
 
+
+def test_noalloc_backward_rejects_problems_beyond_its_scratch(L):
+    """sink_attn_bwd_noalloc refuses a problem whose backward scratch exceeds
+    its static array (checked on the host before any device work; the
+    device pointers here are never touched)."""
+    tq = (B.NOALLOC_SCRATCH_BYTES // 4) // 32 + 64          # D alone overflows
+    cu = np.array([0, tq], np.int32)
+    p = B.make_problem(cu, cu, 32, 32, 128, True)
+    meta, fws, bws = B.sink_attn_metadata(p, cu, cu)
+    assert bws > B.NOALLOC_SCRATCH_BYTES
+    fake = 1 << 20                                            # 16-byte aligned, never read
+    st = B.sink_attn_bwd_noalloc(p, meta, fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                                 fake, 0.1, fake, fake, fake, fake, stream=0, check=False)
+    assert st == B.E_BUFFER_TOO_SMALL
