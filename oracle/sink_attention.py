@@ -437,12 +437,14 @@ def decode_items(cu_q, cu_k, tile_k, chunk_keys, causal, win_left, win_right):
     """Split-KV work for short query groups: for each sequence, the keys kept
     by at least one of its rows, rounded out to tile_k tiles and cut into
     chunks of chunk_keys keys (clipped to the sequence). Returns
-    (items, per_seq): items = (b, split, k_lo, k_hi) in (b, split) order;
-    per_seq[b] = (first item index, number of splits)."""
-    items, per_seq = [], []
+    (items, per_seq): items = (b, split, k_lo, k_hi), the sequences ordered
+    by their total chunk keys (descending, ties: lower b first), each
+    sequence's chunks together in split order; per_seq[b] = (first item
+    index, number of splits)."""
+    by_seq = []
     for b in range(len(cu_q) - 1):
         Lq, Lk = int(cu_q[b + 1] - cu_q[b]), int(cu_k[b + 1] - cu_k[b])
-        first = len(items)
+        mine = []
         if Lq > 0 and Lk > 0:
             cols = keep_mask(Lq, Lk, causal, win_left, win_right).any(axis=0)
             lo, hi = _span(cols)
@@ -451,9 +453,15 @@ def decode_items(cu_q, cu_k, tile_k, chunk_keys, causal, win_left, win_right):
                 stop = min(Lk, -(-hi // tile_k) * tile_k)
                 split = 0
                 for a in range(start, stop, chunk_keys):
-                    items.append((b, split, a, min(stop, a + chunk_keys)))
+                    mine.append((b, split, a, min(stop, a + chunk_keys)))
                     split += 1
-        per_seq.append((first, len(items) - first))
+        by_seq.append(mine)
+    order = sorted(range(len(by_seq)),
+                   key=lambda b: (-sum(it[3] - it[2] for it in by_seq[b]), b))
+    items, per_seq = [], [None] * len(by_seq)
+    for b in order:
+        per_seq[b] = (len(items), len(by_seq[b]))
+        items.extend(by_seq[b])
     return items, per_seq
 
 

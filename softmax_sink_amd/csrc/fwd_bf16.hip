@@ -308,6 +308,17 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void fwd_split_kernel(FwdArgs
   int jlo, jhi;
   row_key_range(i, lq, lk, a.causal, a.win_left, a.win_right, jlo, jhi);
   if (!live_row) jhi = -1;
+  // Keys every live row of this wave keeps (rows past the group do not
+  // count: nothing of theirs is written). A tile inside [wlo, whi] needs no
+  // mask; at decode shapes that is every tile but the ones at a sequence's
+  // end, window or chunk edge.
+  int wlo = live_row ? jlo : INT32_MIN;
+  int whi = live_row ? min(jhi, k_hi - 1) : INT32_MAX;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    wlo = max(wlo, __shfl_xor(wlo, o));
+    whi = min(whi, __shfl_xor(whi, o));
+  }
 
   const float c2 = a.scale * kLog2e;
   float m = kNegInf, l = 0.f;
@@ -358,10 +369,13 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void fwd_split_kernel(FwdArgs
       vec8<T> kf = lds_row_chunk<D, T>(kt_lds, kh * 32 + c, 2 * t + hl);
       s = mfma32(kf, qf[t], s);
     }
+    const int tlo = base + kh * 32;              // this wave's 32 keys of the tile
+    if (tlo < wlo || tlo + 31 > whi) {
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int j = base + kh * 32 + 8 * (rr >> 2) + 4 * hl + (rr & 3);
-      if (j < jlo || j > jhi || j >= k_hi) s[rr] = kNegInf;
+      for (int rr = 0; rr < 16; ++rr) {
+        const int j = tlo + 8 * (rr >> 2) + 4 * hl + (rr & 3);
+        if (j < jlo || j > jhi || j >= k_hi) s[rr] = kNegInf;
+      }
     }
     float mx = kNegInf;
 #pragma unroll

@@ -113,6 +113,37 @@ void sort_items(std::vector<Item>& v, int batch) {
   v.swap(out);
 }
 
+// Split-KV items in dispatch order: sequences by their total chunk keys
+// (descending, ties by b), each sequence's chunks contiguous and in split
+// order (the combine finds chunk s of sequence b at item first(b) + s), so
+// that the short sequences' chunks fill the end of the grid; the partial
+// rows are numbered in this order.
+void order_decode(std::vector<Item>& dec, std::vector<int32_t>& dec_seq, int batch,
+                  const int32_t* cu_q, int hq) {
+  std::vector<int64_t> work(static_cast<size_t>(batch), 0);
+  for (const Item& it : dec) work[it.w[0]] += it.w[3] - it.w[2];
+  std::vector<int> order(static_cast<size_t>(batch));
+  for (int b = 0; b < batch; ++b) order[b] = b;
+  std::sort(order.begin(), order.end(), [&](int x, int y) {
+    return work[x] != work[y] ? work[x] > work[y] : x < y;
+  });
+  std::vector<Item> out;
+  out.reserve(dec.size());
+  int64_t rows = 0;
+  for (int b : order) {
+    const int32_t first = dec_seq[2 * b], n = dec_seq[2 * b + 1];
+    dec_seq[2 * b] = static_cast<int32_t>(out.size());
+    const int64_t lq = cu_q[b + 1] - cu_q[b];
+    for (int32_t s = 0; s < n; ++s) {
+      Item it = dec[first + s];
+      it.w[4] = static_cast<int32_t>(rows);
+      rows += lq * hq;
+      out.push_back(it);
+    }
+  }
+  dec.swap(out);
+}
+
 uint32_t fnv1a(const int32_t* a, int64_t n, uint32_t h) {
   const unsigned char* p = reinterpret_cast<const unsigned char*>(a);
   for (int64_t i = 0; i < n * 4; ++i) { h ^= p[i]; h *= 16777619u; }
@@ -370,6 +401,7 @@ sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
   }
   sort_items(fwd, B);
   sort_items(bwd, B);
+  order_decode(dec, dec_seq, B, cu_q, p.num_heads_q);
 
   const int64_t pre_blocks = (p.total_q + kPreRows - 1) / kPreRows;
   const FwdWorkspace fw = fwd_workspace_layout(dec_rows, p.head_dim, p.dtype, mode);
