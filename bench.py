@@ -327,7 +327,10 @@ def run_workload(name, steps, warmup, progress=True):
             B.sink_attn_metadata_padded(problem, None, None, out=mh)
         else:
             B.sink_attn_metadata(problem, cq, ck, out=mh)
-        meta_dev[slot].copy_(meta_host[slot], non_blocking=True)
+        # the table goes to the device with the library's upload kernel on
+        # the stream (no DMA-engine copy, and no cross-engine wait, before
+        # the attention kernels)
+        B.sink_attn_upload_table(meta_host[slot], meta_dev[slot], len(mh))
         ev = torch.cuda.Event()
         ev.record()
         copied[slot] = ev

@@ -378,6 +378,23 @@ sink_attn_status sink_attn_merge(int32_t num_parts, int32_t total_q,
                                  const float* sink_logits, void* out,
                                  float* lse, hipStream_t stream);
 
+/* Copies `words` int32 of a metadata table from pinned host memory to device
+ * memory with a kernel on `stream` (the GPU reads the pinned pages
+ * directly), instead of a copy on a DMA engine. The kernels that read the
+ * table next in the same stream then depend only on an earlier kernel of
+ * their own queue; a DMA-engine copy between two attention calls costs a
+ * cross-engine wait of tens of microseconds, which at decode shapes (one
+ * call every millisecond) is several percent of the step. The two-phase
+ * metadata model of "CANN ops-transformer: flash_attn" (Function section)
+ * leaves this upload to the caller; this is one way to do it.
+ * host: allocated with hipHostMalloc (torch's pin_memory()); it is read when
+ * the kernel runs, so it must not change before that (stream order).
+ * dev: device memory of at least `words` int32, not overlapping host.
+ * Errors: E_INVALID (NULL pointers, words < 0, host not pinned host memory,
+ * dev not device memory), E_HIP. words = 0 enqueues nothing. */
+sink_attn_status sink_attn_upload_table(const int32_t* host, int32_t* dev, int64_t words,
+                                        hipStream_t stream);
+
 /* Measurement aid: the next sink_attn_fwd or sink_attn_bwd made on this host
  * thread records `start` just before and `stop` just after its main kernel
  * (forward: the attention tile loop, or the split-KV kernel for short query

@@ -117,6 +117,8 @@ def lib():
         L.sink_attn_bwd_padded.restype = ctypes.c_int
         L.sink_attn_merge.argtypes = [ctypes.c_int32] * 6 + [vp, vp, vp, vp, vp, vp]
         L.sink_attn_merge.restype = ctypes.c_int
+        L.sink_attn_upload_table.argtypes = [vp, vp, ctypes.c_int64, vp]
+        L.sink_attn_upload_table.restype = ctypes.c_int
         L.sink_attn_arm_timing.argtypes = [vp, vp]
         L.sink_attn_arm_timing.restype = ctypes.c_int
         L.sink_attn_status_string.argtypes = [ctypes.c_int]
@@ -425,6 +427,23 @@ def sink_attn_bwd_noalloc(problem, meta_host, meta_dev, dout, q, k, v, out, lse,
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def sink_attn_upload_table(host, dev, words=None, stream=None):
+    """Copy an int32 table from a pinned host tensor to a device tensor with
+    a kernel on the stream (see include/sink_attn.h)."""
+    import torch
+    if host.device.type != "cpu" or not host.is_pinned() or host.dtype != torch.int32:
+        raise ValueError("host must be a pinned int32 CPU tensor")
+    if not host.is_contiguous():
+        raise ValueError("host must be contiguous")
+    n = host.numel() if words is None else int(words)
+    _expect(dev, "dev", tuple(dev.shape), torch.int32)
+    if n > min(host.numel(), dev.numel()):
+        raise ValueError(f"{n} words do not fit host ({host.numel()}) or dev ({dev.numel()})")
+    st = lib().sink_attn_upload_table(host.data_ptr(), _ptr(dev), n, _stream(stream))
+    if st != OK:
+        raise SinkAttnError(st, "sink_attn_upload_table")
 
 
 def sink_attn_arm_timing(start, stop):

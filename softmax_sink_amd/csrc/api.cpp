@@ -69,6 +69,19 @@ sink_attn_status common_checks(const sink_attn_problem* p,
   return check_header(*p, meta_host, kv);
 }
 
+// Table upload: each thread moves 16 bytes (or 4 in the ragged tail) from
+// the pinned host table, read by the GPU through its device address.
+__global__ __launch_bounds__(256) void upload_table_kernel(const int32_t* __restrict__ src,
+                                                           int32_t* __restrict__ dst,
+                                                           int64_t words) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i + 4 <= words) {
+    *reinterpret_cast<int4*>(dst + i) = *reinterpret_cast<const int4*>(src + i);
+  } else {
+    for (int64_t j = i; j < words; ++j) dst[j] = src[j];
+  }
+}
+
 // Window bound handed to the kernels. A window of max_seqlen_q +
 // max_seqlen_k or more never excludes a key (the bottom-right aligned row
 // position lies in [-max_seqlen_q, max_seqlen_k)), so it is passed on as
@@ -463,6 +476,35 @@ sink_attn_status sink_attn_merge(int32_t num_parts, int32_t total_q,
   const TimingHook t = take_timing();
   const hipError_t e = launch_merge(a, head_dim, part_dtype, out_dtype, stream, t);
   return e == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_E_HIP;
+}
+
+sink_attn_status sink_attn_upload_table(const int32_t* host, int32_t* dev, int64_t words,
+                                        hipStream_t stream) {
+  if (!host || !dev || words < 0) return SINK_ATTN_E_INVALID;
+  if (words == 0) return SINK_ATTN_OK;
+  // 16-byte moves need both ends 16-byte aligned (pinned and device
+  // allocations are)
+  if (!aligned16(host) || !aligned16(dev)) return SINK_ATTN_E_INVALID;
+  hipPointerAttribute_t ha{}, da{};
+  if (hipPointerGetAttributes(&ha, host) != hipSuccess || ha.type != hipMemoryTypeHost ||
+      !ha.devicePointer) {
+    (void)hipGetLastError();                    // clear a lookup failure
+    return SINK_ATTN_E_INVALID;
+  }
+  if (hipPointerGetAttributes(&da, dev) != hipSuccess || da.type != hipMemoryTypeDevice) {
+    (void)hipGetLastError();
+    return SINK_ATTN_E_INVALID;
+  }
+  const char* h0 = reinterpret_cast<const char*>(host);
+  const char* d0 = reinterpret_cast<const char*>(dev);
+  const int64_t bytes = words * 4;
+  if (h0 < d0 + bytes && d0 < h0 + bytes) return SINK_ATTN_E_INVALID;
+  const int64_t threads = (words + 3) / 4;
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > INT32_MAX) return SINK_ATTN_E_INVALID;
+  hipLaunchKernelGGL(upload_table_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                     stream, static_cast<const int32_t*>(ha.devicePointer), dev, words);
+  return hipGetLastError() == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_E_HIP;
 }
 
 sink_attn_status sink_attn_arm_timing(hipEvent_t start, hipEvent_t stop) {

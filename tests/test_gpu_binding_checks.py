@@ -102,3 +102,28 @@ def test_plan_does_not_wait_for_queued_work():
     assert np.array_equal(plan.meta_dev.cpu().numpy(), plan.meta)
     assert np.array_equal(plan.cu_q.cpu().numpy(), p.cu_q)
     del b
+
+
+def test_upload_table_kernel_copies_and_refuses_pageable_memory():
+    """sink_attn_upload_table moves an int32 table from pinned host memory to
+    the device with a kernel: every word arrives (lengths with a ragged tail
+    and a 16-byte-multiple), and a pageable host buffer is refused on the
+    host before anything is enqueued."""
+    import ctypes
+    import numpy as np
+    import torch
+    from softmax_sink_amd import binding as B
+    rng = np.random.default_rng(5)
+    for n in (1, 3, 4, 1001, 71344):
+        host = torch.from_numpy(rng.integers(-2**31, 2**31 - 1, n, dtype=np.int64).astype(np.int32)).pin_memory()
+        dev = torch.full((n + 5,), -7, dtype=torch.int32, device="cuda")
+        B.sink_attn_upload_table(host, dev, n)
+        torch.cuda.synchronize()
+        assert torch.equal(dev[:n].cpu(), host) and (dev[n:] == -7).all()
+    pageable = np.zeros(64, np.int32)
+    dev = torch.zeros(64, dtype=torch.int32, device="cuda")
+    st = B.lib().sink_attn_upload_table(pageable.ctypes.data, dev.data_ptr(), 64,
+                                        torch.cuda.current_stream().cuda_stream)
+    assert st == B.E_INVALID
+    with pytest.raises(ValueError):
+        B.sink_attn_upload_table(torch.zeros(8, dtype=torch.int32), dev, 8)
