@@ -34,11 +34,13 @@ namespace {
 using namespace dev;
 
 
-// Block-table entries a kernel keeps in LDS: those of one 2048-key span
-// (kDecChunk keys; block size >= 16).
-constexpr int kMaxItemPages = 132;
-static_assert(kMaxItemPages >= 1 + (kDecChunk + 14) / 16, "page list too short");
-constexpr int kPageSpan = kDecChunk;
+// Block-table entries a kernel keeps in LDS: those of one split-KV chunk
+// (kDecChunk keys) or of one kPageSpan-key span of the tiled forward, at the
+// smallest block size (16).
+constexpr int kPageSpan = 2048;
+constexpr int kMaxItemPages = 260;
+static_assert(kMaxItemPages >= 1 + (kDecChunk + 14) / 16 && kMaxItemPages >= 1 + (kPageSpan + 14) / 16,
+              "page list too short");
 
 // PAGED: keys and values come from paged caches through the block table
 // (only the tile addresses change). The block-table entries of the current
@@ -275,8 +277,8 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void fwd_split_kernel(FwdArgs
   __shared__ __attribute__((aligned(16))) char lds1[2 * TILE];
   __shared__ int pages[PAGED ? kMaxItemPages : 1];
 
-  const int item = blockIdx.x / a.hk;
-  const int hk = blockIdx.x % a.hk;
+  int item, hk;
+  chunk_work(blockIdx.x, a.n_items, a.hk, item, hk);
   const int* it = a.items + item * kItemWords;
   const int b = it[0], k_lo = it[2], k_hi = it[3], row_base = it[4];
   const int q0 = q_start(a, b), lq = q_len(a, b);

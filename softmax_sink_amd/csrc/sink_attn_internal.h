@@ -44,7 +44,7 @@ constexpr int kBwdBM = 64;     // query rows per backward tile step (D <= 128)
 constexpr int bwd_tile_rows(int head_dim) { return head_dim > 128 ? 32 : kBwdBM; }
 constexpr int kBwdBN = 128;    // keys per backward work item (2 halves of 64)
 constexpr int kDecBN = 64;     // keys per split-KV tile step
-constexpr int kDecChunk = 2048;// keys per split-KV work item
+constexpr int kDecChunk = 4096;// keys per split-KV work item
 constexpr int kDecMaxRows = 64;// (query rows x GQA group) handled per split item
 constexpr int kPreRows = 64;   // tokens per block of the backward preprocess
 constexpr int kMaxMergeParts = 4096;  // partials one context-parallel merge accepts

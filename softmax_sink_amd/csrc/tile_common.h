@@ -226,5 +226,25 @@ __device__ __forceinline__ int head_of_slot(int j, int hq) {
   return j;
 }
 
+// Work item and kv-head of split-KV block `id` (grid n_items x nh). The nh
+// kv-heads of one key chunk read disjoint 2*D-byte pieces of the same K and
+// V rows; they go to the same XCD (block id mod 8), one after the other, so
+// that the whole rows are fetched close together in time. Items come in
+// groups of 8, one item of each group per XCD; items past the last whole
+// group take the plain order. Measured on the decode stream (8 kv-heads,
+// 256-byte pieces of 2 KB rows): 6.05 TB/s against 5.70 TB/s for a grid
+// with the heads of a chunk on 8 different XCDs.
+__device__ __forceinline__ void chunk_work(int id, int n_items, int nh, int& item, int& h) {
+  const int full = (n_items >> 3) * 8 * nh;      // blocks of the whole groups
+  if (id < full) {
+    const int x = id & 7, u = id >> 3;
+    h = u % nh;
+    item = (u / nh) * 8 + x;
+    return;
+  }
+  item = id / nh;
+  h = id % nh;
+}
+
 }  // namespace dev
 }  // namespace sinkattn

@@ -142,11 +142,15 @@ def test_bf16_decode_group_at_split_limit():
 
 @pytest.mark.parametrize("D", [128, 64])
 def test_bf16_decode_split_kv(D):
-    # short query groups: split-KV kernel + combine (chunk boundaries crossed)
-    p = W.make_problem(50 + D, [1, 5, 16, 3], [700, 2600, 4500, 2049], 32, 8, D, causal=True,
-                       sinks=np.float32(math.log(0.5)), name=f"decode_d{D}")
+    # short query groups: split-KV kernel + combine. Chunk boundaries are
+    # crossed, and the 19 work items make two whole groups of 8 (all
+    # kv-heads of a chunk on one XCD) and a remainder of 3 (plain order).
+    p = W.make_problem(50 + D, [1, 5, 16, 3, 7, 2, 11, 1, 4, 9],
+                       [700, 9000, 4500, 2049, 8193, 300, 12000, 4097, 5000, 1], 32, 8, D,
+                       causal=True, sinks=np.float32(math.log(0.5)), name=f"decode_d{D}")
     g = _check(p)
     assert g.plan.mode == 1
+    assert int(g.plan.meta[25]) == 19       # header word 25: split-KV item count
 
 
 def test_bf16_decode_window_and_no_sink():
