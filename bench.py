@@ -329,8 +329,10 @@ def run_workload(name, steps, warmup, progress=True):
             B.sink_attn_metadata(problem, cq, ck, out=mh)
         # the table goes to the device with the library's upload kernel on
         # the stream (no DMA-engine copy, and no cross-engine wait, before
-        # the attention kernels)
-        B.sink_attn_upload_table(meta_host[slot], meta_dev[slot], len(mh))
+        # the attention kernels); a forward-only step copies just the prefix
+        # the forward reads
+        words = len(mh) if train else B.forward_table_words(mh)
+        B.sink_attn_upload_table(meta_host[slot], meta_dev[slot], words)
         ev = torch.cuda.Event()
         ev.record()
         copied[slot] = ev

@@ -90,7 +90,11 @@
 extern "C" {
 #endif
 
-#define SINK_ATTN_ABI_VERSION 4
+#define SINK_ATTN_ABI_VERSION 5
+
+/* Index of the metadata header word that holds the length (in words) of the
+ * table prefix the forward calls read. */
+#define SINK_ATTN_META_FWD_WORDS 47
 
 typedef enum {
   SINK_ATTN_OK = 0,
@@ -147,7 +151,11 @@ typedef struct {
  * short query groups (max_seqlen_q * num_heads_q / num_heads_k <= 64:
  * decode mode, where the forward runs them; the backward's dQ pass always
  * walks the per-query-tile items). Masked-out tiles are never visited.
- * Copy the table unchanged to device memory (meta_dev) for fwd/bwd.
+ * Copy the table unchanged to device memory (meta_dev) for fwd/bwd. The
+ * forward calls read only the first meta_host[SINK_ATTN_META_FWD_WORDS]
+ * words of meta_dev (the header and the items the forward walks), so a
+ * caller that runs no backward with the table may copy just that prefix;
+ * the backward reads the whole table.
  * Errors: E_INVALID (problem or cu_seqlens checks above, NULL pointers, a
  * padded layout), E_UNSUPPORTED, E_BUFFER_TOO_SMALL (meta_capacity_words <
  * *meta_words; the sizes are still written). */

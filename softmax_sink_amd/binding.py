@@ -429,6 +429,15 @@ def sink_attn_bwd_noalloc(problem, meta_host, meta_dev, dout, q, k, v, out, lse,
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
+META_FWD_WORDS = 47     # header word: length of the table prefix the forward reads
+
+
+def forward_table_words(meta):
+    """Words at the start of a metadata table that the forward calls read
+    (a forward-only caller may copy just these to the device)."""
+    return int(meta[META_FWD_WORDS])
+
+
 def sink_attn_upload_table(host, dev, words=None, stream=None):
     """Copy an int32 table from a pinned host tensor to a device tensor with
     a kernel on the stream (see include/sink_attn.h)."""

@@ -407,11 +407,12 @@ sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
   const FwdWorkspace fw = fwd_workspace_layout(dec_rows, p.head_dim, p.dtype, mode);
   const BwdWorkspace bw = bwd_workspace_layout(p.total_q, p.num_heads_q,
                                                p.head_dim, p.dtype, pre_blocks);
-  const int64_t fwd_off = kHeaderWords;
-  const int64_t bwd_off = fwd_off + static_cast<int64_t>(fwd.size()) * kItemWords;
-  const int64_t dec_off = bwd_off + static_cast<int64_t>(bwd.size()) * kItemWords;
+  const int64_t dec_off = kHeaderWords;
   const int64_t seq_off = dec_off + static_cast<int64_t>(dec.size()) * kItemWords;
-  const int64_t total = seq_off + 2 * static_cast<int64_t>(B);
+  const int64_t fwd_off = seq_off + 2 * static_cast<int64_t>(B);
+  const int64_t bwd_off = fwd_off + static_cast<int64_t>(fwd.size()) * kItemWords;
+  const int64_t total = bwd_off + static_cast<int64_t>(bwd.size()) * kItemWords;
+  const int64_t fwd_words = mode == kModeDecode ? fwd_off : bwd_off;
   if (total >= std::numeric_limits<int32_t>::max() ||
       dec_rows >= std::numeric_limits<int32_t>::max())
     return SINK_ATTN_E_UNSUPPORTED;
@@ -459,6 +460,7 @@ sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
   h[kCuHash] = static_cast<int32_t>(
       fnv1a(cu_k, B + 1, fnv1a(cu_q, B + 1, 2166136261u)));
   h[kMetaWords] = static_cast<int32_t>(total);
+  h[kFwdWords] = static_cast<int32_t>(fwd_words);
   h[kBwdPreBlocks] = static_cast<int32_t>(pre_blocks);
   h[kLayoutQ] = p.layout_q;
   h[kLayoutOut] = p.layout_out;
@@ -480,11 +482,12 @@ sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
     h[kPageLayout] = paged->kv.layout;
     h[kPageHash] = static_cast<int32_t>(hash);
   }
-  int32_t* w = out + fwd_off;
-  for (const Item& it : fwd) { std::memcpy(w, it.w, sizeof(it.w)); w += kItemWords; }
-  for (const Item& it : bwd) { std::memcpy(w, it.w, sizeof(it.w)); w += kItemWords; }
+  int32_t* w = out + dec_off;
   for (const Item& it : dec) { std::memcpy(w, it.w, sizeof(it.w)); w += kItemWords; }
   std::memcpy(w, dec_seq.data(), sizeof(int32_t) * dec_seq.size());
+  w += dec_seq.size();
+  for (const Item& it : fwd) { std::memcpy(w, it.w, sizeof(it.w)); w += kItemWords; }
+  for (const Item& it : bwd) { std::memcpy(w, it.w, sizeof(it.w)); w += kItemWords; }
   return SINK_ATTN_OK;
 }
 
@@ -505,6 +508,7 @@ sink_attn_status check_header(const sink_attn_problem& p, const int32_t* h,
   if (h[kWordFwdBM] != kFwdBM || h[kWordFwdBN] != kFwdBN || h[kWordBwdBM] != bwd_tile_rows(p.head_dim) ||
       h[kWordBwdBN] != kBwdBN || h[kWordDecBN] != kDecBN || h[kWordDecChunk] != kDecChunk)
     return SINK_ATTN_E_META_MISMATCH;
+  if (h[kFwdWords] < kHeaderWords || h[kFwdWords] > h[kMetaWords]) return SINK_ATTN_E_META_MISMATCH;
   if (h[kPaged] != (kv ? 1 : 0)) return SINK_ATTN_E_META_MISMATCH;
   if (kv && (h[kPageSize] != kv->block_size || h[kPageMaxBlocks] != kv->max_blocks_per_seq ||
              h[kPageNumBlocks] != kv->num_blocks || h[kPageLayout] != kv->layout))

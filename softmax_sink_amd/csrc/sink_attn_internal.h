@@ -21,12 +21,18 @@ enum MetaWord : int {
   kBwdPreBlocks,
   kPaged, kPageSize, kPageMaxBlocks, kPageNumBlocks, kPageHash,
   kLayoutQ, kLayoutOut, kSeqQ, kSeqK, kUsedMask, kPageLayout,
+  kFwdWords,           // the forward reads words [0, kFwdWords) of the table
   kHeaderWords = 48
 };
+static_assert(kFwdWords == SINK_ATTN_META_FWD_WORDS, "header word of the forward prefix");
 
 constexpr int32_t kMagicValue = 0x4B4E4953;  // "SINK" little-endian
 constexpr int kItemWords = 8;
 
+// Table order: header, decode items, decode per-sequence table, forward
+// items, backward items. The forward reads the header and, in decode mode,
+// the decode items and per-sequence table, else the forward items: a
+// prefix of the table.
 // Forward item:  b, qt, kt_lo, kt_hi, kf_lo, kf_hi, 0, 0
 // Backward item: b, kt, qt_lo, qt_hi, qf_lo, qf_hi, 0, 0
 // Decode item:   b, split, k_lo, k_hi, row_base, 0, 0, 0

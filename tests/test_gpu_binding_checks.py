@@ -127,3 +127,34 @@ def test_upload_table_kernel_copies_and_refuses_pageable_memory():
     assert st == B.E_INVALID
     with pytest.raises(ValueError):
         B.sink_attn_upload_table(torch.zeros(8, dtype=torch.int32), dev, 8)
+
+
+@pytest.mark.parametrize("lens_q", [[1, 7, 16, 3], [130, 7, 300, 64]])
+def test_forward_reads_only_the_table_prefix(lens_q):
+    """The forward calls read the first meta[META_FWD_WORDS] words of the
+    device table: with only that prefix copied (the rest of the device buffer
+    zero), the forward gives the same bits as with the whole table, in decode
+    mode (split-KV items) and in prefill mode (per-query-tile items)."""
+    hq, hk, D = 16, 4, 128
+    p = W.make_problem(61, lens_q, [5000, 300, 9000, 700], hq, hk, D, causal=True,
+                       name="prefix")
+    prob = B.make_problem(p.cu_q, p.cu_k, hq, hk, D, True)
+    meta, fws, _ = B.sink_attn_metadata(prob, p.cu_q, p.cu_k)
+    pre = B.forward_table_words(meta)
+    decode = max(lens_q) * (hq // hk) <= 64
+    assert int(meta[14]) == (1 if decode else 0) and 48 < pre < len(meta)
+    log(f"case prefix: lens_q={lens_q} mode={int(meta[14])} prefix {pre} of {len(meta)} words")
+    full = torch.from_numpy(meta).cuda()
+    part = torch.zeros_like(full)
+    part[:pre] = full[:pre]
+    q, k, v, s = to_dev(p, "q"), to_dev(p, "k"), to_dev(p, "v"), dev_sinks(p)
+    cq, ck = torch.from_numpy(p.cu_q).cuda(), torch.from_numpy(p.cu_k).cuda()
+    res = []
+    for m in (full, part):
+        out = torch.empty_like(q)
+        lse = torch.empty(hq, p.total_q, dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(fws, 1), dtype=torch.uint8, device="cuda")
+        B.sink_attn_fwd(prob, meta, m, q, k, v, cq, ck, s, float(p.scale), out, lse, ws, fws)
+        torch.cuda.synchronize()
+        res.append((out.view(torch.int16).cpu(), lse.view(torch.int32).cpu()))
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])

@@ -34,7 +34,8 @@ def test_exports_every_declared_symbol(L):
             "sink_attn_arm_timing"} <= names
     for n in names:
         assert hasattr(L, n), n
-    assert B.abi_version() == 4
+    version = re.search(r"#define SINK_ATTN_ABI_VERSION (\d+)", text).group(1)
+    assert B.abi_version() == int(version)
     for s in range(6):
         assert isinstance(B.status_string(s), str)
 
@@ -57,6 +58,16 @@ def _check_against_oracle(cu_q, cu_k, causal, wl, wr, hq=4, hk=2):
     assert _items(meta, W_NFWD, W_FWDOFF) == O.forward_items(cu_q, cu_k, fbm, fbn, causal, wl, wr)
     assert _items(meta, W_NBWD, W_BWDOFF) == O.backward_items(cu_q, cu_k, bbm, bbn, causal, wl, wr)
     ditems, per_seq = O.decode_items(cu_q, cu_k, meta[W_DECBN], meta[W_DECCHUNK], causal, wl, wr)
+    # the forward's regions lie in the prefix it reads (header word 47):
+    # the split-KV items and per-sequence table in decode mode, else the
+    # per-query-tile items; the backward's items lie past it
+    pre, nb = int(meta[B.META_FWD_WORDS]), len(cu_q) - 1
+    if meta[W_MODE] == 1:
+        assert meta[W_DECOFF] + 8 * meta[W_NDEC] <= pre and meta[W_DECSEQ] + 2 * nb <= pre
+        assert meta[W_FWDOFF] >= pre
+    else:
+        assert meta[W_FWDOFF] + 8 * meta[W_NFWD] <= pre
+    assert meta[W_BWDOFF] >= pre and pre <= len(meta)
     if meta[W_MODE] == 0:
         # prefill tables carry no split-KV items (the per-sequence table is
         # all zeros); compare the oracle's split items in decode mode only
@@ -141,7 +152,7 @@ def test_metadata_two_call_protocol_and_sizes(L):
                               ctypes.byref(words), ctypes.byref(fws), ctypes.byref(bws))
     assert st == B.E_BUFFER_TOO_SMALL
     meta, f, b = B.sink_attn_metadata(p, cu, cu)
-    assert meta[0] == 0x4B4E4953 and meta[1] == 4 and len(meta) == words.value
+    assert meta[0] == 0x4B4E4953 and meta[1] == B.abi_version() and len(meta) == words.value
     # bwd workspace: D [Hq,Tq] fp32 + per-block dsink partials (no dQ accumulator)
     assert 300 * 8 * 4 <= b < 300 * 8 * 4 + 4096
     assert f == 0       # prefill mode needs no forward scratch
