@@ -433,35 +433,42 @@ def backward_items(cu_q, cu_k, tile_q, tile_k, causal, win_left, win_right):
     return _dispatch_order(items)
 
 
-def decode_items(cu_q, cu_k, tile_k, chunk_keys, causal, win_left, win_right):
-    """Split-KV work for short query groups: for each sequence, the keys kept
-    by at least one of its rows, rounded out to tile_k tiles and cut into
-    chunks of chunk_keys keys (clipped to the sequence). Returns
-    (items, per_seq): items = (b, split, k_lo, k_hi), the sequences ordered
-    by their total chunk keys (descending, ties: lower b first), each
-    sequence's chunks together in split order; per_seq[b] = (first item
-    index, number of splits)."""
-    by_seq = []
+def decode_items(cu_q, cu_k, tile_k, chunk_keys, causal, win_left, win_right,
+                 tail_keys=None, tail_percent=0):
+    """Split-KV work for short query groups: for each sequence, the span of
+    keys kept by at least one of its rows, rounded out to tile_k tiles. The
+    sequences are ordered by span length (descending, ties: lower b first);
+    each span is cut into chunks of chunk_keys keys (clipped to the span),
+    except that the sequences whose preceding spans (in that order) already
+    make up at least (100 - tail_percent)% of the total span length are cut
+    into chunks of tail_keys keys. Returns (items, per_seq): items =
+    (b, split, k_lo, k_hi), each sequence's chunks together in key order;
+    per_seq[b] = (first item index, number of splits). The cutting and the
+    order are the scheduler's choices (they decide no value), written out
+    here so that its table can be compared item for item."""
+    spans = []
     for b in range(len(cu_q) - 1):
         Lq, Lk = int(cu_q[b + 1] - cu_q[b]), int(cu_k[b + 1] - cu_k[b])
-        mine = []
+        start = stop = 0
         if Lq > 0 and Lk > 0:
             cols = keep_mask(Lq, Lk, causal, win_left, win_right).any(axis=0)
             lo, hi = _span(cols)
             if hi > lo:
                 start = (lo // tile_k) * tile_k
                 stop = min(Lk, -(-hi // tile_k) * tile_k)
-                split = 0
-                for a in range(start, stop, chunk_keys):
-                    mine.append((b, split, a, min(stop, a + chunk_keys)))
-                    split += 1
-        by_seq.append(mine)
-    order = sorted(range(len(by_seq)),
-                   key=lambda b: (-sum(it[3] - it[2] for it in by_seq[b]), b))
-    items, per_seq = [], [None] * len(by_seq)
+        spans.append((start, stop))
+    order = sorted(range(len(spans)), key=lambda b: (-(spans[b][1] - spans[b][0]), b))
+    total = sum(stop - start for start, stop in spans)
+    items, per_seq, before = [], [None] * len(spans), 0
     for b in order:
-        per_seq[b] = (len(items), len(by_seq[b]))
-        items.extend(by_seq[b])
+        start, stop = spans[b]
+        step = chunk_keys
+        if tail_keys is not None and before * 100 >= (100 - tail_percent) * total:
+            step = tail_keys
+        before += stop - start
+        mine = [(b, s, a, min(stop, a + step)) for s, a in enumerate(range(start, stop, step))]
+        per_seq[b] = (len(items), len(mine))
+        items.extend(mine)
     return items, per_seq
 
 

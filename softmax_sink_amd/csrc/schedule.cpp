@@ -113,35 +113,75 @@ void sort_items(std::vector<Item>& v, int batch) {
   v.swap(out);
 }
 
-// Split-KV items in dispatch order: sequences by their total chunk keys
-// (descending, ties by b), each sequence's chunks contiguous and in split
-// order (the combine finds chunk s of sequence b at item first(b) + s), so
-// that the short sequences' chunks fill the end of the grid; the partial
-// rows are numbered in this order.
-void order_decode(std::vector<Item>& dec, std::vector<int32_t>& dec_seq, int batch,
-                  const int32_t* cu_q, int hq) {
-  std::vector<int64_t> work(static_cast<size_t>(batch), 0);
-  for (const Item& it : dec) work[it.w[0]] += it.w[3] - it.w[2];
+// Split-KV blocks (items x kv-heads) of the spans cut into `chunk`-key pieces.
+int64_t decode_blocks(const std::vector<int64_t>& span, int batch, int hk, int32_t chunk) {
+  int64_t blocks = 0;
+  for (int b = 0; b < batch; ++b) blocks += (span[2 * b + 1] - span[2 * b] + chunk - 1) / chunk * hk;
+  return blocks;
+}
+
+// Key chunk of the split-KV items: kDecChunk, halved (down to kDecMinChunk)
+// while the grid would have fewer than kDecMinBlocks blocks, so that short
+// batches still fill the chip.
+int32_t decode_chunk(const std::vector<int64_t>& span, int batch, int hk) {
+  int32_t chunk = kDecChunk;
+  for (;;) {
+    const int64_t blocks = decode_blocks(span, batch, hk, chunk);
+    if (blocks == 0 || blocks >= kDecMinBlocks || chunk / 2 < kDecMinChunk) return chunk;
+    chunk /= 2;
+  }
+}
+
+// Chunk of the sequences at the end of the grid: kDecTailChunk when the grid
+// takes at least two rounds of kDecMinBlocks blocks (short blocks at the end
+// then shorten the last round), else the chunk itself.
+int32_t decode_tail_chunk(const std::vector<int64_t>& span, int batch, int hk, int32_t chunk) {
+  return decode_blocks(span, batch, hk, chunk) >= 2 * kDecMinBlocks
+             ? std::min<int32_t>(chunk, kDecTailChunk) : chunk;
+}
+
+// Split-KV items in dispatch order: sequences by their span length
+// (descending, ties by b), each sequence's chunks contiguous and in key
+// order (the combine finds chunk s of sequence b at item first(b) + s).
+// Spans are cut into `chunk`-key pieces; the sequences that start in the
+// last kDecTailPercent of the total span length (in that order) are cut into
+// pieces of at most kDecTailChunk keys, so that the end of the grid is made
+// of short blocks. Partial rows are numbered in item order; returns their
+// count.
+int64_t decode_items(const std::vector<int64_t>& span, int32_t chunk, int32_t tail_chunk,
+                     int batch, const int32_t* cu_q, int hq, std::vector<Item>& dec,
+                     std::vector<int32_t>& dec_seq) {
   std::vector<int> order(static_cast<size_t>(batch));
-  for (int b = 0; b < batch; ++b) order[b] = b;
+  int64_t total = 0;
+  for (int b = 0; b < batch; ++b) {
+    order[b] = b;
+    total += span[2 * b + 1] - span[2 * b];
+  }
   std::sort(order.begin(), order.end(), [&](int x, int y) {
-    return work[x] != work[y] ? work[x] > work[y] : x < y;
+    const int64_t wx = span[2 * x + 1] - span[2 * x], wy = span[2 * y + 1] - span[2 * y];
+    return wx != wy ? wx > wy : x < y;
   });
-  std::vector<Item> out;
-  out.reserve(dec.size());
-  int64_t rows = 0;
+  int64_t rows = 0, before = 0;
   for (int b : order) {
-    const int32_t first = dec_seq[2 * b], n = dec_seq[2 * b + 1];
-    dec_seq[2 * b] = static_cast<int32_t>(out.size());
+    const int64_t start = span[2 * b], stop = span[2 * b + 1];
     const int64_t lq = cu_q[b + 1] - cu_q[b];
-    for (int32_t s = 0; s < n; ++s) {
-      Item it = dec[first + s];
+    const int64_t step = before * 100 >= (100 - kDecTailPercent) * total ? tail_chunk : chunk;
+    before += stop - start;
+    dec_seq[2 * b] = static_cast<int32_t>(dec.size());
+    int32_t split = 0;
+    for (int64_t a = start; a < stop; a += step) {
+      Item it{};
+      it.w[0] = b;
+      it.w[1] = split++;
+      it.w[2] = static_cast<int32_t>(a);
+      it.w[3] = static_cast<int32_t>(std::min<int64_t>(stop, a + step));
       it.w[4] = static_cast<int32_t>(rows);
       rows += lq * hq;
-      out.push_back(it);
+      dec.push_back(it);
     }
+    dec_seq[2 * b + 1] = split;
   }
-  dec.swap(out);
+  return rows;
 }
 
 uint32_t fnv1a(const int32_t* a, int64_t n, uint32_t h) {
@@ -333,6 +373,7 @@ sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
   const bool want_dec = mode == kModeDecode;
   std::vector<Item> fwd, bwd, dec;
   std::vector<int32_t> dec_seq(2 * static_cast<size_t>(B), 0);
+  std::vector<int64_t> dec_span(2 * static_cast<size_t>(B), 0);   // [start, stop) per sequence
   std::vector<int> cls;
   int64_t dec_rows = 0;
   for (int b = 0; b < B; ++b) {
@@ -371,9 +412,8 @@ sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
       spans(cls, it.w + 2);
       bwd.push_back(it);
     }
-    // split-KV items: the union of the rows' kept keys, rounded out to
-    // kDecBN tiles, cut into kDecChunk-key pieces
-    dec_seq[2 * b] = static_cast<int32_t>(dec.size());
+    // split-KV span: the union of the rows' kept keys, rounded out to
+    // kDecBN tiles
     if (want_dec && lq > 0 && lk > 0) {
       int64_t jlo = kInf, jhi = -1;
       for (int64_t i = 0; i < lq; ++i) {
@@ -382,26 +422,16 @@ sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
         if (a <= c) { jlo = std::min(jlo, a); jhi = std::max(jhi, c + 1); }
       }
       if (jhi > jlo) {
-        const int64_t start = (jlo / kDecBN) * kDecBN;
-        const int64_t stop = std::min<int64_t>(lk, (jhi + kDecBN - 1) / kDecBN * kDecBN);
-        int32_t split = 0;
-        for (int64_t a = start; a < stop; a += kDecChunk) {
-          Item it{};
-          it.w[0] = b;
-          it.w[1] = split++;
-          it.w[2] = static_cast<int32_t>(a);
-          it.w[3] = static_cast<int32_t>(std::min<int64_t>(stop, a + kDecChunk));
-          it.w[4] = static_cast<int32_t>(dec_rows);
-          dec_rows += lq * p.num_heads_q;
-          dec.push_back(it);
-        }
+        dec_span[2 * b] = (jlo / kDecBN) * kDecBN;
+        dec_span[2 * b + 1] = std::min<int64_t>(lk, (jhi + kDecBN - 1) / kDecBN * kDecBN);
       }
     }
-    dec_seq[2 * b + 1] = static_cast<int32_t>(dec.size()) - dec_seq[2 * b];
   }
   sort_items(fwd, B);
   sort_items(bwd, B);
-  order_decode(dec, dec_seq, B, cu_q, p.num_heads_q);
+  const int32_t dec_chunk = decode_chunk(dec_span, B, p.num_heads_k);
+  const int32_t dec_tail = decode_tail_chunk(dec_span, B, p.num_heads_k, dec_chunk);
+  dec_rows = decode_items(dec_span, dec_chunk, dec_tail, B, cu_q, p.num_heads_q, dec, dec_seq);
 
   const int64_t pre_blocks = (p.total_q + kPreRows - 1) / kPreRows;
   const FwdWorkspace fw = fwd_workspace_layout(dec_rows, p.head_dim, p.dtype, mode);
@@ -444,7 +474,9 @@ sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
   h[kWordBwdBM] = bwd_tile_rows(p.head_dim);
   h[kWordBwdBN] = kBwdBN;
   h[kWordDecBN] = kDecBN;
-  h[kWordDecChunk] = kDecChunk;
+  h[kWordDecChunk] = dec_chunk;
+  h[kWordDecTail] = dec_tail;
+  h[kWordDecTailPct] = kDecTailPercent;
   h[kNFwd] = static_cast<int32_t>(fwd.size());
   h[kFwdOff] = static_cast<int32_t>(fwd_off);
   h[kNBwd] = static_cast<int32_t>(bwd.size());
@@ -506,7 +538,9 @@ sink_attn_status check_header(const sink_attn_problem& p, const int32_t* h,
       h[kSeqQ] != p.seq_q || h[kSeqK] != p.seq_k)
     return SINK_ATTN_E_META_MISMATCH;
   if (h[kWordFwdBM] != kFwdBM || h[kWordFwdBN] != kFwdBN || h[kWordBwdBM] != bwd_tile_rows(p.head_dim) ||
-      h[kWordBwdBN] != kBwdBN || h[kWordDecBN] != kDecBN || h[kWordDecChunk] != kDecChunk)
+      h[kWordBwdBN] != kBwdBN || h[kWordDecBN] != kDecBN || h[kWordDecChunk] < kDecMinChunk ||
+      h[kWordDecChunk] > kDecChunk || h[kWordDecTail] < kDecMinChunk ||
+      h[kWordDecTail] > h[kWordDecChunk] || h[kWordDecTailPct] != kDecTailPercent)
     return SINK_ATTN_E_META_MISMATCH;
   if (h[kFwdWords] < kHeaderWords || h[kFwdWords] > h[kMetaWords]) return SINK_ATTN_E_META_MISMATCH;
   if (h[kPaged] != (kv ? 1 : 0)) return SINK_ATTN_E_META_MISMATCH;

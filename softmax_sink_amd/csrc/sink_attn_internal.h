@@ -22,7 +22,9 @@ enum MetaWord : int {
   kPaged, kPageSize, kPageMaxBlocks, kPageNumBlocks, kPageHash,
   kLayoutQ, kLayoutOut, kSeqQ, kSeqK, kUsedMask, kPageLayout,
   kFwdWords,           // the forward reads words [0, kFwdWords) of the table
-  kHeaderWords = 48
+  kWordDecTail,        // split-KV chunk of the sequences at the end of the grid
+  kWordDecTailPct,     // share (percent) of the span length cut into those
+  kHeaderWords = 56
 };
 static_assert(kFwdWords == SINK_ATTN_META_FWD_WORDS, "header word of the forward prefix");
 
@@ -50,7 +52,11 @@ constexpr int kBwdBM = 64;     // query rows per backward tile step (D <= 128)
 constexpr int bwd_tile_rows(int head_dim) { return head_dim > 128 ? 32 : kBwdBM; }
 constexpr int kBwdBN = 128;    // keys per backward work item (2 halves of 64)
 constexpr int kDecBN = 64;     // keys per split-KV tile step
-constexpr int kDecChunk = 4096;// keys per split-KV work item
+constexpr int kDecChunk = 4096;// keys per split-KV work item (at most)
+constexpr int kDecMinChunk = 512;      // shortest chunk, for grids too small to fill the chip
+constexpr int kDecMinBlocks = 512;     // split-KV blocks a grid should reach (one per slot)
+constexpr int kDecTailChunk = 1024;    // chunk of the sequences at the end of a long grid
+constexpr int kDecTailPercent = 10;    // share of the span length cut that way
 constexpr int kDecMaxRows = 64;// (query rows x GQA group) handled per split item
 constexpr int kPreRows = 64;   // tokens per block of the backward preprocess
 constexpr int kMaxMergeParts = 4096;  // partials one context-parallel merge accepts

@@ -268,6 +268,19 @@ DECODE_PAGE_ROWS = 16      # block size of the paged decode workload
 DECODE_PAGE_SEED = 55
 
 
+def _decode_draw():
+    rng = np.random.default_rng(5)
+    lq = rng.integers(1, 17, 64)
+    lk = rng.integers(512, 32769, 64)
+    return rng, lq, lk
+
+
+def decode_lengths():
+    """Query and key lengths of the decode workload (no tensors drawn)."""
+    _, lq, lk = _decode_draw()
+    return lq, lk
+
+
 def config(name):
     """The named workload with its fixed seed."""
     if name == "softmax1_fp32":
@@ -306,9 +319,7 @@ def config(name):
         p.meta["layout"] = "BNSD"
         return p
     if name in ("decode_softmax_n", "decode_paged"):
-        rng = np.random.default_rng(5)
-        lq = rng.integers(1, 17, 64)
-        lk = rng.integers(512, 32769, 64)
+        rng, lq, lk = _decode_draw()
         p = make_problem(5, lq, lk, 32, 8, 128, causal=True,
                          sinks=np.float32(math.log(0.5)), name=name,
                          rng=rng)

@@ -142,7 +142,7 @@ def test_forward_reads_only_the_table_prefix(lens_q):
     meta, fws, _ = B.sink_attn_metadata(prob, p.cu_q, p.cu_k)
     pre = B.forward_table_words(meta)
     decode = max(lens_q) * (hq // hk) <= 64
-    assert int(meta[14]) == (1 if decode else 0) and 48 < pre < len(meta)
+    assert int(meta[14]) == (1 if decode else 0) and 56 < pre < len(meta)
     log(f"case prefix: lens_q={lens_q} mode={int(meta[14])} prefix {pre} of {len(meta)} words")
     full = torch.from_numpy(meta).cuda()
     part = torch.zeros_like(full)

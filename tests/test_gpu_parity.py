@@ -142,15 +142,29 @@ def test_bf16_decode_group_at_split_limit():
 
 @pytest.mark.parametrize("D", [128, 64])
 def test_bf16_decode_split_kv(D):
-    # short query groups: split-KV kernel + combine. Chunk boundaries are
-    # crossed, and the 19 work items make two whole groups of 8 (all
-    # kv-heads of a chunk on one XCD) and a remainder of 3 (plain order).
+    # short query groups: split-KV kernel + combine. A small grid: the
+    # chunk shrinks to 512 keys (header word 20) so that the 97 items x 8
+    # kv-heads fill the chip; chunk boundaries are crossed, and the items
+    # make whole groups of 8 (all kv-heads of a chunk on one XCD) and a
+    # remainder of 1 (plain order).
     p = W.make_problem(50 + D, [1, 5, 16, 3, 7, 2, 11, 1, 4, 9],
-                       [700, 9000, 4500, 2049, 8193, 300, 12000, 4097, 5000, 1], 32, 8, D,
+                       [700, 9000, 4500, 2049, 8193, 300, 12000, 4097, 5000, 600], 32, 8, D,
                        causal=True, sinks=np.float32(math.log(0.5)), name=f"decode_d{D}")
     g = _check(p)
     assert g.plan.mode == 1
-    assert int(g.plan.meta[25]) == 19       # header word 25: split-KV item count
+    assert (int(g.plan.meta[25]), int(g.plan.meta[20])) == (97, 512)   # items, chunk
+
+
+def test_bf16_decode_long_grid_tail_chunks():
+    # a grid of two rounds and more (115 items x 16 kv-heads): 4096-key
+    # chunks, the sequences of the last 10% of the span length in 1024-key
+    # chunks (header words 20 and 48), and a remainder of 3 items
+    rng = np.random.default_rng(77)
+    lq, lk = rng.integers(1, 5, 40), rng.integers(2000, 14001, 40)
+    p = W.make_problem(78, lq, lk, 32, 16, 128, causal=True, name="decode_tail")
+    g = _check(p, bwd=False)
+    assert g.plan.mode == 1
+    assert [int(g.plan.meta[w]) for w in (25, 20, 48)] == [115, 4096, 1024]
 
 
 def test_bf16_decode_window_and_no_sink():

@@ -10,12 +10,14 @@ import pytest
 
 import oracle as O
 from softmax_sink_amd import binding as B
+from softmax_sink_amd import workloads as W
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HDR = os.path.join(ROOT, "include", "sink_attn.h")
 
 # header word indices / tile shapes as laid out by the library
 W_MODE, W_FWDBM, W_FWDBN, W_BWDBM, W_BWDBN, W_DECBN, W_DECCHUNK = 14, 15, 16, 17, 18, 19, 20
+W_DECTAIL, W_DECTAILPCT = 48, 49      # split-KV chunk of the grid's last sequences, share cut so
 W_NFWD, W_FWDOFF, W_NBWD, W_BWDOFF, W_NDEC, W_DECOFF, W_DECSEQ, W_DECROWS = range(21, 29)
 
 
@@ -57,7 +59,8 @@ def _check_against_oracle(cu_q, cu_k, causal, wl, wr, hq=4, hk=2):
     fbm, fbn, bbm, bbn = meta[W_FWDBM], meta[W_FWDBN], meta[W_BWDBM], meta[W_BWDBN]
     assert _items(meta, W_NFWD, W_FWDOFF) == O.forward_items(cu_q, cu_k, fbm, fbn, causal, wl, wr)
     assert _items(meta, W_NBWD, W_BWDOFF) == O.backward_items(cu_q, cu_k, bbm, bbn, causal, wl, wr)
-    ditems, per_seq = O.decode_items(cu_q, cu_k, meta[W_DECBN], meta[W_DECCHUNK], causal, wl, wr)
+    ditems, per_seq = O.decode_items(cu_q, cu_k, meta[W_DECBN], meta[W_DECCHUNK], causal, wl, wr,
+                                     meta[W_DECTAIL], meta[W_DECTAILPCT])
     # the forward's regions lie in the prefix it reads (header word 47):
     # the split-KV items and per-sequence table in decode mode, else the
     # per-query-tile items; the backward's items lie past it
@@ -273,7 +276,8 @@ def test_paged_metadata_matches_oracle_schedule():
         assert fws > 0 and meta[W_MODE] == 1
         assert meta[W_PAGED:W_PAGED + 4].tolist() == [1, bs, table.shape[1], kv.num_blocks]
         cu_k = np.r_[0, np.cumsum(used)].astype(np.int32)
-        ditems, per_seq = O.decode_items(cu_q, cu_k, meta[W_DECBN], meta[W_DECCHUNK], True, -1, -1)
+        ditems, per_seq = O.decode_items(cu_q, cu_k, meta[W_DECBN], meta[W_DECCHUNK], True, -1, -1,
+                                         meta[W_DECTAIL], meta[W_DECTAILPCT])
         assert _items(meta, W_NDEC, W_DECOFF, 4) == ditems
         # a paged table serves the forward only: in decode mode it holds
         # neither backward nor per-query-tile items
@@ -571,3 +575,39 @@ def test_noalloc_backward_rejects_problems_beyond_its_scratch(L):
     st = B.sink_attn_bwd_noalloc(p, meta, fake, fake, fake, fake, fake, fake, fake, fake, fake,
                                  fake, 0.1, fake, fake, fake, fake, stream=0, check=False)
     assert st == B.E_BUFFER_TOO_SMALL
+
+
+@pytest.mark.parametrize("name,lens_q,lens_k,hk,chunk,tail", [
+    # 64 sequences (the decode workload): 2312 blocks at 4096 keys, two
+    # rounds and more, so the last 10% of the span length goes in 1024s
+    ("decode_softmax_n", None, None, 8, 4096, 1024),
+    # one 32k sequence: 64 blocks at 4096 keys; halved to 512 keys (512
+    # blocks, one per slot); one round, no tail cut
+    ("b1_k32k", [1], [32768], 8, 512, 512),
+    # 16 x 16k: 512 blocks already at 4096 keys; one round, no tail cut
+    ("b16_k16k", [2] * 16, [16384] * 16, 8, 4096, 4096),
+    # a single short sequence stops at the shortest chunk
+    ("b1_k1000", [3], [1000], 1, 512, 512),
+])
+def test_split_kv_chunk_choice(name, lens_q, lens_k, hk, chunk, tail):
+    """The split-KV chunk is 4096 keys, halved down to 512 while the grid
+    (items x kv-heads) has fewer than 512 blocks; when the grid has at least
+    1024 blocks, the sequences in the last 10% of the span length (longest
+    first) are cut into 1024-key items. The items equal the oracle's
+    bookkeeping for those parameters."""
+    if lens_q is None:
+        lens_q, lens_k = W.decode_lengths()
+        hq = 32
+        cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+        cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    else:
+        cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+        cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+        hq = 4 * hk
+    _, (meta, _, _) = _meta(cu_q, cu_k, hq, hk, 128, True)
+    assert meta[W_MODE] == 1
+    assert (meta[W_DECCHUNK], meta[W_DECTAIL], meta[W_DECTAILPCT]) == (chunk, tail, 10)
+    ditems, per_seq = O.decode_items(cu_q, cu_k, meta[W_DECBN], chunk, True, -1, -1, tail, 10)
+    assert _items(meta, W_NDEC, W_DECOFF, 4) == ditems
+    blocks = len(ditems) * hk
+    assert blocks >= 512 or chunk == 512

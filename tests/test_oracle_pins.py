@@ -433,6 +433,30 @@ def test_items_cover_every_kept_element():
                 for _, _, a, c in mine:
                     got[a:c] = True
                 assert not (colkeep & ~got).any()
+        # cutting the sequences of the last half of the span length into
+        # one-tile pieces covers the same keys, contiguously, in the same
+        # sequence order; the longest sequence keeps its 4-tile pieces
+        titems, tper = O.decode_items(cu_q, cu_k, tk, 4 * tk, causal, wl, wr, tk, 50)
+        assert sorted(range(len(tper)), key=lambda b: tper[b][0]) == \
+            sorted(range(len(per_seq)), key=lambda b: per_seq[b][0])
+        for b, (first, n) in enumerate(tper):
+            mine, plain = titems[first:first + n], ditems[per_seq[b][0]:per_seq[b][0] + per_seq[b][1]]
+            assert (n == 0) == (len(plain) == 0)
+            if n:
+                assert (mine[0][2], mine[-1][3]) == (plain[0][2], plain[-1][3])
+                assert all(x[3] == y[2] for x, y in zip(mine, mine[1:]))
+                assert [it[1] for it in mine] == list(range(n)) and all(it[0] == b for it in mine)
+        if titems:
+            b0 = titems[0][0]
+            assert titems[tper[b0][0]:tper[b0][0] + tper[b0][1]] == \
+                ditems[per_seq[b0][0]:per_seq[b0][0] + per_seq[b0][1]]
+            spans = {b: (ditems[f][2], ditems[f + n - 1][3]) for b, (f, n) in enumerate(per_seq) if n}
+            total, before = sum(hi - lo for lo, hi in spans.values()), 0
+            for b in sorted(spans, key=lambda b: tper[b][0]):
+                if 2 * before >= total:
+                    first, n = tper[b]
+                    assert all(it[3] - it[2] <= tk for it in titems[first:first + n])
+                before += spans[b][1] - spans[b][0]
 
 
 def test_dsink_only_matches_full_backward():
