@@ -364,22 +364,29 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
   }
 
-  // role 0 writes dV, role 1 dK (times the softmax scale)
+  // role 0 writes dV, role 1 dK (times the softmax scale), each its
+  // [128 keys x D] tile through LDS so that the stores write whole rows
+  // (both roles at once where the staging buffers hold two tiles, else one
+  // after the other)
+  static_assert(KB == 1 && W == 4 && kBwdBN == 128, "one 128-key tile per role");
   const float sc = role == 0 ? 1.f : a.scale;
+  T* dst = static_cast<T*>(role == 0 ? a.dv : a.dk) + koff + (int64_t)kt * kBwdBN * kstride;
+  const int tid = threadIdx.x & 255, nrows = lk - kt * kBwdBN;
+  constexpr int kOut = TileRows<D>::kBytes;
+  wait_vmem();
+  __syncthreads();                              // every wave is done with the LDS stages
+  if constexpr (2 * kOut <= S::bytes) {
+    tile_rows_to_lds<D, T>(&acc[0][0], sc, smem + role * kOut, tid);
+    __syncthreads();
+    tile_rows_from_lds<D, T>(smem + role * kOut, dst, kstride, nrows, tid);
+  } else {
+    static_assert(kOut <= S::bytes, "one tile fits the stages");
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    const int j = jbase + 32 * kb;
-    if (j < lk) {
-      T* dst = static_cast<T*>(role == 0 ? a.dv : a.dk) + koff + (int64_t)j * kstride;
-#pragma unroll
-      for (int db = 0; db < NB; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int d = 32 * db + 8 * g4 + 4 * hl;
-          *reinterpret_cast<u32x2*>(dst + d) =
-              pack4_bits<T>(acc[db][kb][4 * g4] * sc, acc[db][kb][4 * g4 + 1] * sc,
-                         acc[db][kb][4 * g4 + 2] * sc, acc[db][kb][4 * g4 + 3] * sc);
-        }
+    for (int rr = 0; rr < 2; ++rr) {
+      if (role == rr) tile_rows_to_lds<D, T>(&acc[0][0], sc, smem, tid);
+      __syncthreads();
+      if (role == rr) tile_rows_from_lds<D, T>(smem, dst, kstride, nrows, tid);
+      __syncthreads();
     }
   }
 }
@@ -513,19 +520,13 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdArgs a)
   }
   if (kt < kt_hi) tile_step(std::integral_constant<int, 0>{}, kt);
 
-  if (i < lq) {
-    T* dqp = static_cast<T*>(a.dq) + roff;
-    const float sc = a.scale;
-#pragma unroll
-    for (int n = 0; n < NB; ++n)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = 32 * n + 8 * g + 4 * hl;
-        *reinterpret_cast<u32x2*>(dqp + d) =
-            pack4_bits<T>(o[n][4 * g] * sc, o[n][4 * g + 1] * sc, o[n][4 * g + 2] * sc,
-                       o[n][4 * g + 3] * sc);
-      }
-  }
+  // dQ (times the softmax scale) through LDS, whole rows per store (the
+  // tile buffers are idle: the last step waited for its transfers and synced)
+  static_assert(kFwdBM == 128 && kFwdBM * D * 2 <= 2 * TILE, "the dQ tile fits one buffer");
+  store_tile_rows<D, T>(o, a.scale, lds0,
+                        static_cast<T*>(a.dq) + (int64_t)q0 * a.g.q_seq +
+                            (int64_t)qt * kFwdBM * a.g.q_row + h * a.g.q_head,
+                        a.g.q_row, lq - qt * kFwdBM);
 }
 
 template <int D, typename T>

@@ -237,25 +237,19 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void fwd_prefill_kernel(FwdAr
   }
   if (kt < kt_hi) tile_step(std::integral_constant<int, 0>{}, kt);
 
-  // epilogue: out = O / l, lse = m + log2(l) (natural log), sink included
+  // epilogue: out = O / l, lse = m + log2(l) (natural log), sink included;
+  // O goes through LDS (the tile buffers are idle: the last step waited for
+  // its transfers and synced) so that the stores write whole rows
   const float lt = l + half_partner(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (i < lq) {
-    T* op = static_cast<T*>(a.out) + (int64_t)q0 * a.g.o_seq + (int64_t)i * a.g.o_row +
-            h * a.g.o_head;
-#pragma unroll
-    for (int n = 0; n < NB; ++n)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = 32 * n + 8 * g + 4 * hl;
-        *reinterpret_cast<u32x2*>(op + d) =
-            pack4_bits<T>(o[n][4 * g] * inv, o[n][4 * g + 1] * inv,
-                       o[n][4 * g + 2] * inv, o[n][4 * g + 3] * inv);
-      }
-    if (hl == 0)
-      a.lse[(int64_t)q0 * a.g.l_seq + (int64_t)i * a.g.l_row + h * a.g.l_head] =
-          lt > 0.f ? (m + log2_hw(lt)) * kLn2 : kNegInf;
-  }
+  if (i < lq && hl == 0)
+    a.lse[(int64_t)q0 * a.g.l_seq + (int64_t)i * a.g.l_row + h * a.g.l_head] =
+        lt > 0.f ? (m + log2_hw(lt)) * kLn2 : kNegInf;
+  static_assert(kFwdBM == 128 && kFwdBM * D * 2 <= 2 * TILE, "the O tile fits one buffer");
+  store_tile_rows<D, T>(o, inv, lds0,
+                        static_cast<T*>(a.out) + (int64_t)q0 * a.g.o_seq +
+                            (int64_t)qt * kFwdBM * a.g.o_row + h * a.g.o_head,
+                        a.g.o_row, lq - qt * kFwdBM);
 }
 
 // ---------------------------------------------------------------------------

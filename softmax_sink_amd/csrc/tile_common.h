@@ -226,6 +226,61 @@ __device__ __forceinline__ int head_of_slot(int j, int hq) {
   return j;
 }
 
+// Store a [128 x D] result tile held in the MFMA output layout of four
+// waves -- row r = 32w + c of the tile in lane (hl, c) of wave w (thread
+// `tid` = 64w + 32hl + c of the group), column 32n + 8g + 4hl + e in
+// acc[n][4g + e] -- scaled and rounded to T, into rows [0, nrows) of `dst`
+// (row stride `stride` elements), through 128 * D * 2 bytes of LDS that the
+// caller guarantees idle (no transfer in flight, no wave still reading).
+// First each lane puts its 8-byte pieces into 16-byte granules of its row
+// (granule j of row r at j ^ (r & SW), so that the 32 rows of a wave spread
+// over the banks); after a barrier, D/8 threads store each row, 16 bytes
+// apiece, so that every store instruction writes whole rows. Written
+// straight from the MFMA layout instead, every store instruction of a wave
+// covered 16 bytes of 32 different rows, and issuing a tile's stores took
+// about 4000 cycles.
+template <int D> struct TileRows {
+  static constexpr int GR = D / 8;             // 16-byte granules per row
+  static constexpr int SW = (GR < 16 ? GR : 16) - 1;
+  static constexpr int RPP = 256 / GR;         // rows per store pass
+  static constexpr int kBytes = 128 * D * 2;
+};
+template <int D, typename T>
+__device__ __forceinline__ void tile_rows_to_lds(const f32x16* acc, float scale, char* lds, int tid) {
+  using R = TileRows<D>;
+  const int hl = (tid >> 5) & 1, r = (tid >> 6) * 32 + (tid & 31);
+#pragma unroll
+  for (int n = 0; n < D / 32; ++n)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int j = 4 * n + g;                 // granule of column 32n + 8g + 4hl
+      *reinterpret_cast<u32x2*>(lds + r * (D * 2) + ((j ^ (r & R::SW)) * 16) + hl * 8) =
+          pack4_bits<T>(acc[n][4 * g] * scale, acc[n][4 * g + 1] * scale,
+                        acc[n][4 * g + 2] * scale, acc[n][4 * g + 3] * scale);
+    }
+}
+template <int D, typename T>
+__device__ __forceinline__ void tile_rows_from_lds(const char* lds, T* dst, int64_t stride, int nrows,
+                                                   int tid) {
+  using R = TileRows<D>;
+  const int tr = tid / R::GR, tg = tid % R::GR;
+#pragma unroll
+  for (int r0 = 0; r0 < 128; r0 += R::RPP) {
+    const int rr = r0 + tr;
+    if (rr < nrows)
+      *reinterpret_cast<u32x4*>(dst + (int64_t)rr * stride + tg * 8) =
+          *reinterpret_cast<const u32x4*>(lds + rr * (D * 2) + ((tg ^ (rr & R::SW)) * 16));
+  }
+}
+// Both halves for a 256-thread block.
+template <int D, typename T>
+__device__ __forceinline__ void store_tile_rows(const f32x16* acc, float scale, char* lds, T* dst,
+                                                int64_t stride, int nrows) {
+  tile_rows_to_lds<D, T>(acc, scale, lds, threadIdx.x);
+  __syncthreads();
+  tile_rows_from_lds<D, T>(lds, dst, stride, nrows, threadIdx.x);
+}
+
 // Work item and kv-head of split-KV block `id` (grid n_items x nh). The nh
 // kv-heads of one key chunk read disjoint 2*D-byte pieces of the same K and
 // V rows; they go to the same XCD (block id mod 8), one after the other, so
