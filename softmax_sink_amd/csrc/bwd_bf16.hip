@@ -100,8 +100,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int* itw = a.items + item * kItemWords;
   const int b = itw[0], kt = itw[1], qt_lo = itw[2], qt_hi = itw[3];
   const int qf_lo = itw[4], qf_hi = itw[5];
-  const int q0 = q_start(a, b), lq = q_len(a, b);
-  const int k0 = k_start(a, b), lk = k_len(a, b);
+  const int q0 = itw[8], lq = itw[9], k0 = itw[10], lk = itw[11];
   const int G = a.group;
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -408,8 +407,7 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdArgs a)
   const int* it = a.items_q + item * kItemWords;
   const int b = it[0], qt = it[1], kt_lo = it[2], kt_hi = it[3];
   const int kf_lo = it[4], kf_hi = it[5];
-  const int q0 = q_start(a, b), lq = q_len(a, b);
-  const int k0 = k_start(a, b), lk = k_len(a, b);
+  const int q0 = it[8], lq = it[9], k0 = it[10], lk = it[11];
   const int hk = h / a.group;
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;

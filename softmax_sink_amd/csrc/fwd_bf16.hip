@@ -64,10 +64,7 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void fwd_prefill_kernel(FwdAr
   const int* it = a.items + item * kItemWords;
   const int b = it[0], qt = it[1], kt_lo = it[2], kt_hi = it[3];
   const int kf_lo = it[4], kf_hi = it[5];
-  const int q0 = q_start(a, b), lq = q_len(a, b);
-  int k0 = 0, lk;
-  if constexpr (PAGED) lk = a.seqused_k[b];
-  else { k0 = k_start(a, b); lk = k_len(a, b); }
+  const int q0 = it[8], lq = it[9], k0 = it[10], lk = it[11];
   const int hk = h / a.group;
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -275,10 +272,7 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void fwd_split_kernel(FwdArgs
   chunk_work(blockIdx.x, a.n_items, a.hk, item, hk);
   const int* it = a.items + item * kItemWords;
   const int b = it[0], k_lo = it[2], k_hi = it[3], row_base = it[4];
-  const int q0 = q_start(a, b), lq = q_len(a, b);
-  int k0 = 0, lk;
-  if constexpr (PAGED) lk = a.seqused_k[b];
-  else { k0 = k_start(a, b); lk = k_len(a, b); }
+  const int q0 = it[8], lq = it[9], k0 = it[10], lk = it[11];
   const int G = a.group;
   const int rows = lq * G;
 

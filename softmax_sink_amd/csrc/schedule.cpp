@@ -514,6 +514,19 @@ sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
     h[kPageLayout] = paged->kv.layout;
     h[kPageHash] = static_cast<int32_t>(hash);
   }
+  // per-sequence rows and lengths into words 8-11 of every item
+  auto lengths = [&](std::vector<Item>& v) {
+    for (Item& it : v) {
+      const int b = it.w[0];
+      it.w[8] = p.seq_q ? b * p.seq_q : cu_q[b];
+      it.w[9] = cu_q[b + 1] - cu_q[b];
+      it.w[10] = paged ? 0 : (p.seq_k ? b * p.seq_k : cu_k[b]);
+      it.w[11] = cu_k[b + 1] - cu_k[b];
+    }
+  };
+  lengths(dec);
+  lengths(fwd);
+  lengths(bwd);
   int32_t* w = out + dec_off;
   for (const Item& it : dec) { std::memcpy(w, it.w, sizeof(it.w)); w += kItemWords; }
   std::memcpy(w, dec_seq.data(), sizeof(int32_t) * dec_seq.size());

@@ -29,7 +29,7 @@ enum MetaWord : int {
 static_assert(kFwdWords == SINK_ATTN_META_FWD_WORDS, "header word of the forward prefix");
 
 constexpr int32_t kMagicValue = 0x4B4E4953;  // "SINK" little-endian
-constexpr int kItemWords = 8;
+constexpr int kItemWords = 16;
 
 // Table order: header, decode items, decode per-sequence table, forward
 // items, backward items. The forward reads the header and, in decode mode,
@@ -38,6 +38,10 @@ constexpr int kItemWords = 8;
 // Forward item:  b, qt, kt_lo, kt_hi, kf_lo, kf_hi, 0, 0
 // Backward item: b, kt, qt_lo, qt_hi, qf_lo, qf_hi, 0, 0
 // Decode item:   b, split, k_lo, k_hi, row_base, 0, 0, 0
+// Words 8-11 of every item: the sequence's first query row and query row
+// count, first key row and key row count (as q_start, q_len, k_start,
+// k_len give them; first key row 0 for a paged cache), so that a block has
+// them with its item instead of one memory latency later; 12-15 unused.
 // Decode per-sequence table (2 words per sequence): first item, count.
 
 enum Mode : int32_t { kModePrefill = 0, kModeDecode = 1 };

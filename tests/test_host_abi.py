@@ -18,6 +18,7 @@ HDR = os.path.join(ROOT, "include", "sink_attn.h")
 # header word indices / tile shapes as laid out by the library
 W_MODE, W_FWDBM, W_FWDBN, W_BWDBM, W_BWDBN, W_DECBN, W_DECCHUNK = 14, 15, 16, 17, 18, 19, 20
 W_DECTAIL, W_DECTAILPCT = 48, 49      # split-KV chunk of the grid's last sequences, share cut so
+ITEM = 16                             # words per work item
 W_NFWD, W_FWDOFF, W_NBWD, W_BWDOFF, W_NDEC, W_DECOFF, W_DECSEQ, W_DECROWS = range(21, 29)
 
 
@@ -49,7 +50,7 @@ def _meta(cu_q, cu_k, hq=4, hk=2, d=128, causal=True, wl=-1, wr=-1, dtype=B.BF16
 
 def _items(meta, n_word, off_word, width=6):
     n, off = meta[n_word], meta[off_word]
-    return [tuple(int(x) for x in meta[off + 8 * i: off + 8 * i + width]) for i in range(n)]
+    return [tuple(int(x) for x in meta[off + ITEM * i: off + ITEM * i + width]) for i in range(n)]
 
 
 def _check_against_oracle(cu_q, cu_k, causal, wl, wr, hq=4, hk=2):
@@ -61,15 +62,20 @@ def _check_against_oracle(cu_q, cu_k, causal, wl, wr, hq=4, hk=2):
     assert _items(meta, W_NBWD, W_BWDOFF) == O.backward_items(cu_q, cu_k, bbm, bbn, causal, wl, wr)
     ditems, per_seq = O.decode_items(cu_q, cu_k, meta[W_DECBN], meta[W_DECCHUNK], causal, wl, wr,
                                      meta[W_DECTAIL], meta[W_DECTAILPCT])
+    # every item carries its sequence's first rows and lengths (words 8-11)
+    for n_word, off_word in ((W_NFWD, W_FWDOFF), (W_NBWD, W_BWDOFF), (W_NDEC, W_DECOFF)):
+        for it in meta[meta[off_word]: meta[off_word] + ITEM * meta[n_word]].reshape(-1, ITEM):
+            b = it[0]
+            assert tuple(it[8:12]) == (cu_q[b], cu_q[b + 1] - cu_q[b], cu_k[b], cu_k[b + 1] - cu_k[b])
     # the forward's regions lie in the prefix it reads (header word 47):
     # the split-KV items and per-sequence table in decode mode, else the
     # per-query-tile items; the backward's items lie past it
     pre, nb = int(meta[B.META_FWD_WORDS]), len(cu_q) - 1
     if meta[W_MODE] == 1:
-        assert meta[W_DECOFF] + 8 * meta[W_NDEC] <= pre and meta[W_DECSEQ] + 2 * nb <= pre
+        assert meta[W_DECOFF] + ITEM * meta[W_NDEC] <= pre and meta[W_DECSEQ] + 2 * nb <= pre
         assert meta[W_FWDOFF] >= pre
     else:
-        assert meta[W_FWDOFF] + 8 * meta[W_NFWD] <= pre
+        assert meta[W_FWDOFF] + ITEM * meta[W_NFWD] <= pre
     assert meta[W_BWDOFF] >= pre and pre <= len(meta)
     if meta[W_MODE] == 0:
         # prefill tables carry no split-KV items (the per-sequence table is
@@ -82,7 +88,7 @@ def _check_against_oracle(cu_q, cu_k, causal, wl, wr, hq=4, hk=2):
     seq = meta[meta[W_DECSEQ]: meta[W_DECSEQ] + 2 * (len(cu_q) - 1)].reshape(-1, 2)
     assert [tuple(int(x) for x in r) for r in seq] == per_seq
     # partial-row bases: running sum of (query rows x q-heads) over the items
-    bases = [int(meta[meta[W_DECOFF] + 8 * i + 4]) for i in range(meta[W_NDEC])]
+    bases = [int(meta[meta[W_DECOFF] + ITEM * i + 4]) for i in range(meta[W_NDEC])]
     want, acc = [], 0
     for b, _, _, _ in ditems:
         want.append(acc)
@@ -286,8 +292,11 @@ def test_paged_metadata_matches_oracle_schedule():
         meta_c, _, _ = B.sink_attn_metadata(p, cu_q, cu_k)
         assert meta_c[W_PAGED] == 0
         n = meta[W_NDEC]
-        assert np.array_equal(meta[meta[W_DECOFF]:meta[W_DECOFF] + 8 * n],
-                              meta_c[meta_c[W_DECOFF]:meta_c[W_DECOFF] + 8 * n])
+        its = meta[meta[W_DECOFF]:meta[W_DECOFF] + ITEM * n].reshape(n, ITEM)
+        its_c = meta_c[meta_c[W_DECOFF]:meta_c[W_DECOFF] + ITEM * n].reshape(n, ITEM)
+        # identical but for the first key row (word 10): 0 in a paged cache
+        assert np.array_equal(np.delete(its, 10, axis=1), np.delete(its_c, 10, axis=1))
+        assert not its[:, 10].any() and np.array_equal(its_c[:, 10], cu_k[its_c[:, 0]])
 
 
 def test_paged_metadata_rejects():
@@ -434,6 +443,10 @@ def test_padded_schedule_equals_packed_schedule(layout, lout):
                               (W_NDEC, W_DECOFF, 5)):
             assert _items(meta, nw, ow, width) == _items(pm, nw, ow, width)
         assert meta[W_MODE] == pm[W_MODE]
+        # padded rows: sequence b starts at row b * S (words 8 and 10)
+        for nw, ow in ((W_NFWD, W_FWDOFF), (W_NBWD, W_BWDOFF), (W_NDEC, W_DECOFF)):
+            for it in meta[meta[ow]: meta[ow] + ITEM * meta[nw]].reshape(-1, ITEM):
+                assert tuple(it[8:12]) == (it[0] * 70, uq[it[0]], it[0] * 130, uk[it[0]])
         lay = B.LAYOUTS
         assert list(meta[W_LAYOUT:W_LAYOUT + 5]) == [lay[layout], lay[lout or layout], 70, 130, 3]
         # D [Hq, B*S_q] covers the padding rows too
