@@ -261,8 +261,8 @@ def run_workload(name, steps, warmup, progress=True):
         # device copies in the padded layout; p itself stays packed (the
         # oracle's sample reads it)
         src = dataclasses.replace(p, **{
-            name: W.pad_rows(getattr(p, name), cu, seq, padded, 0)
-            for name, cu, seq in (("q", p.cu_q, seq_q), ("k", p.cu_k, seq_k),
+            t: W.pad_rows(getattr(p, t), cu, seq, padded, 0)
+            for t, cu, seq in (("q", p.cu_q, seq_q), ("k", p.cu_k, seq_k),
                                   ("v", p.cu_k, seq_k), ("dout", p.cu_q, seq_q))})
     else:
         src = p
@@ -386,8 +386,8 @@ def run_workload(name, steps, warmup, progress=True):
     step_flops = fwd_flops + (bwd_flops if train else 0.0)
     value = step_flops / (ms * 1e-3) / 1e12
     kms = {}
-    for name, a, b in main_events:
-        kms.setdefault(name, []).append(a.elapsed_time(b))
+    for ev, a, b in main_events:
+        kms.setdefault(ev, []).append(a.elapsed_time(b))
     kavg = {n: float(np.mean(x)) for n, x in kms.items()}
     esize = 2 if p.dtype == "bf16" else 4
     if decode:
