@@ -483,50 +483,53 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(FwdArgs a) {
   if (i >= lq) return;                          // padding of a padded layout
   const int first = a.dec_seq[2 * b], n = a.dec_seq[2 * b + 1];
   const float sink = a.sinks ? a.sinks[h] : kNegInf;
-  // pass 1: the largest chunk maximum (lanes over chunks)
-  float mt = sink * kLog2e;
-  for (int g = 0; g < n; g += 64) {
-    const int s = g + lane;
-    if (s < n) mt = fmaxf(mt, a.ws_m[a.items[(first + s) * kItemWords + 4] + h * lq + i]);
-  }
-  for (int o = 32; o > 0; o >>= 1) mt = fmaxf(mt, __shfl_xor(mt, o));
-  const float mu = mt == kNegInf ? 0.f : mt;
-  // pass 2: weights, denominator and O
+  // Chunks eight at a time: lane u < 8 reads the row base of chunk g + u,
+  // then the (m, l) of that chunk and, across all lanes, the O partials of
+  // all eight chunks go out together, so that a row of up to eight chunks
+  // costs one dependent load after its row bases. A running maximum merges
+  // the groups (O and l rescaled when it grows); sums in a fixed order.
   constexpr int PER = D / 64;
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
   float lpart = 0.f;
-  for (int g = 0; g < n; g += 64) {
-    const int s = g + lane;
+  float mt = sink * kLog2e;                     // running maximum, the sink included
+  for (int g = 0; g < n; g += 8) {
+    const int cnt = min(8, n - g);
     int prow = 0;
-    float f = 0.f;
-    if (s < n) {
-      prow = a.items[(first + s) * kItemWords + 4] + h * lq + i;
-      f = exp2_hw(a.ws_m[prow] - mu);
-      lpart += a.ws_l[prow] * f;
+    if (lane < cnt) prow = a.items[(first + g + lane) * kItemWords + 4] + h * lq + i;
+    float v[8][PER];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      // a slot past the last chunk re-reads chunk 0 of the group (weight 0)
+      const float* po = a.ws_o + (int64_t)__builtin_amdgcn_readlane(prow, u < cnt ? u : 0) * D + lane * PER;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) v[u][e] = po[e];
     }
-    const int cnt = min(64, n - g);
+    float mc = kNegInf, lc = 0.f;
+    if (lane < cnt) {
+      mc = a.ws_m[prow];
+      lc = a.ws_l[prow];
+    }
+    float gm = mc;
+    for (int o = 32; o > 0; o >>= 1) gm = fmaxf(gm, __shfl_xor(gm, o));
+    const float m_new = fmaxf(mt, gm);
+    const float mu = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = exp2_hw(mt - mu);       // 0 while nothing was counted
+    const float f = exp2_hw(mc - mu);           // 0 for lanes past the group
+    mt = m_new;
+    lpart = lpart * alpha + lc * f;
     const int fbits = __float_as_int(f);
-    // eight chunks at a time: all eight loads are in flight before the
-    // first product; a slot past the last chunk re-reads chunk c0 with
-    // weight 0, which leaves the sum as it was
-    for (int c0 = 0; c0 < cnt; c0 += 8) {
-      float v[8][PER], fc[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int c = c0 + u < cnt ? c0 + u : c0;
-        const float* po = a.ws_o + (int64_t)__builtin_amdgcn_readlane(prow, c) * D + lane * PER;
-        fc[u] = c0 + u < cnt ? __int_as_float(__builtin_amdgcn_readlane(fbits, c)) : 0.f;
+    for (int e = 0; e < PER; ++e) acc[e] *= alpha;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) v[u][e] = po[e];
-      }
+    for (int u = 0; u < 8; ++u) {
+      const float fu = u < cnt ? __int_as_float(__builtin_amdgcn_readlane(fbits, u)) : 0.f;
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] += v[u][e] * fc[u];
+      for (int e = 0; e < PER; ++e) acc[e] += v[u][e] * fu;
     }
   }
+  const float mu = mt == kNegInf ? 0.f : mt;
   for (int o = 32; o > 0; o >>= 1) lpart += __shfl_xor(lpart, o);
   const float lt = lpart + exp2_hw(sink * kLog2e - mu);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
