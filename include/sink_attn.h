@@ -155,7 +155,10 @@ typedef struct {
  * forward calls read only the first meta_host[SINK_ATTN_META_FWD_WORDS]
  * words of meta_dev (the header and the items the forward walks), so a
  * caller that runs no backward with the table may copy just that prefix;
- * the backward reads the whole table.
+ * the backward reads the whole table. The tile kernels take each sequence's
+ * first rows and lengths from the table (the host cu_seqlens it was built
+ * from), other kernels from the device cu_seqlens: the two copies must hold
+ * the same values.
  * Errors: E_INVALID (problem or cu_seqlens checks above, NULL pointers, a
  * padded layout), E_UNSUPPORTED, E_BUFFER_TOO_SMALL (meta_capacity_words <
  * *meta_words; the sizes are still written). */
