@@ -347,7 +347,10 @@ sink_attn_status sink_attn_bwd_padded(const sink_attn_problem* p,
  * Every call on a GPU shares that GPU's array: calls that overlap on one
  * GPU (on two streams, or two host threads) race and give wrong results;
  * calls ordered on one stream are safe. The kernels write every scratch
- * word before reading it, so nothing is cleared between calls.
+ * word before reading it, so nothing is cleared between calls. Under HIP
+ * graph capture, make the first call on a device before capturing (the
+ * address lookup is not a stream operation); the call itself enqueues
+ * kernel launches only.
  * Errors: as sink_attn_bwd; E_BUFFER_TOO_SMALL when the metadata's
  * bwd_workspace_bytes exceed SINK_ATTN_NOALLOC_SCRATCH_BYTES; E_HIP when
  * the array's address cannot be obtained. */
