@@ -107,7 +107,11 @@ typedef enum {
 
 /* Element type of q, k, v, out, dout, dq, dk, dv (lse, sinks, dsink are
  * always fp32). fp16 is the CANN page's other input type (q, k, v
- * validation); it runs the same MFMA kernels as bf16. */
+ * validation); it runs the same MFMA kernels as bf16. fp32 runs a plain
+ * VALU path, one thread per query row (or key row in the dK/dV pass), with
+ * no tile schedule and no MFMA: it serves as the exact-arithmetic
+ * configuration for small problems and is orders of magnitude slower than
+ * the 16-bit path on long sequences. */
 typedef enum { SINK_ATTN_FP32 = 0, SINK_ATTN_BF16 = 1, SINK_ATTN_FP16 = 2 } sink_attn_dtype;
 
 /* Tensor layouts (CANN page, layout matching table): k and v always share
