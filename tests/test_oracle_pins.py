@@ -603,3 +603,46 @@ def test_sampled_rows_equal_full_problem_rows(mask):
     t_empty = cu_q[4]                       # first row of the (4, 0) sequence
     assert np.isneginf(lse[3, t_empty]) and lse[0, t_empty] == sinks[0]
     assert np.isfinite(lse[3]).any()
+
+
+# --- kept-pair count, the FLOP basis of every throughput figure, against
+# closed forms of the bottom-right aligned masks ("pytorch/pytorch issue
+# #108108": the causal diagonal ends in the bottom-right corner; windows
+# inclusive on both sides, reading A4) -------------------------------------
+def _causal_closed_form(Lq, Lk, wl=-1):
+    """Row i keeps keys max(0, i + off - wl) .. min(Lk - 1, i + off),
+    off = Lk - Lq, summed with integer arithmetic only."""
+    off, total = Lk - Lq, 0
+    for i in range(Lq):
+        hi = min(Lk - 1, i + off)
+        lo = 0 if wl < 0 else max(0, i + off - wl)
+        total += max(0, hi - lo + 1)
+    return total
+
+
+def test_count_kept_pairs_closed_forms():
+    cu = lambda lens: np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    # square causal: L (L + 1) / 2 per sequence
+    lens = [1, 7, 64, 300]
+    assert O.count_kept_pairs(cu(lens), cu(lens), True, -1, -1) == sum(L * (L + 1) // 2 for L in lens)
+    # no mask: Lq Lk, empty sequences included
+    lq, lk = [3, 0, 50, 9], [5, 4, 0, 9]
+    assert O.count_kept_pairs(cu(lq), cu(lk), False, -1, -1) == sum(a * b for a, b in zip(lq, lk))
+    # causal, Lq < Lk: every row keeps off + i + 1 keys, Lq off + Lq (Lq + 1) / 2
+    assert O.count_kept_pairs(cu([4]), cu([10]), True, -1, -1) == 4 * 6 + 4 * 5 // 2
+    # causal, Lq > Lk: the first Lq - Lk rows keep nothing, then 1 .. Lk
+    assert O.count_kept_pairs(cu([10]), cu([4]), True, -1, -1) == 4 * 5 // 2
+    # causal with a left window wl on a square sequence of L > wl rows:
+    # wl (wl + 1) / 2 + (L - wl)(wl + 1); the GQA window workload's
+    # 8192 rows and wl = 1024 give 7,872,000 per (sequence, head)
+    L, wl = 8192, 1024
+    want = wl * (wl + 1) // 2 + (L - wl) * (wl + 1)
+    assert want == 7_872_000
+    assert O.count_kept_pairs(cu([L]), cu([L]), True, wl, 0) == want
+    # a small sweep against the row-by-row integer form
+    rng = np.random.default_rng(11)
+    for _ in range(20):
+        a, b = (int(x) for x in rng.integers(0, 90, 2))
+        w = int(rng.integers(-1, 40))
+        assert O.count_kept_pairs(cu([a]), cu([b]), True, w, 0 if w >= 0 else -1) == \
+            _causal_closed_form(a, b, w)
