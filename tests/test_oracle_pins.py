@@ -607,8 +607,8 @@ def test_sampled_rows_equal_full_problem_rows(mask):
 
 # --- kept-pair count, the FLOP basis of every throughput figure, against
 # closed forms of the bottom-right aligned masks ("pytorch/pytorch issue
-# #108108": the causal diagonal ends in the bottom-right corner; windows
-# inclusive on both sides, reading A4) -------------------------------------
+# #108108": the causal diagonal ends in the bottom-right corner; window
+# bounds are read as inclusive on both sides) ------------------------------
 def _causal_closed_form(Lq, Lk, wl=-1):
     """Row i keeps keys max(0, i + off - wl) .. min(Lk - 1, i + off),
     off = Lk - Lq, summed with integer arithmetic only."""
