@@ -624,3 +624,34 @@ def test_split_kv_chunk_choice(name, lens_q, lens_k, hk, chunk, tail):
     assert _items(meta, W_NDEC, W_DECOFF, 4) == ditems
     blocks = len(ditems) * hk
     assert blocks >= 512 or chunk == 512
+
+
+def test_metadata_calls_from_many_host_threads_agree():
+    """Calls are reentrant: eight host threads building tables for different
+    problems at once (ctypes drops the GIL around the foreign call, so the
+    C code runs concurrently) get exactly the tables of one-at-a-time calls."""
+    import concurrent.futures as cf
+    rng = np.random.default_rng(5)
+    cases = []
+    for _ in range(48):
+        n = int(rng.integers(1, 20))
+        lq = rng.integers(0, 700, n)
+        lk = lq + rng.integers(0, 300, n)
+        lq[0], lk[0] = max(lq[0], 1), max(lk[0], 1)
+        cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+        cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+        hk = int(rng.choice([1, 2, 8]))
+        causal = bool(rng.integers(0, 2))
+        wl = int(rng.choice([-1, 64, 500]))
+        cases.append((cu_q, cu_k, 8, hk, 128, causal, wl, 0 if causal else -1))
+
+    def table(c):
+        cu_q, cu_k, hq, hk, d, causal, wl, wr = c
+        return _meta(cu_q, cu_k, hq, hk, d, causal, wl, wr)[1]
+
+    want = [table(c) for c in cases]
+    for _ in range(3):
+        with cf.ThreadPoolExecutor(8) as ex:
+            got = list(ex.map(table, cases))
+        for (m0, f0, b0), (m1, f1, b1) in zip(want, got):
+            assert np.array_equal(m0, m1) and (f0, b0) == (f1, b1)
