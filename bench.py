@@ -161,8 +161,10 @@ def other_configs():
 
 def traffic_record(workload, kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary,
-    if it was taken on the current kernel source; else None."""
+    if it was taken on the current kernel source and compile flags; else
+    None."""
     import hashlib
+    from softmax_sink_amd.build import SOURCE_FLAGS
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -173,6 +175,10 @@ def traffic_record(workload, kernel):
     h = hashlib.sha256()
     for name in rec["sources"]:
         h.update(open(os.path.join(ROOT, "softmax_sink_amd", "csrc", name), "rb").read())
+    # extra compile flags of the kernel's source file, where it has any
+    flags = SOURCE_FLAGS.get(rec["sources"][0], [])
+    if flags:
+        h.update(" ".join(flags).encode())
     if h.hexdigest() != rec["sources_sha256"]:
         return None
     return rec["hbm_bytes_per_launch"]

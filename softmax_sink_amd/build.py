@@ -17,6 +17,14 @@ OBJDIR = os.path.join(ROOT, "_build")
 SOURCES = ["schedule.cpp", "metadata.cpp", "api.cpp", "fwd_bf16.hip", "bwd_bf16.hip", "f32_path.hip",
            "merge.hip"]
 ARCH = os.environ.get("SINK_ATTN_ARCH", "gfx950")
+# Per-source compiler flags. The backward kernels are scheduled with the
+# max-ILP machine scheduler: same instructions and results bit for bit, and
+# the dK/dV kernel 2.4% faster on the long causal training workload (3.238 ->
+# 3.160 ms, median of six alternating passes); the forward gained nothing
+# from it and keeps the default scheduler.
+SOURCE_FLAGS = {
+    "bwd_bf16.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
 
 
 def hipcc():
@@ -39,6 +47,7 @@ def _compile(src):
     cmd = [hipcc()] + flags()
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
+    cmd += SOURCE_FLAGS.get(src, [])
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
