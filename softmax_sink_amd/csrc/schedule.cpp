@@ -11,6 +11,7 @@
 #include <cmath>
 #include <cstring>
 #include <limits>
+#include <utility>
 #include <vector>
 
 #include "sink_attn_internal.h"
@@ -39,46 +40,65 @@ RowBounds row_bounds(const sink_attn_problem& p, int64_t lq, int64_t lk) {
   return r;
 }
 
-enum TileClass { kDead = 0, kPartial = 1, kFull = 2 };
+// Tile spans of one work item in O(1). A tile is live when some row of it
+// keeps some key of it, and full when it has its nominal shape and every
+// row keeps every key. The kept keys of row i, [lo(i), hi(i)], move up by
+// one key per row and are never empty (hi - lo = wl + wr_eff >= 0), so any
+// run of rows keeps one contiguous key interval; the live tiles are those
+// that interval meets, and the full tiles a contiguous run inside them.
+// Spans are [lo, hi) with the canonical empty forms: no live tile ->
+// (0, 0, 0, 0); no full tile -> full = (lo, lo).
+void put_spans(int64_t lo, int64_t hi, int64_t flo, int64_t fhi, int32_t* out4) {
+  if (hi <= lo) lo = hi = 0;
+  if (fhi <= flo) flo = fhi = lo;
+  out4[0] = static_cast<int32_t>(lo);
+  out4[1] = static_cast<int32_t>(hi);
+  out4[2] = static_cast<int32_t>(flo);
+  out4[3] = static_cast<int32_t>(fhi);
+}
 
-// Class of the tile rows [r0, r1) x keys [c0, c1) of one sequence, in O(1)
-// from the monotone row bounds: live iff some row keeps some key of the
-// tile; full iff the tile has its nominal shape and every row keeps every
-// key (the last row's lower bound and the first row's upper bound decide).
-TileClass classify(const RowBounds& rb, int64_t r0, int64_t r1, int64_t c0,
-                   int64_t c1, int64_t tile_q, int64_t tile_k) {
-  if (r1 <= r0 || c1 <= c0) return kDead;
-  // rows with lo(i) <= c1-1 form a prefix [r0, a); rows with hi(i) >= c0 a
-  // suffix [b, r1)
-  int64_t a = r1;
-  if (rb.wl >= 0) a = std::min<int64_t>(r1, c1 - rb.off + rb.wl);
-  int64_t b = r0;
-  if (rb.wr_eff < kInf) b = std::max<int64_t>(r0, c0 - rb.off - rb.wr_eff);
-  if (std::max(r0, b) >= std::min(r1, a)) return kDead;
-  if (r1 - r0 == tile_q && c1 - c0 == tile_k && rb.lo(r1 - 1) <= c0 &&
-      rb.hi(r0) >= c1 - 1)
-    return kFull;
-  return kPartial;
+// Key tiles of width bn over [0, lk) for the query rows [r0, r1).
+void key_tile_spans(const RowBounds& rb, int64_t r0, int64_t r1, int64_t lk, int64_t bm,
+                    int64_t bn, int32_t* out4) {
+  const int64_t k0 = std::max<int64_t>(0, rb.lo(r0));
+  const int64_t k1 = std::min<int64_t>(lk - 1, rb.hi(r1 - 1));   // kept keys [k0, k1]
+  if (r1 <= r0 || k1 < k0) return put_spans(0, 0, 0, 0, out4);
+  int64_t flo = 0, fhi = 0;
+  if (r1 - r0 == bm) {
+    // c0 >= lo(r1 - 1), c0 + bn - 1 <= hi(r0), c0 + bn <= lk
+    const int64_t c_min = std::max<int64_t>(0, rb.lo(r1 - 1));
+    const int64_t c_max = std::min<int64_t>(rb.hi(r0) - bn + 1, lk - bn);
+    if (c_max >= c_min) {
+      flo = (c_min + bn - 1) / bn;
+      fhi = c_max / bn + 1;
+    }
+  }
+  put_spans(k0 / bn, k1 / bn + 1, flo, fhi, out4);
+}
+
+// Query tiles of height bm over [0, lq) for the keys [c0, c1).
+void query_tile_spans(const RowBounds& rb, int64_t c0, int64_t c1, int64_t lq, int64_t bm,
+                      int64_t bn, int32_t* out4) {
+  // rows with lo(i) <= c1 - 1 and hi(i) >= c0: [i0, i1)
+  const int64_t i1 = rb.wl >= 0 ? std::min<int64_t>(lq, c1 - rb.off + rb.wl) : lq;
+  const int64_t i0 = rb.wr_eff < kInf ? std::max<int64_t>(0, c0 - rb.off - rb.wr_eff) : 0;
+  if (c1 <= c0 || i1 <= i0) return put_spans(0, 0, 0, 0, out4);
+  int64_t flo = 0, fhi = 0;
+  if (c1 - c0 == bn) {
+    // r0 + bm <= lq, lo(r0 + bm - 1) <= c0, hi(r0) >= c1 - 1
+    const int64_t r_top = (rb.wl >= 0 ? std::min<int64_t>(lq, c0 - rb.off + rb.wl + 1) : lq) - bm;
+    const int64_t r_min = rb.wr_eff < kInf ? std::max<int64_t>(0, c1 - 1 - rb.off - rb.wr_eff) : 0;
+    if (r_top >= r_min) {
+      flo = (r_min + bm - 1) / bm;
+      fhi = r_top / bm + 1;
+    }
+  }
+  put_spans(i0 / bm, (i1 - 1) / bm + 1, flo, fhi, out4);
 }
 
 struct Item {
   int32_t w[kItemWords];
 };
-
-// Contiguous span of non-dead tiles and, inside it, of full tiles, with the
-// canonical empty forms: no live tile -> (0,0,0,0); no full tile ->
-// full = (lo, lo).
-void spans(const std::vector<int>& cls, int32_t* out4) {
-  int n = static_cast<int>(cls.size());
-  int lo = -1, hi = -1, flo = -1, fhi = -1;
-  for (int t = 0; t < n; ++t) {
-    if (cls[t] != kDead) { if (lo < 0) lo = t; hi = t + 1; }
-    if (cls[t] == kFull) { if (flo < 0) flo = t; fhi = t + 1; }
-  }
-  if (lo < 0) { lo = hi = 0; }
-  if (flo < 0) { flo = fhi = lo; }
-  out4[0] = lo; out4[1] = hi; out4[2] = flo; out4[3] = fhi;
-}
 
 // Dispatch order: sequences by their total live tile count, descending
 // (ties: lower index first); inside a sequence, live tile count descending,
@@ -101,14 +121,25 @@ void sort_items(std::vector<Item>& v, int batch) {
   std::sort(order.begin(), order.end(), [&](int x, int y) {
     return work[x] != work[y] ? work[x] > work[y] : x < y;
   });
+  // each group is ordered through (live count, position) keys, so that the
+  // 64-byte items move once
   std::vector<Item> out;
   out.reserve(v.size());
+  std::vector<std::pair<int32_t, uint32_t>> key;
   for (int b : order) {
-    const size_t lo = out.size();
-    out.insert(out.end(), v.begin() + first[b], v.begin() + first[b + 1]);
-    std::stable_sort(out.begin() + lo, out.end(), [](const Item& x, const Item& y) {
-      return x.w[3] - x.w[2] > y.w[3] - y.w[2];
-    });
+    const size_t lo = first[b], hi = first[b + 1];
+    bool sorted = true;
+    for (size_t i = lo + 1; i < hi && sorted; ++i)
+      sorted = v[i - 1].w[3] - v[i - 1].w[2] >= v[i].w[3] - v[i].w[2];
+    if (sorted) {
+      out.insert(out.end(), v.begin() + lo, v.begin() + hi);
+      continue;
+    }
+    key.clear();
+    for (size_t i = lo; i < hi; ++i)
+      key.emplace_back(-(v[i].w[3] - v[i].w[2]), static_cast<uint32_t>(i));
+    std::sort(key.begin(), key.end());       // count descending, then position
+    for (const auto& k : key) out.push_back(v[k.second]);
   }
   v.swap(out);
 }
@@ -372,55 +403,47 @@ sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
   const bool want_fwd = want_bwd || mode == kModePrefill;
   const bool want_dec = mode == kModeDecode;
   std::vector<Item> fwd, bwd, dec;
+  {
+    int64_t nf = 0, nb = 0;
+    for (int b = 0; b < B; ++b) {
+      nf += want_fwd ? (cu_q[b + 1] - cu_q[b] + kFwdBM - 1) / kFwdBM : 0;
+      nb += want_bwd ? (cu_k[b + 1] - cu_k[b] + kBwdBN - 1) / kBwdBN : 0;
+    }
+    fwd.reserve(static_cast<size_t>(nf));
+    bwd.reserve(static_cast<size_t>(nb));
+  }
   std::vector<int32_t> dec_seq(2 * static_cast<size_t>(B), 0);
   std::vector<int64_t> dec_span(2 * static_cast<size_t>(B), 0);   // [start, stop) per sequence
-  std::vector<int> cls;
   int64_t dec_rows = 0;
   for (int b = 0; b < B; ++b) {
     const int64_t lq = cu_q[b + 1] - cu_q[b], lk = cu_k[b + 1] - cu_k[b];
     const RowBounds rb = row_bounds(p, lq, lk);
     // forward items: one per query tile
     const int64_t nqt = want_fwd ? (lq + kFwdBM - 1) / kFwdBM : 0;
-    const int64_t nkt = (lk + kFwdBN - 1) / kFwdBN;
     for (int64_t qt = 0; qt < nqt; ++qt) {
-      cls.assign(static_cast<size_t>(nkt), kDead);
       const int64_t r0 = qt * kFwdBM, r1 = std::min(lq, r0 + kFwdBM);
-      for (int64_t kt = 0; kt < nkt; ++kt) {
-        const int64_t c0 = kt * kFwdBN, c1 = std::min(lk, c0 + kFwdBN);
-        cls[kt] = classify(rb, r0, r1, c0, c1, kFwdBM, kFwdBN);
-      }
       Item it{};
       it.w[0] = b;
       it.w[1] = static_cast<int32_t>(qt);
-      spans(cls, it.w + 2);
+      key_tile_spans(rb, r0, r1, lk, kFwdBM, kFwdBN, it.w + 2);
       fwd.push_back(it);
     }
     // backward items: one per key tile
     const int64_t bbm = bwd_tile_rows(p.head_dim);
-    const int64_t bnq = (lq + bbm - 1) / bbm;
     const int64_t bnk = want_bwd ? (lk + kBwdBN - 1) / kBwdBN : 0;
     for (int64_t kt = 0; kt < bnk; ++kt) {
-      cls.assign(static_cast<size_t>(bnq), kDead);
       const int64_t c0 = kt * kBwdBN, c1 = std::min(lk, c0 + kBwdBN);
-      for (int64_t qt = 0; qt < bnq; ++qt) {
-        const int64_t r0 = qt * bbm, r1 = std::min(lq, r0 + bbm);
-        cls[qt] = classify(rb, r0, r1, c0, c1, bbm, kBwdBN);
-      }
       Item it{};
       it.w[0] = b;
       it.w[1] = static_cast<int32_t>(kt);
-      spans(cls, it.w + 2);
+      query_tile_spans(rb, c0, c1, lq, bbm, kBwdBN, it.w + 2);
       bwd.push_back(it);
     }
-    // split-KV span: the union of the rows' kept keys, rounded out to
-    // kDecBN tiles
+    // split-KV span: the keys kept by any row (one interval, the rows'
+    // intervals being contiguous), rounded out to kDecBN tiles
     if (want_dec && lq > 0 && lk > 0) {
-      int64_t jlo = kInf, jhi = -1;
-      for (int64_t i = 0; i < lq; ++i) {
-        const int64_t a = std::max<int64_t>(0, rb.lo(i));
-        const int64_t c = std::min<int64_t>(lk - 1, rb.hi(i));
-        if (a <= c) { jlo = std::min(jlo, a); jhi = std::max(jhi, c + 1); }
-      }
+      const int64_t jlo = std::max<int64_t>(0, rb.lo(0));
+      const int64_t jhi = std::min<int64_t>(lk - 1, rb.hi(lq - 1)) + 1;
       if (jhi > jlo) {
         dec_span[2 * b] = (jlo / kDecBN) * kDecBN;
         dec_span[2 * b + 1] = std::min<int64_t>(lk, (jhi + kDecBN - 1) / kDecBN * kDecBN);

@@ -114,6 +114,31 @@ def test_schedule_matches_oracle_random():
         _check_against_oracle(cu_q, cu_k, causal, wl, wr)
 
 
+@pytest.mark.parametrize("d", [128, 256])
+def test_schedule_matches_oracle_at_tile_edges(d):
+    """Lengths within two rows of a tile multiple and windows on either side
+    of the tile widths, where the live and full tile spans change: the
+    library's items (computed from the row bounds) against the oracle's
+    element-by-element tile classes. D = 256 walks 32-row backward tiles."""
+    rng = np.random.default_rng(77 + d)
+    edges = [64 * m + e for m in range(1, 9) for e in (-2, -1, 0, 1, 2)]
+    wins = [0, 1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 300]
+    for trial in range(40):
+        Bn = int(rng.integers(1, 4))
+        lq = rng.choice(edges, Bn)
+        lk = lq.copy() if trial % 4 == 0 else rng.choice(edges, Bn)
+        causal = bool(trial % 2)
+        wl = int(rng.choice([-1] + wins))
+        wr = (0 if rng.integers(0, 2) else -1) if causal else int(rng.choice([-1] + wins))
+        cu_q = np.r_[0, np.cumsum(lq)].astype(np.int32)
+        cu_k = np.r_[0, np.cumsum(lk)].astype(np.int32)
+        p, (meta, _, _) = _meta(cu_q, cu_k, 4, 2, d, causal, wl, wr)
+        fbm, fbn, bbm, bbn = meta[W_FWDBM], meta[W_FWDBN], meta[W_BWDBM], meta[W_BWDBN]
+        assert bbm == (32 if d == 256 else 64)
+        assert _items(meta, W_NFWD, W_FWDOFF) == O.forward_items(cu_q, cu_k, fbm, fbn, causal, wl, wr)
+        assert _items(meta, W_NBWD, W_BWDOFF) == O.backward_items(cu_q, cu_k, bbm, bbn, causal, wl, wr)
+
+
 def test_split_kv_schedule_matches_oracle_random():
     """Decode-mode tables (query rows x GQA group <= 64): split-KV items,
     per-sequence table and partial-row bases against the oracle."""
