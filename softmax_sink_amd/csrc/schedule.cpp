@@ -402,15 +402,18 @@ sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
   const bool want_bwd = paged == nullptr;
   const bool want_fwd = want_bwd || mode == kModePrefill;
   const bool want_dec = mode == kModeDecode;
+  // One forward item per query tile and one backward item per key tile; a
+  // call that only asks for the sizes counts them without building them.
+  const bool fill = out != nullptr;
+  int64_t n_fwd = 0, n_bwd = 0;
+  for (int b = 0; b < B; ++b) {
+    n_fwd += want_fwd ? (cu_q[b + 1] - cu_q[b] + kFwdBM - 1) / kFwdBM : 0;
+    n_bwd += want_bwd ? (cu_k[b + 1] - cu_k[b] + kBwdBN - 1) / kBwdBN : 0;
+  }
   std::vector<Item> fwd, bwd, dec;
-  {
-    int64_t nf = 0, nb = 0;
-    for (int b = 0; b < B; ++b) {
-      nf += want_fwd ? (cu_q[b + 1] - cu_q[b] + kFwdBM - 1) / kFwdBM : 0;
-      nb += want_bwd ? (cu_k[b + 1] - cu_k[b] + kBwdBN - 1) / kBwdBN : 0;
-    }
-    fwd.reserve(static_cast<size_t>(nf));
-    bwd.reserve(static_cast<size_t>(nb));
+  if (fill) {
+    fwd.reserve(static_cast<size_t>(n_fwd));
+    bwd.reserve(static_cast<size_t>(n_bwd));
   }
   std::vector<int32_t> dec_seq(2 * static_cast<size_t>(B), 0);
   std::vector<int64_t> dec_span(2 * static_cast<size_t>(B), 0);   // [start, stop) per sequence
@@ -419,7 +422,7 @@ sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
     const int64_t lq = cu_q[b + 1] - cu_q[b], lk = cu_k[b + 1] - cu_k[b];
     const RowBounds rb = row_bounds(p, lq, lk);
     // forward items: one per query tile
-    const int64_t nqt = want_fwd ? (lq + kFwdBM - 1) / kFwdBM : 0;
+    const int64_t nqt = want_fwd && fill ? (lq + kFwdBM - 1) / kFwdBM : 0;
     for (int64_t qt = 0; qt < nqt; ++qt) {
       const int64_t r0 = qt * kFwdBM, r1 = std::min(lq, r0 + kFwdBM);
       Item it{};
@@ -430,7 +433,7 @@ sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
     }
     // backward items: one per key tile
     const int64_t bbm = bwd_tile_rows(p.head_dim);
-    const int64_t bnk = want_bwd ? (lk + kBwdBN - 1) / kBwdBN : 0;
+    const int64_t bnk = want_bwd && fill ? (lk + kBwdBN - 1) / kBwdBN : 0;
     for (int64_t kt = 0; kt < bnk; ++kt) {
       const int64_t c0 = kt * kBwdBN, c1 = std::min(lk, c0 + kBwdBN);
       Item it{};
@@ -463,8 +466,8 @@ sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
   const int64_t dec_off = kHeaderWords;
   const int64_t seq_off = dec_off + static_cast<int64_t>(dec.size()) * kItemWords;
   const int64_t fwd_off = seq_off + 2 * static_cast<int64_t>(B);
-  const int64_t bwd_off = fwd_off + static_cast<int64_t>(fwd.size()) * kItemWords;
-  const int64_t total = bwd_off + static_cast<int64_t>(bwd.size()) * kItemWords;
+  const int64_t bwd_off = fwd_off + n_fwd * kItemWords;
+  const int64_t total = bwd_off + n_bwd * kItemWords;
   const int64_t fwd_words = mode == kModeDecode ? fwd_off : bwd_off;
   if (total >= std::numeric_limits<int32_t>::max() ||
       dec_rows >= std::numeric_limits<int32_t>::max())
@@ -500,9 +503,9 @@ sink_attn_status build_metadata(const sink_attn_problem& p, const int32_t* cu_q,
   h[kWordDecChunk] = dec_chunk;
   h[kWordDecTail] = dec_tail;
   h[kWordDecTailPct] = kDecTailPercent;
-  h[kNFwd] = static_cast<int32_t>(fwd.size());
+  h[kNFwd] = static_cast<int32_t>(n_fwd);
   h[kFwdOff] = static_cast<int32_t>(fwd_off);
-  h[kNBwd] = static_cast<int32_t>(bwd.size());
+  h[kNBwd] = static_cast<int32_t>(n_bwd);
   h[kBwdOff] = static_cast<int32_t>(bwd_off);
   h[kNDec] = static_cast<int32_t>(dec.size());
   h[kDecOff] = static_cast<int32_t>(dec_off);
