@@ -28,8 +28,10 @@ DMA = re.compile(r"^(buffer_load_dword\w*\s.*\blds\b|global_load_lds_\w+)")
 
 def _assembly(src, tmp):
     out = os.path.join(tmp, src + ".s")
-    cmd = [B.hipcc()] + B.flags() + ["--cuda-device-only", "-S", "-o", out,
-                                     os.path.join(B.CSRC, src)]
+    # the library's own flags for this source, so that the schedule checked
+    # is the one that ships
+    cmd = [B.hipcc()] + B.flags() + B.SOURCE_FLAGS.get(src, []) + [
+        "--cuda-device-only", "-S", "-o", out, os.path.join(B.CSRC, src)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     return open(out).read().split("\n")
